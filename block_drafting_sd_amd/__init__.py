@@ -1,0 +1,169 @@
+"""Block-parallel speculative draft-and-verify step for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI declared in ``include/sd.h``; the three
+functions keep the C names.  PyTorch supplies device memory and the stream;
+arguments are checked for dtype / contiguity / device and passed as raw
+pointers.  All computation happens in ``libsd_amd.so``.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+import torch
+
+from ._lib import LIB_PATH, SdError, check, load  # noqa: F401
+
+__all__ = ["sd_draft_attn", "sd_lm_head_probs", "sd_verify", "sd_version",
+           "draft_attn_workspace_size", "lm_head_workspace_size",
+           "verify_workspace_size", "SdError", "load"]
+
+
+def _req(t: torch.Tensor, name: str, dtypes, device=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
+_BF16 = (torch.bfloat16,)
+_I32 = (torch.int32,)
+_U32 = (torch.int32, torch.uint32)
+_F32 = (torch.float32,)
+
+
+def _stream_handle(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def sd_version() -> str:
+    return load().sd_version().decode()
+
+
+def draft_attn_workspace_size(batch, num_heads_q, num_heads_kv, head_dim, max_total_ctx,
+                              split_tokens=0) -> int:
+    return int(load().sd_draft_attn_workspace_size(batch, num_heads_q, num_heads_kv, head_dim,
+                                                   max_total_ctx, split_tokens))
+
+
+def lm_head_workspace_size(M, V) -> int:
+    return int(load().sd_lm_head_workspace_size(M, V))
+
+
+def verify_workspace_size(batch, total_q, total_target_rows, V) -> int:
+    return int(load().sd_verify_workspace_size(batch, total_q, total_target_rows, V))
+
+
+def _workspace(ws, nbytes, device):
+    if ws is None:
+        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError(f"workspace too small: {ws.numel() * ws.element_size()} < {nbytes}")
+    return ws
+
+
+def sd_draft_attn(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_len, q_off, *,
+                  max_draft_k: int, max_total_ctx: int, softmax_scale: Optional[float] = None,
+                  split_tokens: int = 0, out=None, workspace=None, stream=None):
+    """Draft-block attention; see ``sd_draft_attn`` in include/sd.h."""
+    lib = load()
+    dev = q.device
+    _req(q, "q", _BF16, dev)
+    _req(k_blk, "k_blk", _BF16, dev)
+    _req(v_blk, "v_blk", _BF16, dev)
+    _req(k_cache, "k_cache", _BF16, dev)
+    _req(v_cache, "v_cache", _BF16, dev)
+    _req(page_table, "page_table", _I32, dev)
+    _req(ctx_len, "ctx_len", _I32, dev)
+    _req(q_off, "q_off", _I32, dev)
+    total_q, hq, D = q.shape
+    hkv = k_blk.shape[1]
+    num_pages, _, _, page_size, _ = k_cache.shape
+    batch, max_pages = page_table.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    nbytes = lib.sd_draft_attn_workspace_size(batch, hq, hkv, D, max_total_ctx, split_tokens)
+    workspace = _workspace(workspace, nbytes, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    st = lib.sd_draft_attn(_ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(k_cache), _ptr(v_cache),
+                           _ptr(page_table), _ptr(ctx_len), _ptr(q_off), batch, total_q,
+                           max_draft_k, num_pages, max_pages, page_size, hq, hkv, D,
+                           int(max_total_ctx), int(split_tokens), float(softmax_scale),
+                           _ptr(out), _ptr(workspace), workspace.numel(), _stream_handle(stream))
+    check("sd_draft_attn", st)
+    return out
+
+
+def sd_lm_head_probs(hidden, w_vocab, q_off, req_id, seed: int, *, logits=None, lse=None,
+                     draft_tokens=None, workspace=None, stream=None
+                     ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """LM head + softmax statistics + draft sampling; see include/sd.h."""
+    lib = load()
+    dev = hidden.device
+    _req(hidden, "hidden", _BF16, dev)
+    _req(w_vocab, "w_vocab", _BF16, dev)
+    _req(q_off, "q_off", _I32, dev)
+    _req(req_id, "req_id", _U32, dev)
+    M, H = hidden.shape
+    V = w_vocab.shape[0]
+    batch = q_off.numel() - 1
+    if logits is None:
+        logits = torch.empty(M, V, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(M, dtype=torch.float32, device=dev)
+    if draft_tokens is None:
+        draft_tokens = torch.empty(M, dtype=torch.int32, device=dev)
+    nbytes = lib.sd_lm_head_workspace_size(M, V)
+    workspace = _workspace(workspace, nbytes, dev)
+    st = lib.sd_lm_head_probs(_ptr(hidden), _ptr(w_vocab), M, H, V, _ptr(q_off), batch,
+                              _ptr(req_id), int(seed) & ((1 << 64) - 1), _ptr(logits),
+                              _ptr(lse), _ptr(draft_tokens), _ptr(workspace), workspace.numel(),
+                              _stream_handle(stream))
+    check("sd_lm_head_probs", st)
+    return logits, lse, draft_tokens
+
+
+def sd_verify(target_logits, t_off, draft_logits, draft_lse, draft_tokens, q_off, req_id,
+              seed: int, *, accepted_len=None, next_token=None, accept_ratio=None,
+              want_ratio: bool = True, workspace=None, stream=None):
+    """Speculative-sampling verification; see include/sd.h.
+    Returns (accepted_len, next_token, accept_ratio or None)."""
+    lib = load()
+    dev = target_logits.device
+    _req(target_logits, "target_logits", _F32, dev)
+    _req(t_off, "t_off", _I32, dev)
+    _req(draft_logits, "draft_logits", _F32, dev)
+    if draft_lse is not None:
+        _req(draft_lse, "draft_lse", _F32, dev)
+    _req(draft_tokens, "draft_tokens", _I32, dev)
+    _req(q_off, "q_off", _I32, dev)
+    _req(req_id, "req_id", _U32, dev)
+    R, V = target_logits.shape
+    total_q = draft_tokens.numel()
+    batch = t_off.numel() - 1
+    if accepted_len is None:
+        accepted_len = torch.empty(batch, dtype=torch.int32, device=dev)
+    if next_token is None:
+        next_token = torch.empty(batch, dtype=torch.int32, device=dev)
+    if accept_ratio is None and want_ratio and total_q > 0:
+        accept_ratio = torch.empty(total_q, dtype=torch.float32, device=dev)
+    nbytes = lib.sd_verify_workspace_size(batch, total_q, R, V)
+    workspace = _workspace(workspace, nbytes, dev)
+    st = lib.sd_verify(_ptr(target_logits), _ptr(t_off), _ptr(draft_logits), _ptr(draft_lse),
+                       _ptr(draft_tokens), _ptr(q_off), batch, total_q, R, V, _ptr(req_id),
+                       int(seed) & ((1 << 64) - 1), _ptr(accepted_len), _ptr(next_token),
+                       _ptr(accept_ratio), _ptr(workspace), workspace.numel(),
+                       _stream_handle(stream))
+    check("sd_verify", st)
+    return accepted_len, next_token, accept_ratio

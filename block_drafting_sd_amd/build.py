@@ -1,0 +1,81 @@
+"""Build the step's shared library (HIP C++ for gfx950) in-tree.
+
+``python -m block_drafting_sd_amd.build`` compiles every ``csrc/*.hip`` with
+hipcc into ``block_drafting_sd_amd/libsd_amd.so``.  hipcc cross-compiles for
+gfx950 on a machine without a GPU.
+"""
+from __future__ import annotations
+
+import glob
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libsd_amd.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+ARCH = "gfx950"
+
+# -packed-fp32-ops: keep hipcc from forming v_pk_{add,mul,fma}_f32 from
+# ordinary float code (the host pass warns that it does not know the
+# feature; that is harmless).
+HIP_FLAGS = [
+    "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found (ROCm is required to build the library)")
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    """Compile every source and link ``libsd_amd.so``; returns its path."""
+    cc = hipcc()
+    srcs = sources()
+    with tempfile.TemporaryDirectory(prefix="sd_amd_build_") as tmp:
+        objs, procs = [], []
+        for s in srcs:
+            o = os.path.join(tmp, os.path.basename(s) + ".o")
+            cmd = [cc, *HIP_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", s, "-o", o]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((s, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                              stderr=subprocess.STDOUT, text=True)))
+            objs.append(o)
+            while len([p for _, p in procs if p.poll() is None]) >= jobs:
+                procs[0][1].wait()
+        for s, p in procs:
+            out, _ = p.communicate()
+            keep = [l for l in out.splitlines() if "packed-fp32-ops" not in l]
+            if p.returncode != 0:
+                raise RuntimeError(f"hipcc failed on {s}:\n" + "\n".join(keep))
+            if keep and verbose:
+                print("\n".join(keep))
+        tmp_lib = os.path.join(tmp, LIB_NAME)
+        cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("link failed:\n" + r.stdout)
+        shutil.copyfile(tmp_lib, LIB_PATH + ".tmp")
+        os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,81 @@
+// Launch-argument structs and launcher entry points behind the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sd {
+
+// ----------------------------------------------------------- draft attention
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k_blk;
+  const uint16_t* v_blk;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* page_table;
+  const int32_t* ctx_len;
+  const int32_t* q_off;
+  uint16_t* out;
+  int32_t batch, total_q, max_draft_k, num_pages, max_pages;
+  int32_t hq, hkv, group;
+  int32_t split_tokens;   // prefix tokens per work item (multiple of 64)
+  int32_t max_items;      // work items the partial buffers hold
+  float scale_log2;       // softmax_scale * log2(e)
+  int32_t* item_off;      // [batch + 1] first work item of each request
+  float* part_lse;        // [max_items][64]       (log2 units)
+  float* part_o;          // [max_items][D/4][64][4]
+};
+
+constexpr int kAttnRows = 64;        // query rows per (request, kv head) item
+constexpr int kAttnTile = 32;        // keys per inner tile (two 16-token pages)
+
+int64_t attn_max_items(int32_t batch, int32_t hkv, int64_t max_total_ctx,
+                       int32_t split_tokens);
+int32_t attn_split_tokens(int32_t hkv, int64_t max_total_ctx, int32_t requested);
+hipError_t launch_draft_attn(const AttnArgs& a, int head_dim, hipStream_t s);
+
+// ------------------------------------------------------------------ LM head
+struct LmArgs {
+  const uint16_t* hidden;   // [M, H]
+  const uint16_t* w;        // [V, H]
+  const int32_t* q_off;     // [batch + 1]
+  const uint32_t* req_id;   // [batch]
+  float* logits;            // [M, V]
+  float* lse;               // [M]
+  int32_t* tokens;          // [M]
+  float4* part;             // [M][n_vt] (max, sumexp, best key, best index)
+  int32_t M, H, V, batch, n_vt, n_mt;
+  uint32_t key0, key1;
+};
+
+constexpr int kLmBV = 128;   // vocab rows per workgroup tile
+constexpr int kLmBM = 128;   // draft rows per workgroup tile
+constexpr int kLmBK = 64;    // hidden dims per pipeline stage
+
+hipError_t launch_lm_head(const LmArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------------- verify
+struct VerifyArgs {
+  const float* target;      // [R, V]
+  const int32_t* t_off;     // [batch + 1]
+  const float* draft;       // [total_q, V]
+  const float* draft_lse;   // [total_q] or null
+  const int32_t* tokens;    // [total_q]
+  const int32_t* q_off;     // [batch + 1]
+  const uint32_t* req_id;   // [batch]
+  int32_t* accepted;        // [batch]
+  int32_t* next_token;      // [batch]
+  float* accept_ratio;      // [total_q] or null
+  float2* row_part;         // [(R + total_q) * n_chunks] (max, sumexp)
+  float4* samp_part;        // [batch * n_chunks * 2]
+  int32_t batch, total_q, R, V, n_chunks, chunk;
+  uint32_t key0, key1;
+};
+
+constexpr int kVerifyChunk = 8192;   // vocab entries per workgroup
+
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t s);
+
+}  // namespace sd

@@ -1,0 +1,195 @@
+// Speculative-sampling verification ("LongSpark", sec. 2.1, eqs. (1)-(2) and
+// the bonus-token rule after eq. (2); "ForeSpark", sec. 4.4 for verify
+// budgets b_b <= K_b).
+//
+// Three launches, no host synchronisation:
+//   1. verify_rowstats  grid (rows x vocab chunks): per chunk (max, sum exp)
+//      of every target row (and of every draft row when no draft lse is
+//      given).  Streams the logits once: HBM-bound.
+//   2. verify_sample    grid (requests x vocab chunks): every workgroup of a
+//      request merges the row statistics it needs, evaluates all of the
+//      request's ratio tests in parallel, takes the first rejection, and
+//      draws Gumbel-max candidates of its vocab chunk from the residual
+//      [p_j - q_j]_+ (and from p_j as the fallback), or from p_{b+1}.
+//   3. verify_finalize  one thread per request merges the chunk candidates.
+#include "sd_common.h"
+#include "sd_internal.h"
+
+#include <float.h>
+
+namespace sd {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxVerify = 255;   // b_b handled per request
+
+// (max, sum exp(x - max)) of one vocab chunk of one row.
+__global__ __launch_bounds__(kThreads) void verify_rowstats(VerifyArgs a) {
+  __shared__ float sh[kThreads / 64];
+  const int row = blockIdx.x / a.n_chunks;
+  const int c = blockIdx.x % a.n_chunks;
+  const float* src = row < a.R ? a.target + static_cast<size_t>(row) * a.V
+                               : a.draft + static_cast<size_t>(row - a.R) * a.V;
+  const int lo = c * a.chunk;
+  const int hi = min(a.V, lo + a.chunk);
+  float mx = -FLT_MAX;
+  for (int i = lo + threadIdx.x; i < hi; i += kThreads) mx = fmaxf(mx, src[i]);
+  mx = block_reduce_max<kThreads>(mx, sh);
+  float se = 0.f;
+  for (int i = lo + threadIdx.x; i < hi; i += kThreads)
+    se += __builtin_amdgcn_exp2f((src[i] - mx) * kLog2e);
+  se = block_reduce_sum<kThreads>(se, sh);
+  if (threadIdx.x == 0) a.row_part[blockIdx.x] = make_float2(mx, se);
+}
+
+__device__ float merge_lse(const float2* part, int n) {
+  float mx = -FLT_MAX;
+  for (int i = 0; i < n; ++i) mx = fmaxf(mx, part[i].x);
+  float s = 0.f;
+  for (int i = 0; i < n; ++i) s += part[i].y * __builtin_amdgcn_exp2f((part[i].x - mx) * kLog2e);
+  return mx + logf(s);
+}
+
+__global__ __launch_bounds__(kThreads) void verify_sample(VerifyArgs a) {
+  __shared__ float s_lse_p[kMaxVerify + 1];
+  __shared__ float s_lse_q[kMaxVerify];
+  __shared__ int s_ok[kMaxVerify + 1];
+  __shared__ int s_a;
+  __shared__ float shk[kThreads / 64];
+  __shared__ int shi[kThreads / 64];
+
+  const int b = blockIdx.x / a.n_chunks;
+  const int c = blockIdx.x % a.n_chunks;
+  const int tid = threadIdx.x;
+  const int t0 = clampi(a.t_off[b], 0, a.R);
+  const int t1 = clampi(a.t_off[b + 1], t0, a.R);
+  const int q0 = clampi(a.q_off[b], 0, a.total_q);
+  const int kb = clampi(a.q_off[b + 1], q0, a.total_q) - q0;
+  if (t1 == t0) {   // no target row: nothing to verify (contract violation)
+    if (c == 0 && tid == 0) a.accepted[b] = 0;
+    if (tid == 0) {
+      a.samp_part[blockIdx.x * 2] = make_float4(-FLT_MAX, __int_as_float(-1), 0.f, 0.f);
+      a.samp_part[blockIdx.x * 2 + 1] = make_float4(-FLT_MAX, __int_as_float(-1), 0.f, 0.f);
+    }
+    return;
+  }
+  const int nv = min(min(t1 - t0 - 1, kb), kMaxVerify);
+  const uint32_t rid = a.req_id[b];
+
+  // A: log-normalisers of the rows this request may touch
+  for (int i = tid; i <= nv; i += kThreads)
+    s_lse_p[i] = merge_lse(a.row_part + static_cast<size_t>(t0 + i) * a.n_chunks, a.n_chunks);
+  for (int i = tid; i < nv; i += kThreads)
+    s_lse_q[i] = a.draft_lse ? a.draft_lse[q0 + i]
+                             : merge_lse(a.row_part + static_cast<size_t>(a.R + q0 + i) * a.n_chunks,
+                                         a.n_chunks);
+  __syncthreads();
+
+  // B: every ratio test in parallel (eq. (1)): r_j = min(1, p_j(y_j)/q_j(y_j))
+  for (int i = tid; i < nv; i += kThreads) {
+    const int j = i + 1;
+    const int y = clampi(a.tokens[q0 + i], 0, a.V - 1);
+    const float lp = a.target[static_cast<size_t>(t0 + i) * a.V + y] - s_lse_p[i];
+    const float lq = a.draft[static_cast<size_t>(q0 + i) * a.V + y] - s_lse_q[i];
+    float r = 1.f;
+    if (expf(lq) > 0.f) r = fminf(1.f, expf(lp - lq));
+    const u32x4 w = philox4x32_10(u32x4{0u, static_cast<uint32_t>(j), rid, kStreamAccept},
+                                  a.key0, a.key1);
+    s_ok[i] = accept_from_bits(w[0]) < r;
+    if (c == 0 && a.accept_ratio) a.accept_ratio[q0 + i] = r;
+  }
+  if (c == 0 && a.accept_ratio)
+    for (int i = nv + tid; i < kb; i += kThreads) a.accept_ratio[q0 + i] = __int_as_float(0x7fc00000);
+  __syncthreads();
+
+  // C: the first rejection ends the round
+  if (tid == 0) {
+    int acc = nv;
+    for (int i = 0; i < nv; ++i)
+      if (!s_ok[i]) {
+        acc = i;
+        break;
+      }
+    s_a = acc;
+    if (c == 0) a.accepted[b] = acc;
+  }
+  __syncthreads();
+  const int acc = s_a;
+  const bool residual = acc < nv;
+  const int j = acc + 1;                      // position of the drawn token
+  const float* xrow = a.target + static_cast<size_t>(t0 + acc) * a.V;
+  const float* zrow = a.draft + static_cast<size_t>(q0 + acc) * a.V;
+  const float lse_p = s_lse_p[acc];
+  const float lse_q = residual ? s_lse_q[acc] : 0.f;
+
+  // D: Gumbel-max candidates of this vocab chunk
+  Cand best_r{-FLT_MAX, 0x7fffffff}, best_p{-FLT_MAX, 0x7fffffff};
+  int any_pos = 0;
+  const int lo = c * a.chunk;
+  const int hi = min(a.V, lo + a.chunk);
+  for (int g = lo + 4 * tid; g < hi; g += 4 * kThreads) {
+    const u32x4 w = philox4x32_10(u32x4{static_cast<uint32_t>(g >> 2), static_cast<uint32_t>(j),
+                                        rid, kStreamSample},
+                                  a.key0, a.key1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int v = g + e;
+      if (v < hi) {
+        const float gn = gumbel_from_bits(w[e]);
+        const float x = xrow[v];
+        const float kp = x + gn;
+        if (better(kp, v, best_p.key, best_p.idx)) best_p = Cand{kp, v};
+        if (residual) {
+          const float res = expf(x - lse_p) - expf(zrow[v] - lse_q);
+          if (res > 0.f) {
+            any_pos = 1;
+            const float kr = logf(res) + gn;
+            if (better(kr, v, best_r.key, best_r.idx)) best_r = Cand{kr, v};
+          }
+        }
+      }
+    }
+  }
+  best_r = block_best<kThreads>(best_r, shk, shi);
+  best_p = block_best<kThreads>(best_p, shk, shi);
+  any_pos = __syncthreads_or(any_pos);
+  if (tid == 0) {
+    a.samp_part[blockIdx.x * 2] =
+        make_float4(best_r.key, __int_as_float(best_r.idx), any_pos ? 1.f : 0.f, 0.f);
+    a.samp_part[blockIdx.x * 2 + 1] = make_float4(best_p.key, __int_as_float(best_p.idx), 0.f, 0.f);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void verify_finalize(VerifyArgs a) {
+  const int b = blockIdx.x * kThreads + threadIdx.x;
+  if (b >= a.batch) return;
+  const float4* p = a.samp_part + static_cast<size_t>(b) * a.n_chunks * 2;
+  bool any_pos = false;
+  for (int c = 0; c < a.n_chunks; ++c) any_pos |= p[2 * c].z != 0.f;
+  const int sel = any_pos ? 0 : 1;   // residual draw, else a draw from p
+  float bk = -FLT_MAX;
+  int bi = 0x7fffffff;
+  for (int c = 0; c < a.n_chunks; ++c) {
+    const float4 q = p[2 * c + sel];
+    const int idx = __float_as_int(q.y);
+    if (idx >= 0 && better(q.x, idx, bk, bi)) {
+      bk = q.x;
+      bi = idx;
+    }
+  }
+  a.next_token[b] = bi == 0x7fffffff ? -1 : bi;
+}
+
+}  // namespace
+
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t s) {
+  const int rows = a.R + (a.draft_lse ? 0 : a.total_q);
+  if (rows > 0)
+    hipLaunchKernelGGL(verify_rowstats, dim3(rows * a.n_chunks), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(verify_sample, dim3(a.batch * a.n_chunks), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(verify_finalize, dim3((a.batch + kThreads - 1) / kThreads), dim3(kThreads),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace sd

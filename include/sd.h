@@ -1,0 +1,214 @@
+/*
+ * sd.h -- C ABI of one block-parallel speculative draft-and-verify step on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The step has three parts, one entry point each:
+ *   sd_draft_attn     draft-block attention over the target's paged KV cache
+ *   sd_lm_head_probs  drafter LM head, softmax statistics, draft sampling
+ *   sd_verify         lossless speculative-sampling verification
+ *
+ * Conventions shared by every call
+ *   - Tensor arguments are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees, copies to the host or synchronises; scratch
+ *     memory is the caller's `workspace` (size from the matching
+ *     *_workspace_size function, any alignment of at least 256 bytes).
+ *   - Every call enqueues its kernels on `stream` (a hipStream_t; NULL is the
+ *     default stream) and returns at once.  The status reports host-side
+ *     argument validation and launch errors only; NULL pointers, sizes out of
+ *     range and a short workspace are rejected before anything is launched.
+ *   - Integer arrays that live on the device (lengths, offsets, page ids,
+ *     tokens) are never read on the host.  Values that break the documented
+ *     contract give unspecified results but never an out-of-bounds access:
+ *     kernels clamp page ids, lengths and offsets to the host-given sizes.
+ *   - bf16 is IEEE binary32 truncated to its upper 16 bits (bfloat16);
+ *     fp32 is IEEE binary32.  All arrays are dense, row-major, unpadded.
+ *   - Re-entrant: the library holds no global state.  Calls that share a
+ *     workspace must not overlap in time.
+ *
+ * Randomness: every random decision uses Philox-4x32-10 (Salmon et al.,
+ * "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11) keyed by
+ * (seed mod 2^32, seed >> 32) with counter (v >> 2, j, req_id[b], stream):
+ * word (v & 3) serves vocab entry v, j is the 1-based draft position (b_b + 1
+ * for the bonus token), stream 0 = draft sampling, 1 = acceptance test
+ * (word 0 of counter (0, j, req_id, 1), u = (x >> 8) * 2^-24), 2 = correction
+ * or bonus token.  Tokens are Gumbel-max draws argmax_v(key_v - log(-log u_v))
+ * with u = (2 (x >> 9) + 1) * 2^-24; the smallest index wins a tie.
+ */
+#ifndef SD_H
+#define SD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t sd_status;
+
+enum {
+  SD_OK = 0,
+  SD_ERR_NULL = 1,      /* a required pointer is NULL                        */
+  SD_ERR_SHAPE = 2,     /* a size argument is out of the supported range     */
+  SD_ERR_WORKSPACE = 3, /* workspace NULL or smaller than required           */
+  SD_ERR_LAUNCH = 4,    /* the HIP runtime rejected a launch                 */
+  SD_ERR_DEVICE = 5     /* no gfx950 device is current                       */
+};
+
+/* Static description of a status code (never NULL). */
+const char* sd_status_str(sd_status s);
+
+/* Library version string, e.g. "0.1.0". */
+const char* sd_version(void);
+
+/* ------------------------------------------------------------------------
+ * sd_draft_attn -- draft-block attention over the target's paged KV cache.
+ *
+ * Defined by: "ForeSpark: Joint draft and verification budget scheduling for
+ * parallel speculative decoding", sec. 1 and sec. 4.1 (each draft position
+ * attends bidirectionally to every draft position and to the context, which
+ * enters as extra keys and values); "LongSpark: Efficient speculative
+ * decoding with a fixed-cost parallel drafter", App. A.1, Fig. 6 (one
+ * attention normalisation across all sources; bidirectional among the block's
+ * slots); "H-Spec: Parallel speculative decoding without a drafter-side KV
+ * cache", sec. 3.3.2 (draft attention reads the target's KV cache in place;
+ * head counts and dims equal the target's; block Q/K use RoPE positions that
+ * continue the prefix, so q, k_blk and the cache are all post-RoPE).
+ *
+ * For request b with prefix length N_b = ctx_len[b] and K_b = q_off[b+1] -
+ * q_off[b] draft rows, every query head h (KV head g = h / (Hq / Hkv)) of
+ * every draft row r computes, with one softmax and NO mask,
+ *     out[r, h] = softmax(s) . [V_prefix(g); v_blk[q_off[b]..q_off[b+1]-1, g]]
+ *     s = softmax_scale * q[r, h] . [K_prefix(g); k_blk[rows of b, g]]
+ * where K_prefix / V_prefix are the N_b cached rows of head g in logical
+ * token order.  Scores, softmax and accumulation are fp32; out is rounded to
+ * bf16 (nearest even).
+ *
+ * Arguments
+ *   q        bf16 [total_q, Hq, D]   draft queries, request b owns rows
+ *                                    q_off[b] .. q_off[b+1]-1
+ *   k_blk    bf16 [total_q, Hkv, D]  draft-block keys (same rows)
+ *   v_blk    bf16 [total_q, Hkv, D]  draft-block values
+ *   k_cache  bf16 [num_pages, Hkv, D/8, page_size, 8]  target keys: dims
+ *            8c..8c+7 of the token in slot t of a page are at [page, g, c, t, :]
+ *   v_cache  bf16 [num_pages, Hkv, D, page_size]  target values: dim d of the
+ *            token in slot t is at [page, g, d, t]
+ *   page_table int32 [batch, max_pages]: logical page i of request b is
+ *            physical page page_table[b*max_pages + i]; token n is slot n % 16
+ *            of logical page n / 16
+ *   ctx_len  int32 [batch]  N_b >= 0, N_b <= max_pages * page_size
+ *   q_off    int32 [batch+1] non-decreasing, q_off[0] = 0,
+ *            q_off[batch] = total_q, 1 <= K_b <= max_draft_k
+ *   max_draft_k  host bound on K_b; (Hq/Hkv) * max_draft_k <= 64
+ *   num_pages    rows of the caches (page ids are clamped to it)
+ *   page_size    16
+ *   num_heads_q, num_heads_kv  Hq % Hkv == 0
+ *   head_dim     64 or 128
+ *   max_total_ctx  host upper bound on sum_b N_b (sizes the launch)
+ *   split_tokens   prefix tokens per split-K work item; 0 lets the library
+ *                  choose; otherwise a multiple of 64
+ *   softmax_scale  usually 1/sqrt(head_dim)
+ *   out      bf16 [total_q, Hq, D]
+ * ------------------------------------------------------------------------ */
+size_t sd_draft_attn_workspace_size(int32_t batch, int32_t num_heads_q,
+                                    int32_t num_heads_kv, int32_t head_dim,
+                                    int64_t max_total_ctx, int32_t split_tokens);
+
+sd_status sd_draft_attn(const void* q, const void* k_blk, const void* v_blk,
+                        const void* k_cache, const void* v_cache,
+                        const int32_t* page_table, const int32_t* ctx_len,
+                        const int32_t* q_off, int32_t batch, int32_t total_q,
+                        int32_t max_draft_k, int32_t num_pages,
+                        int32_t max_pages, int32_t page_size,
+                        int32_t num_heads_q, int32_t num_heads_kv,
+                        int32_t head_dim, int64_t max_total_ctx,
+                        int32_t split_tokens, float softmax_scale, void* out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * sd_lm_head_probs -- drafter LM head, softmax statistics, draft sampling.
+ *
+ * Defined by: "LongSpark", sec. 2.3 and App. A.1, Fig. 6 (the frozen target
+ * normalisation and vocabulary head map the final draft states to base
+ * logits for all positions in parallel) and sec. 2.1, eq. (4) (the proposal
+ * of slot j is softmax of its logits; slots are sampled independently);
+ * "DeLS-Spec: Decoupled long-short contexts for parallel speculative
+ * drafting" (block-parallel drafting is one forward pass then one sampling
+ * step).
+ *
+ * For every row m < M:  logits[m, v] = sum_k hidden[m, k] * w_vocab[v, k]
+ * (bf16 products, fp32 accumulation), lse[m] = log sum_v exp(logits[m, v]),
+ * draft_tokens[m] = argmax_v (logits[m, v] - log(-log u_v)) with the stream-0
+ * uniforms of (request b, position j = m - q_off[b] + 1).  The draft
+ * distribution is q_m = exp(logits[m, :] - lse[m]).
+ *
+ * Arguments
+ *   hidden   bf16 [M, H]  final draft states after the target's final norm
+ *   w_vocab  bf16 [V, H]  the target's LM head (nn.Linear layout), in place
+ *   M >= 1, H a multiple of 64 (<= 65536), 1 <= V < 2^31
+ *   q_off    int32 [batch+1] row offsets of the requests (as for attention);
+ *            rows outside [0, q_off[batch]) use position m + 1 of request 0
+ *   req_id   uint32 [batch]  Philox counter word of each request
+ *   logits   fp32 [M, V] out;  lse fp32 [M] out;  draft_tokens int32 [M] out
+ * ------------------------------------------------------------------------ */
+size_t sd_lm_head_workspace_size(int32_t M, int32_t V);
+
+sd_status sd_lm_head_probs(const void* hidden, const void* w_vocab, int32_t M,
+                           int32_t H, int32_t V, const int32_t* q_off,
+                           int32_t batch, const uint32_t* req_id,
+                           uint64_t seed, float* logits, float* lse,
+                           int32_t* draft_tokens, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * sd_verify -- lossless speculative-sampling verification.
+ *
+ * Defined by: "LongSpark", sec. 2.1, eq. (1) (drafts are tested in order and
+ * y_j is accepted with probability min(1, p_j(y_j) / q_j(y_j))), eq. (2)
+ * (at the first rejection the correction token is drawn from
+ * [p_j - q_j]_+ / sum [p_j - q_j]_+) and the text after eq. (2) (if every
+ * tested draft is accepted one more token is drawn from the target's next
+ * distribution); "ForeSpark", sec. 4.4 (only a prefix of b_b <= K_b drafts is
+ * verified; the target scores them as one packed batch).
+ *
+ * Request b owns target rows t_off[b] .. t_off[b+1]-1, i.e. b_b + 1 rows:
+ * p_j = softmax(target_logits[t_off[b] + j - 1]) for j = 1 .. b_b + 1.  Its
+ * drafts are draft_tokens[q_off[b] + j - 1] with distribution
+ * q_j = exp(draft_logits[q_off[b] + j - 1] - draft_lse[...]).  For j = 1..b_b:
+ * r_j = min(1, p_j(y_j) / q_j(y_j)) (1 if q_j(y_j) underflows to 0); y_j is
+ * accepted iff u_j < r_j with u_j the stream-1 uniform of position j.  The
+ * first rejection j gives accepted_len = j - 1 and next_token = Gumbel-max
+ * draw from [p_j - q_j]_+ (from p_j if that is identically 0); if none is
+ * rejected accepted_len = b_b and next_token is a Gumbel-max draw from
+ * p_{b_b+1}.  Draws use the stream-2 uniforms of position j (b_b + 1 for the
+ * bonus).  Probabilities are evaluated in fp32.
+ *
+ * Arguments
+ *   target_logits fp32 [total_target_rows, V]
+ *   t_off    int32 [batch+1], 0 <= b_b = t_off[b+1] - t_off[b] - 1 <= K_b
+ *   draft_logits  fp32 [total_q, V]  (as written by sd_lm_head_probs)
+ *   draft_lse     fp32 [total_q] or NULL (then computed here)
+ *   draft_tokens  int32 [total_q]
+ *   q_off    int32 [batch+1]  as for sd_lm_head_probs
+ *   req_id   uint32 [batch], seed: as for sd_lm_head_probs
+ *   accepted_len int32 [batch] out;  next_token int32 [batch] out
+ *   accept_ratio fp32 [total_q] out or NULL: r_j at every tested position,
+ *                NaN at positions not tested
+ * ------------------------------------------------------------------------ */
+size_t sd_verify_workspace_size(int32_t batch, int32_t total_q,
+                                int32_t total_target_rows, int32_t V);
+
+sd_status sd_verify(const float* target_logits, const int32_t* t_off,
+                    const float* draft_logits, const float* draft_lse,
+                    const int32_t* draft_tokens, const int32_t* q_off,
+                    int32_t batch, int32_t total_q, int32_t total_target_rows,
+                    int32_t V, const uint32_t* req_id, uint64_t seed,
+                    int32_t* accepted_len, int32_t* next_token,
+                    float* accept_ratio, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SD_H */

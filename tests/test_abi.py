@@ -1,0 +1,127 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/sd.h declares, and rejects bad arguments before launching anything
+(no pointer is dereferenced on the host, so fake device addresses are safe)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import block_drafting_sd_amd as sd
+from block_drafting_sd_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sd.h")
+
+FAKE = 1 << 20        # 16-byte aligned, never dereferenced by validation
+ODD = FAKE + 8        # not 16-byte aligned
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(sd_[a-z_0-9]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from block_drafting_sd_amd import build
+        build.build()
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) >= {"sd_draft_attn", "sd_lm_head_probs", "sd_verify"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_status_strings_and_version(lib):
+    for s in range(6):
+        assert lib.sd_status_str(s)
+    assert lib.sd_status_str(99) == b"unknown status"
+    assert sd.sd_version() == "0.1.0"
+
+
+def test_workspace_sizes(lib):
+    n = lib.sd_draft_attn_workspace_size(16, 32, 8, 128, 16 * 131072, 0)
+    assert n > 16 * 131072 // 8192 * 8 * 64 * 128 * 4
+    assert lib.sd_draft_attn_workspace_size(0, 32, 8, 128, 1, 0) == 0
+    assert lib.sd_lm_head_workspace_size(256, 151936) >= 256 * (151936 // 128) * 16
+    assert lib.sd_lm_head_workspace_size(0, 10) == 0
+    assert lib.sd_verify_workspace_size(16, 256, 272, 151936) > 0
+    assert lib.sd_verify_workspace_size(16, 256, 0, 151936) == 0
+
+
+def _attn(lib, **kw):
+    a = dict(q=FAKE, k_blk=FAKE, v_blk=FAKE, k_cache=FAKE, v_cache=FAKE, page_table=FAKE,
+             ctx_len=FAKE, q_off=FAKE, batch=2, total_q=8, max_draft_k=4, num_pages=10,
+             max_pages=5, page_size=16, hq=8, hkv=2, d=128, max_total_ctx=100, split=0,
+             scale=0.088, out=FAKE, ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.sd_draft_attn(a["q"], a["k_blk"], a["v_blk"], a["k_cache"], a["v_cache"],
+                             a["page_table"], a["ctx_len"], a["q_off"], a["batch"],
+                             a["total_q"], a["max_draft_k"], a["num_pages"], a["max_pages"],
+                             a["page_size"], a["hq"], a["hkv"], a["d"], a["max_total_ctx"],
+                             a["split"], a["scale"], a["out"], a["ws"], a["ws_bytes"],
+                             a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(page_table=None), 1), (dict(out=None), 1),
+    (dict(batch=0), 2), (dict(page_size=32), 2), (dict(d=96), 2), (dict(hq=6, hkv=4), 2),
+    (dict(max_draft_k=17), 2),            # group 4 * 17 > 64 query rows
+    (dict(split=100), 2), (dict(scale=float("inf")), 2), (dict(q=ODD), 2),
+    (dict(ws=None), 3), (dict(ws_bytes=10), 3),
+    (dict(total_q=0), 0),                 # nothing to do: returns before launching
+])
+def test_draft_attn_validation(lib, kw, status):
+    assert _attn(lib, **kw) == status
+
+
+def _lm(lib, **kw):
+    a = dict(hidden=FAKE, w=FAKE, M=16, H=256, V=1024, q_off=FAKE, batch=1, req=FAKE, seed=1,
+             logits=FAKE, lse=FAKE, tok=FAKE, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.sd_lm_head_probs(a["hidden"], a["w"], a["M"], a["H"], a["V"], a["q_off"],
+                                a["batch"], a["req"], a["seed"], a["logits"], a["lse"],
+                                a["tok"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=None), 1), (dict(req=None), 1), (dict(tok=None), 1),
+    (dict(M=0), 2), (dict(H=100), 2), (dict(H=0), 2), (dict(V=0), 2), (dict(logits=ODD), 2),
+    (dict(ws=None), 3), (dict(ws_bytes=1), 3),
+])
+def test_lm_head_validation(lib, kw, status):
+    assert _lm(lib, **kw) == status
+
+
+def _vf(lib, **kw):
+    a = dict(target=FAKE, t_off=FAKE, draft=FAKE, lse=None, tok=FAKE, q_off=FAKE, batch=2,
+             total_q=8, R=10, V=1024, req=FAKE, seed=3, acc=FAKE, nxt=FAKE, ratio=None,
+             ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.sd_verify(a["target"], a["t_off"], a["draft"], a["lse"], a["tok"], a["q_off"],
+                         a["batch"], a["total_q"], a["R"], a["V"], a["req"], a["seed"],
+                         a["acc"], a["nxt"], a["ratio"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(target=None), 1), (dict(acc=None), 1), (dict(draft=None), 1),
+    (dict(batch=0), 2), (dict(R=0), 2), (dict(V=0), 2),
+    (dict(ws=None), 3), (dict(ws_bytes=5), 3),
+])
+def test_verify_validation(lib, kw, status):
+    assert _vf(lib, **kw) == status
+
+
+def test_python_binding_rejects_cpu_dtype_mismatch():
+    import torch
+    x = torch.zeros(4, 4, dtype=torch.float32)
+    with pytest.raises(TypeError):
+        sd.sd_lm_head_probs(x, x, torch.zeros(2, dtype=torch.int32),
+                            torch.zeros(1, dtype=torch.int32), 0)

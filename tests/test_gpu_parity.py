@@ -1,0 +1,147 @@
+"""GPU parity: the HIP library through its C ABI against the CPU oracle.
+
+Attention outputs within 1e-2 max-abs; probabilities within 1e-5; draft
+tokens, accepted lengths and next tokens exact except audited near-ties
+(|u - r| < 1e-5 or a Gumbel top-2 key gap < 1e-5).
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_drafting_sd_amd as sd
+from oracle import compare, lm_head as olm, step as ostep, verify as overify
+from synth import StepInputs, device as sdev
+from synth.configs import C0_TINY, C1_32K, C3_VERIFY, C4_RAGGED, small
+
+from gpu_common import (DEV, bits, gpu_attention, gpu_lm_head, log, oracle_attention,
+                        request_rows, requires_gpu)
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+# ------------------------------------------------------------------ attention
+
+def _edge_cfg(**kw):
+    base = dict(name="attn_edge", batch=5, ctx=("list", (0, 1, 37, 160, 1000)),
+                draft_k=("list", (3, 1, 16, 5, 8)), verify="full", num_heads_q=8,
+                num_heads_kv=2, head_dim=128, hidden=64, vocab=64, seed=4242)
+    base.update(kw)
+    return C1_32K.with_(**base)
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("split", [0, 64, 192])
+def test_attention_edge_shapes(head_dim, split):
+    inp = StepInputs(_edge_cfg(head_dim=head_dim))
+    log(f"attention edge D={head_dim} split={split}")
+    rep = compare.attention_report(gpu_attention(inp, split_tokens=split), oracle_attention(inp))
+    log(str(rep))
+    assert rep["ok"] and rep["rel_l2"] < 1e-2
+
+
+def test_attention_tiny_workload():
+    inp = StepInputs(C0_TINY)
+    rep = compare.attention_report(gpu_attention(inp), oracle_attention(inp))
+    log(str(rep))
+    assert rep["ok"] and rep["rel_l2"] < 1e-2
+
+
+def test_attention_peaked_queries():
+    inp = StepInputs(_edge_cfg(q_scale=8.0, seed=99))
+    rep = compare.attention_report(gpu_attention(inp), oracle_attention(inp))
+    log(str(rep))
+    assert rep["ok"] and rep["rel_l2"] < 2e-2
+
+
+def test_attention_mha_and_small_groups():
+    inp = StepInputs(_edge_cfg(num_heads_q=4, num_heads_kv=4, head_dim=64))
+    rep = compare.attention_report(gpu_attention(inp), oracle_attention(inp))
+    log(str(rep))
+    assert rep["ok"]
+
+
+# -------------------------------------------------------------------- LM head
+
+@pytest.mark.parametrize("M,H,V", [(16, 256, 1024), (5, 64, 1000), (130, 128, 1001),
+                                   (257, 512, 4096)])
+def test_lm_head_shapes(M, H, V):
+    cfg = C0_TINY.with_(name="lm", batch=1, draft_k=M, hidden=H, vocab=V, seed=M * 7 + V)
+    inp = StepInputs(cfg)
+    z, lse, tok = gpu_lm_head(inp)
+    ref = ostep.run_lm_head(inp.hidden, inp.w_vocab, inp.budgets.q_off, inp.req_id,
+                            inp.philox_seed)
+    rep = compare.lm_head_report(z, lse, tok, ref)
+    log(f"lm_head M={M} H={H} V={V} {rep}")
+    assert rep["ok"]
+    assert rep["logit_max_abs"] < 1e-5
+
+
+def test_lm_head_qwen_vocab_sampled_rows():
+    cfg = small(C1_32K, batch=3, ctx=16)
+    inp = StepInputs(cfg)
+    z, lse, tok = gpu_lm_head(inp)
+    rows = np.array([0, 1, 15, 16, 31, 47])
+    ref = ostep.run_lm_head(inp.hidden, inp.w_vocab, inp.budgets.q_off, inp.req_id,
+                            inp.philox_seed, rows=rows)
+    rep = compare.lm_head_report(z, lse, tok, ref)
+    log(f"lm_head qwen vocab {rep}")
+    assert rep["ok"]
+
+
+# --------------------------------------------------------------------- verify
+
+def _verify_gpu(inp, draft_logits, draft_tokens, draft_lse=None):
+    t = sdev.verify_tensors(inp, DEV)
+    dl = torch.from_numpy(draft_logits).to(DEV)
+    dt = torch.from_numpy(draft_tokens.astype(np.int32)).to(DEV)
+    lse = None if draft_lse is None else torch.from_numpy(draft_lse.astype(np.float32)).to(DEV)
+    acc, nxt, ratio = sd.sd_verify(t["target_logits"], t["t_off"], dl, lse, dt, t["q_off"],
+                                   t["req_id"], inp.philox_seed)
+    torch.cuda.synchronize()
+    return acc.cpu().numpy(), nxt.cpu().numpy(), ratio.cpu().numpy()
+
+
+@pytest.mark.parametrize("verify_mode", ["full", "uniform", "zero"])
+@pytest.mark.parametrize("V", [1000, 8193, 20000])
+def test_verify_only_random_drafts(verify_mode, V):
+    cfg = C0_TINY.with_(name="verify", batch=24, ctx=16, draft_k=(1, 4, 16), verify=verify_mode,
+                        vocab=V, seed=V + len(verify_mode), target=("normal", 1.0))
+    inp = StepInputs(cfg)
+    b = inp.budgets
+    dl = inp.random_draft_logits(sigma=1.0)
+    dt = inp.random_draft_tokens()
+    acc, nxt, ratio = _verify_gpu(inp, dl, dt)
+    ref = overify.verify(inp.target_logits, b.t_off, dl, dt, b.q_off, inp.req_id,
+                         inp.philox_seed)
+    rep = compare.verify_report(acc, nxt, ref, range(cfg.batch))
+    rr = compare.ratio_report(ratio, ref, b.q_off, range(cfg.batch))
+    log(f"verify {verify_mode} V={V} {rep} ratio {rr}")
+    assert rep["ok"] and rr["max_abs"] < 1e-5
+
+
+def test_verify_drafts_from_q_accept_often():
+    # target = draft logits + small noise: long accepted runs, bonus tokens
+    cfg = C0_TINY.with_(name="verify_close", batch=32, ctx=16, draft_k=8, verify="full",
+                        vocab=3000, seed=5, target=("normal", 1.0))
+    inp = StepInputs(cfg)
+    b = inp.budgets
+    dl = inp.random_draft_logits(sigma=1.0)
+    rq, pos = olm.row_owner(b.q_off)
+    dt, _ = olm.draft_tokens(dl.astype(np.float64), rq, pos, inp.req_id, inp.philox_seed)
+    rng = np.random.default_rng(0)
+    src = np.concatenate([np.r_[np.arange(b.q_off[i], b.q_off[i + 1]), b.q_off[i + 1] - 1]
+                          for i in range(cfg.batch)])
+    tgt = (dl[src] + rng.standard_normal((len(src), cfg.vocab)) * 0.1).astype(np.float32)
+    inp.__dict__["target_logits"] = tgt
+    acc, nxt, ratio = _verify_gpu(inp, dl, dt)
+    ref = overify.verify(tgt, b.t_off, dl, dt, b.q_off, inp.req_id, inp.philox_seed)
+    rep = compare.verify_report(acc, nxt, ref, range(cfg.batch))
+    log(f"verify close {rep}")
+    assert rep["ok"] and rep["mean_accepted"] > 4
+
+
+# ---------------------------------------------------------------- whole step
+
+def test_step_tiny_end_to_end():
+    from __graft_entry__ import smoke
+    smoke()
