@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Throughput of one block-parallel draft-and-verify step on one MI355X.
+
+Default workload: 16 requests with 131072-token prefixes (Qwen3-8B shapes:
+32 query / 8 KV heads, head dim 128, 16-token pages with a shuffled page
+table, 8 GiB of bf16 prefix KV), a block of K = 16 drafts per request, an
+LM head of 4096 x 151936, and full verification of the 16 drafts against 17
+target rows per request.  A step = draft attention + LM head/sampling +
+verification over one batch; inputs are resident in HBM before timing.
+
+Prints ONE JSON line: drafted+verified tokens/s (sum of K_b per step / step
+time), the attention call's achieved HBM bandwidth against the 8 TB/s peak,
+and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(inp, n_req: int = 1):
+    """The oracle as it stands, on the first ``n_req`` requests of the workload
+    (attention over all KV heads, LM head rows, verification); scaled to
+    drafted+verified tokens/s."""
+    import numpy as np
+    from oracle import step as ostep, verify as overify
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    b = inp.budgets
+    reqs = list(range(n_req))
+    rows = np.concatenate([np.arange(b.q_off[r], b.q_off[r + 1]) for r in reqs])
+    t0 = time.perf_counter()
+    ostep.run_attention(inp.q, inp.k_blk, inp.v_blk, inp.k_cache, inp.v_cache, inp.page_table,
+                        b.ctx_len, b.q_off, inp.cfg.num_heads_kv, inp.softmax_scale,
+                        requests=reqs)
+    t1 = time.perf_counter()
+    lm = ostep.run_lm_head(inp.hidden, inp.w_vocab, b.q_off, inp.req_id, inp.philox_seed,
+                           rows=rows)
+    t2 = time.perf_counter()
+    full_z = np.zeros((inp.total_q, inp.cfg.vocab), np.float64)
+    full_z[rows] = lm["logits"]
+    tok = np.zeros(inp.total_q, np.int32)
+    tok[rows] = lm["tokens"]
+    overify.verify(inp.target_logits, b.t_off, full_z, tok, b.q_off, inp.req_id,
+                   inp.philox_seed, requests=reqs)
+    t3 = time.perf_counter()
+    tokens = int(sum(b.draft_k[r] for r in reqs))
+    return {"value": tokens / (t3 - t0), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"{n_req} of {inp.cfg.batch} requests: attention over all "
+                       f"{inp.cfg.num_heads_kv} KV heads at N={int(b.ctx_len[0])}, LM head on "
+                       f"{len(rows)} rows x {inp.cfg.vocab}, verification; "
+                       f"attn {t1 - t0:.2f}s lm {t2 - t1:.2f}s verify {t3 - t2:.2f}s")}
+
+
+def copy_calibration(gib: float):
+    """A plain device copy of known size, for scaling PMC byte counters."""
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {n * 4} bytes read and written per copy, 3 copies")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload index (default 2: 128K, batch 16)")
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-requests", type=int, default=1)
+    ap.add_argument("--calibrate-copy", type=float, default=0.0,
+                    help="GiB: also run a plain device copy of this size (PMC calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is "
+                                   "described in DESIGN.md, not implemented",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_drafting_sd_amd as sd
+    from block_drafting_sd_amd.step import DraftVerifyStep, StepShape
+    from synth import StepInputs, by_index, device as sdev
+
+    sd.load()
+    dev = torch.device("cuda:0")
+    cfg = by_index(args.config)
+    inp = StepInputs(cfg)
+    b = inp.budgets
+    t_gen = time.perf_counter()
+    log(f"[bench] generating inputs for {cfg.name} ...")
+    t = {}
+    t.update(sdev.attention_tensors(inp, dev))
+    t.update(sdev.lm_head_tensors(inp, dev))
+    t.update(sdev.verify_tensors(inp, dev))
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident in HBM ({time.perf_counter() - t_gen:.1f}s)")
+    shape = StepShape(batch=cfg.batch, total_q=inp.total_q,
+                      total_target_rows=inp.total_target_rows, num_heads_q=cfg.num_heads_q,
+                      num_heads_kv=cfg.num_heads_kv, head_dim=cfg.head_dim, hidden=cfg.hidden,
+                      vocab=cfg.vocab, max_total_ctx=inp.max_total_ctx,
+                      max_draft_k=int(b.draft_k.max()), split_tokens=args.split_tokens)
+    step = DraftVerifyStep(shape, dev)
+    seed = inp.philox_seed
+
+    if args.calibrate_copy > 0:
+        copy_calibration(args.calibrate_copy)
+
+    for i in range(args.warmup):
+        step.run(t, seed + i)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done")
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record()
+        step.attention(t)
+        e[1].record()
+        step.lm_head(t, seed + 1000 + i)
+        e[2].record()
+        step.verify(t, seed + 1000 + i)
+        e[3].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    log(f"[bench] timed {args.steps} steps in {elapsed:.3f}s")
+
+    attn_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    lm_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    ver_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    tokens_per_step = int(b.draft_k.sum())
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = tokens_per_step * args.steps / elapsed
+    emitted = int(step.accepted.sum().item()) + cfg.batch
+
+    c = cfg
+    kv_bytes = int(b.ctx_len.astype(np.int64).sum()) * c.num_heads_kv * c.head_dim * 2 * 2
+    blk_bytes = inp.total_q * c.num_heads_kv * c.head_dim * 2 * 2
+    q_out_bytes = 2 * inp.total_q * c.num_heads_q * c.head_dim * 2
+    attn_bytes = kv_bytes + blk_bytes + q_out_bytes
+    attn_avg_s = float(attn_ms.mean()) * 1e-3
+    attn_gbs = attn_bytes / attn_avg_s / 1e9
+    lm_flops = 2.0 * inp.total_q * c.hidden * c.vocab
+    lm_tflops = lm_flops / (float(lm_ms.mean()) * 1e-3) / 1e12
+
+    out = {
+        "metric": "drafted+verified tokens/s at 128K ctx, batch 16; attn HBM GB/s % of peak",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian inputs of the workload's shapes; no trained weights)",
+        "config": {"workload": c.name, "batch": c.batch, "prefix_tokens": int(b.ctx_len.max()),
+                   "draft_k": int(b.draft_k.max()), "num_heads_q": c.num_heads_q,
+                   "num_heads_kv": c.num_heads_kv, "head_dim": c.head_dim,
+                   "page_size": c.page_size, "hidden": c.hidden, "vocab": c.vocab,
+                   "split_tokens": args.split_tokens or "auto"},
+        "roofline": {"kernel": "sd_draft_attn (attn_worklist + attn_splitk + attn_combine)",
+                     "bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes": attn_bytes,
+                     "avg_ms": round(float(attn_ms.mean()), 4)},
+        "breakdown_ms": {"attention": round(float(attn_ms.mean()), 4),
+                         "lm_head": round(float(lm_ms.mean()), 4),
+                         "verify": round(float(ver_ms.mean()), 4)},
+        "lm_head": {"tflops": round(lm_tflops, 1),
+                    "frac_mfma_bf16": round(lm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "w_hbm_gbs": round(c.vocab * c.hidden * 2 / (float(lm_ms.mean()) * 1e-3) / 1e9, 1)},
+        "emitted_tokens_per_step_last": emitted,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_requests)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
