@@ -17,6 +17,6 @@ Modules:
 Every function is pinned by ``tests/test_oracle_*.py`` against facts the
 pages and the mathematics fix (the lossless theorem by exact enumeration,
 closed-form acceptance rates, decode-attention and SDPA special cases,
-published Philox known-answer vectors, chi-square tests of the samplers).
+bit-exact agreement of Philox with rocRAND's implementation, chi-square tests of the samplers).
 """
 from . import attention, lm_head, philox, step, verify  # noqa: F401

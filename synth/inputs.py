@@ -319,49 +319,56 @@ class StepInputs:
 
     @cached_property
     def target_logits(self) -> np.ndarray:
+        """fp32 ``[R, V]`` target logits of the ``("normal", sigma)`` workloads.
+        The drafter-plus-noise workload is built by ``target_from_drafter``
+        from drafter logits the caller supplies."""
         c = self.cfg
+        if c.target[0] != "normal":
+            raise ValueError(f"{c.name}: target logits depend on the drafter's; "
+                             "build them with target_from_drafter(drafter_logits)")
         R, V = self.total_target_rows, c.vocab
         bud = self.budgets
         out = np.empty((R, V), np.float32)
         row_req = np.repeat(np.arange(c.batch), np.diff(bud.t_off))
         n_chunks = (R + TGT_ROWS_PER_CHUNK - 1) // TGT_ROWS_PER_CHUNK
         sig = self.target_sigma
-        if c.target[0] == "normal":
-            def work(ch):
-                lo = ch * TGT_ROWS_PER_CHUNK
-                hi = min(R, lo + TGT_ROWS_PER_CHUNK)
-                x = _rng(c.seed, TAG_TGT, ch).standard_normal((hi - lo, V),
-                                                             dtype=np.float32)
-                x *= sig[row_req[lo:hi], None].astype(np.float32)
-                out[lo:hi] = x
-        else:
-            base = self._drafter_logits_for_target()
-            src = self.target_row_source()
 
-            def work(ch):
-                lo = ch * TGT_ROWS_PER_CHUNK
-                hi = min(R, lo + TGT_ROWS_PER_CHUNK)
-                x = _rng(c.seed, TAG_NOISE, ch).standard_normal((hi - lo, V))
-                x *= sig[row_req[lo:hi], None]
-                x += base[src[lo:hi]]
-                out[lo:hi] = x.astype(np.float32)
+        def work(ch):
+            lo = ch * TGT_ROWS_PER_CHUNK
+            hi = min(R, lo + TGT_ROWS_PER_CHUNK)
+            x = _rng(c.seed, TAG_TGT, ch).standard_normal((hi - lo, V), dtype=np.float32)
+            x *= sig[row_req[lo:hi], None].astype(np.float32)
+            out[lo:hi] = x
 
         with ThreadPoolExecutor(_threads()) as ex:
             list(ex.map(work, range(n_chunks)))
         return out
 
-    def _drafter_logits_for_target(self) -> np.ndarray:
-        """hidden @ W^T in float64 from the bf16 inputs: only used to *build*
-        the correlated target logits of the drafter-plus-noise workload."""
-        import torch
-        h = torch.from_numpy(self.hidden.astype(np.uint32) << 16).view(torch.float32)
-        w = torch.from_numpy(self.w_vocab.astype(np.uint32) << 16).view(torch.float32)
-        M, V = h.shape[0], w.shape[0]
-        out = np.empty((M, V), np.float64)
-        step = 16384
-        hd = h.double()
-        for lo in range(0, V, step):
-            out[:, lo:lo + step] = (hd @ w[lo:lo + step].double().T).numpy()
+    def target_from_drafter(self, drafter_logits: np.ndarray) -> np.ndarray:
+        """Target logits of the drafter-plus-noise workload: for every target
+        row, the drafter logits of the row ``target_row_source`` names plus
+        seeded N(0, sigma_b^2) noise, rounded to fp32.  ``drafter_logits``
+        ``[total_q, V]`` come from whoever evaluates the drafter's LM head."""
+        c = self.cfg
+        R, V = self.total_target_rows, c.vocab
+        bud = self.budgets
+        assert drafter_logits.shape == (self.total_q, V)
+        out = np.empty((R, V), np.float32)
+        row_req = np.repeat(np.arange(c.batch), np.diff(bud.t_off))
+        n_chunks = (R + TGT_ROWS_PER_CHUNK - 1) // TGT_ROWS_PER_CHUNK
+        sig = self.target_sigma
+        src = self.target_row_source()
+
+        def work(ch):
+            lo = ch * TGT_ROWS_PER_CHUNK
+            hi = min(R, lo + TGT_ROWS_PER_CHUNK)
+            x = _rng(c.seed, TAG_NOISE, ch).standard_normal((hi - lo, V))
+            x *= sig[row_req[lo:hi], None]
+            x += drafter_logits[src[lo:hi]]
+            out[lo:hi] = x.astype(np.float32)
+
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, range(n_chunks)))
         return out
 
     # ----------------------------------------------------------------- misc
