@@ -31,6 +31,15 @@ HIP_FLAGS = [
 ]
 
 
+# Extra flags for single sources.  The attention kernel keeps its MFMA
+# accumulators in ordinary VGPRs: the softmax reads every score and rescales
+# the output accumulators, which would otherwise cost a copy out of (and back
+# into) the accumulation registers per tile.
+FILE_FLAGS = {
+    "attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -50,7 +59,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         objs, procs = [], []
         for s in srcs:
             o = os.path.join(tmp, os.path.basename(s) + ".o")
-            cmd = [cc, *HIP_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", s, "-o", o]
+            cmd = [cc, *HIP_FLAGS, *FILE_FLAGS.get(os.path.basename(s), []),
+                   f"-I{INCLUDE}", f"-I{CSRC}", "-c", s, "-o", o]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((s, subprocess.Popen(cmd, stdout=subprocess.PIPE,

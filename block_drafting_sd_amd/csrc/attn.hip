@@ -13,28 +13,43 @@
 //   output and log-sum-exp), which `attn_combine` merges with the log-sum-exp
 //   rule of "LongSpark", App. A.2, eq. (11).
 //
-// Inner tile (one wave): 32 keys = two 16-token pages.
+// Prefix items stream the cache through a ring of NS LDS stages of 32 keys
+// (two 16-token pages, 128*D bytes) filled by gfx950 direct-to-LDS loads
+// (global_load_lds_dwordx4): a load writes 16 bytes per lane straight into
+// LDS without passing through registers, so NS-1 stages (NS-1 x 16 KiB at
+// D = 128) are in flight per workgroup while the current one is computed.
+// Wave 0 fetches the stage's keys, wave 1 its values; each 1 KiB wave load is
+// laid out so that lane l of the consuming wave reads its MFMA operand at
+// byte 16 l of a 1 KiB chunk (conflict-free ds_read_b128).  The waits are
+// explicit: a wave waits for its own loads of the stage (vmcnt), then a
+// workgroup barrier publishes the stage to both waves and frees the stage
+// computed in the previous iteration for the next loads.
+//
+// Inner tile (per wave, 32 query rows x 32 keys):
 //   S^T[32 keys x 32 queries] = K * Q^T      (MFMA 32x32x16 bf16, D/16 steps)
-//   O^T[D x 32 queries]     += V^T * P^T     (MFMA 32x32x16 bf16, 2 steps)
+//   O^T[D x 32 queries]     += V^T * P^T     (MFMA 32x32x16 bf16, 2 per 32 dims)
 // The key order inside a tile is permuted so that the softmax values a lane
 // holds after the first product are exactly the B operand of the second one
-// (no LDS round trip), and so that every K and V operand is one coalesced
-// 16-byte load from the cache layouts [page][g][D/8][16][8] and [page][g][D][16].
+// (no LDS round trip).  Both waves compute from the same stage: wave w owns
+// query rows 32w .. 32w+31 of the item's (up to) 64 rows.
 #include "sd_common.h"
 #include "sd_internal.h"
 
 #include <float.h>
 
+#include <type_traits>
+
 namespace sd {
 
 int32_t attn_split_tokens(int32_t hkv, int64_t max_total_ctx, int32_t requested) {
   if (requested > 0) return requested;
-  // aim for ~2048 prefix work items (8 per CU), at least 256 tokens each
+  // aim for ~2048 prefix work items (8 per CU), at least 256 tokens each and
+  // at most the page ids one workgroup stages in LDS
   const int64_t target_items = 2048;
   int64_t s = (static_cast<int64_t>(hkv) * max_total_ctx + target_items - 1) / target_items;
   s = (s + 255) / 256 * 256;
   if (s < 256) s = 256;
-  if (s > 65536) s = 65536;
+  if (s > kAttnMaxSplitPages * 16) s = kAttnMaxSplitPages * 16;
   return static_cast<int32_t>(s);
 }
 
@@ -106,28 +121,6 @@ __device__ __forceinline__ void tile_row_key(int rho, int& page_sel, int& slot) 
   slot = 8 * hp + 4 * (a & 1) + bq;
 }
 
-template <int D>
-__device__ __forceinline__ void load_cache_tile(const AttnArgs& a, int g, int pg0, int pg1,
-                                                int lane, KvTile<D>& t) {
-  const int h = lane >> 5;
-  int sel, slot;
-  tile_row_key(lane & 31, sel, slot);
-  const int pk = sel ? pg1 : pg0;
-  const uint16_t* kb = a.k_cache + (static_cast<size_t>(pk) * a.hkv + g) * (D / 8) * 128 + slot * 8;
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) t.k[s] = load_bf16x8(kb + (2 * s + h) * 128);
-#pragma unroll
-  for (int m = 0; m < D / 32; ++m) {
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int pg = p ? pg1 : pg0;
-      const uint16_t* vb = a.v_cache +
-                           ((static_cast<size_t>(pg) * a.hkv + g) * D + 32 * m + (lane & 31)) * 16 + 8 * h;
-      t.v[m][p] = load_bf16x8(vb);
-    }
-  }
-}
-
 // Draft-block keys/values [total_q][hkv][D], tile keys kappa = base..base+31.
 template <int D>
 __device__ __forceinline__ void load_block_tile(const AttnArgs& a, int g, int q0, int kb,
@@ -162,11 +155,20 @@ template <int D>
 struct AttnState {
   bf16x8 q[D / 16];          // B operands Q^T of this wave's 32 query rows
   f32x16 o[D / 32];          // O^T accumulators, one per 32-dim tile
-  float m, l;                // running max (raw score units), partial sum
+  float m, l;                // exponent reference (log2 units), partial sum
 };
 
+// Growth of the running maximum (log2 units) tolerated before the output is
+// rescaled: probabilities are then at most 2^8 before normalisation, far
+// from fp32 / bf16 overflow, and the rescale (a pass over every accumulator)
+// runs only a handful of times per work item.
+constexpr float kRescaleLog2 = 8.f;
+
 // One 32-key tile: scores, online softmax, P V.  `valid` = number of keys of
-// the tile that exist (keys past it are masked).
+// the tile that exist (keys past it are masked).  st.m is a running upper
+// bound on nothing: it is the reference point of the exponentials, raised to
+// the tile maximum only when that exceeds it by more than kRescaleLog2 (the
+// softmax is invariant to the choice; "LongSpark", App. A.2, eq. (11)).
 template <int D>
 __device__ __forceinline__ void attend_tile(AttnState<D>& st, const KvTile<D>& t, int valid,
                                             float sl2, int lane) {
@@ -184,24 +186,27 @@ __device__ __forceinline__ void attend_tile(AttnState<D>& st, const KvTile<D>& t
   float mx = s[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-  mx = fmaxf(mx, xor_shuffle(mx, 32));
-  const float m_new = fmaxf(st.m, mx);
-  const float alpha = __builtin_amdgcn_exp2f((st.m - m_new) * sl2);
-  float p[16];
-  float ps = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    p[i] = __builtin_amdgcn_exp2f((s[i] - m_new) * sl2);
-    ps += p[i];
-  }
-  st.l = st.l * alpha + ps;
-  st.m = m_new;
-  if (__any(alpha != 1.f)) {
+  mx = fmaxf(mx, xor_shuffle(mx, 32)) * sl2;        // log2 units
+  const bool raise = mx > st.m + kRescaleLog2;       // always true on the first tile
+  if (__any(raise)) {
+    const float m_new = raise ? mx : st.m;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    st.l *= alpha;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt) st.o[mt] *= alpha;
+    st.m = m_new;
   }
+  float p[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sl2, -st.m));
   const bf16x8 p0 = pack_bf16x8(p);
   const bf16x8 p1 = pack_bf16x8(p + 8);
+  // The normaliser sums the same bf16-rounded weights that multiply V, so the
+  // rounding of a dominant weight cancels in O / l.
+  float ps = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ps += static_cast<float>(p0[i]) + static_cast<float>(p1[i]);
+  st.l += ps;
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) {
     st.o[mt] = mfma_32x32x16(t.v[mt][0], p0, st.o[mt]);
@@ -209,11 +214,114 @@ __device__ __forceinline__ void attend_tile(AttnState<D>& st, const KvTile<D>& t
   }
 }
 
-// One workgroup per work item; wave w owns query rows 32w .. 32w+31 of the
-// item's (up to) 64 rows.  Both waves stream the same keys, so the second
-// wave's requests are served by the CU's L1 / the XCD's L2, not HBM.
+// ------------------------------------------------------- LDS-staged stream
+typedef __attribute__((address_space(3))) char lds_char;
+
+// One direct-to-LDS load: lane l's 16 bytes at `src` land at LDS byte
+// address lds + 16 l (lds wave-uniform, passed in m0).  The instruction's
+// immediate offset is left at 0: the hardware adds it to the LDS address as
+// well as to the global one.  Written as inline assembly so that the
+// compiler does not tie later LDS reads to it with a blanket wait for every
+// load in flight; the stream's waits are explicit (wait_vmcnt) instead.
+__device__ __forceinline__ void dma16(const uint16_t* src, uint32_t lds) {
+  // one wait state between the m0 write and the load that reads it
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      ::"v"(src), "s"(lds)
+      : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)(p))));
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait for the loads of the oldest stage when `ahead` newer stages (L loads
+// each) may stay in flight; ahead in [0, C].
+template <int L, int C>
+__device__ __forceinline__ void wait_stage(int ahead) {
+  if constexpr (C == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (ahead >= C) wait_vmcnt<C * L>();
+    else wait_stage<L, C - 1>(ahead);
+  }
+}
+
+// Workgroup barrier that the compiler may not move memory accesses across and
+// that, unlike __syncthreads(), does not first drain every load in flight.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Elements (uint16) of one stage: D/16 key chunks then D/16 value chunks of
+// 512 elements (1 KiB) each.
 template <int D>
-__global__ __launch_bounds__(128) void attn_splitk(AttnArgs a) {
+constexpr int stage_elems() { return (D / 8) * 512; }
+
+// Issue this wave's direct-to-LDS loads of one 32-key stage (pages pg0, pg1).
+//  wave 0: key chunk c (c < D/16): lane l = (row rho = l % 32, half h = l / 32)
+//          fetches dims 16 c + 8 h .. +8 of the key that S^T row rho holds.
+//  wave 1: value chunk (page p, dims 32 m ..): lane l fetches 8 tokens
+//          8 h .. 8 h + 7 of dim 32 m + l % 32.
+template <int D>
+__device__ __forceinline__ void issue_stage(const AttnArgs& a, int g, int pg0, int pg1, int wave,
+                                            int lane, uint16_t* stage) {
+  const int h = lane >> 5;
+  const uint32_t lds = lds_addr(stage);
+  if (wave == 0) {
+    int sel, slot;
+    tile_row_key(lane & 31, sel, slot);
+    const int pg = sel ? pg1 : pg0;
+    const uint16_t* src =
+        a.k_cache + (static_cast<size_t>(pg) * a.hkv + g) * (D * 16) + h * 128 + slot * 8;
+    static_for<0, D / 16>([&](auto c) { dma16(src + c * 256, lds + c * 1024); });
+  } else {
+    const size_t col = (lane & 31) * 16 + 8 * h;
+    const uint16_t* src0 = a.v_cache + (static_cast<size_t>(pg0) * a.hkv + g) * (D * 16) + col;
+    const uint16_t* src1 = a.v_cache + (static_cast<size_t>(pg1) * a.hkv + g) * (D * 16) + col;
+    static_for<0, D / 32>([&](auto m) {
+      dma16(src0 + m * 512, lds + (D / 16 + m) * 1024);
+      dma16(src1 + m * 512, lds + (D / 16 + D / 32 + m) * 1024);
+    });
+  }
+}
+
+// MFMA operands of one staged tile, read back from LDS (lane l reads bytes
+// 16 l .. 16 l + 15 of every 1 KiB chunk).
+template <int D>
+__device__ __forceinline__ void read_stage(const uint16_t* stage, int lane, KvTile<D>& t) {
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) t.k[c] = load_bf16x8(stage + c * 512 + lane * 8);
+#pragma unroll
+  for (int m = 0; m < D / 32; ++m)
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      t.v[m][p] = load_bf16x8(stage + (D / 16 + p * (D / 32) + m) * 512 + lane * 8);
+}
+
+// One workgroup (two waves) per work item; wave w owns query rows
+// 32w .. 32w+31 of the item's (up to) 64 rows.
+template <int D, int NS>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_splitk(AttnArgs a) {
+  static_assert(NS >= 2, "at least two stages");
+  __shared__ __attribute__((aligned(1024))) uint16_t s_kv[NS * stage_elems<D>()];
+  __shared__ int s_pages[kAttnMaxSplitPages];
+
   const int item = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -232,12 +340,12 @@ __global__ __launch_bounds__(128) void attn_splitk(AttnArgs a) {
   const int g = rel / (r.ns + 1);
   const int sp = rel % (r.ns + 1);
   const int rows = a.group * r.kb;
-  if (32 * wave >= rows) return;          // no query rows for this wave
-  const int h = lane >> 5;
+  const bool active = 32 * wave < rows;   // this wave has query rows
   const float sl2 = a.scale_log2;
 
   AttnState<D> st;
   {
+    const int h = lane >> 5;
     const int qi = 32 * wave + (lane & 31);
     const bool ok = qi < rows;
     const int j = ok ? qi / a.group : 0;
@@ -252,51 +360,55 @@ __global__ __launch_bounds__(128) void attn_splitk(AttnArgs a) {
   }
 
   if (sp < r.ns) {
-    // prefix split: tokens [t_begin, t_end), 32 per tile
+    // prefix split: tokens [t_begin, t_end), 32 per stage
     const int t_begin = sp * a.split_tokens;
     const int t_end = min(r.n, t_begin + a.split_tokens);
-    const int* pt = a.page_table + static_cast<size_t>(b) * a.max_pages;
-    auto pages = [&](int tt, int& p0, int& p1) {
-      const int lp = tt >> 4;
-      p0 = clampi(pt[lp], 0, a.num_pages - 1);
-      p1 = tt + 16 < t_end ? clampi(pt[lp + 1], 0, a.num_pages - 1) : p0;
-    };
-    // ping-pong between two register tiles: the next tile's loads are in
-    // flight while the current one is computed
-    KvTile<D> ta, tb;
-    int p0, p1;
-    pages(t_begin, p0, p1);
-    load_cache_tile<D>(a, g, p0, p1, lane, ta);
-    for (int tt = t_begin;;) {
-      if (tt + kAttnTile < t_end) {
-        pages(tt + kAttnTile, p0, p1);
-        load_cache_tile<D>(a, g, p0, p1, lane, tb);
+    const int n_pages = (t_end - t_begin + 15) >> 4;
+    const int* pt = a.page_table + static_cast<size_t>(b) * a.max_pages + (t_begin >> 4);
+    for (int i = threadIdx.x; i < 2 * ((n_pages + 1) >> 1); i += 128)
+      s_pages[i] = clampi(pt[min(i, n_pages - 1)], 0, a.num_pages - 1);
+    // Q operands loaded (a wait the compiler sees, so that it does not keep
+    // a wait for them inside the stream loop) and page ids visible
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    constexpr int L = D / 16;              // direct-to-LDS loads per wave per stage
+    const int n_tiles = (t_end - t_begin + kAttnTile - 1) / kAttnTile;
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t)
+      if (t < n_tiles)
+        issue_stage<D>(a, g, s_pages[2 * t], s_pages[2 * t + 1], wave, lane,
+                       s_kv + t * stage_elems<D>());
+    for (int t = 0; t < n_tiles; ++t) {
+      wait_stage<L, NS - 2>(n_tiles - 1 - t);
+      stage_barrier();
+      const int tn = t + NS - 1;           // refill the stage computed last iteration
+      if (tn < n_tiles)
+        issue_stage<D>(a, g, s_pages[2 * tn], s_pages[2 * tn + 1], wave, lane,
+                       s_kv + (tn % NS) * stage_elems<D>());
+      if (active) {
+        KvTile<D> kv;
+        read_stage<D>(s_kv + (t % NS) * stage_elems<D>(), lane, kv);
+        attend_tile<D>(st, kv, min(kAttnTile, t_end - t_begin - t * kAttnTile), sl2, lane);
       }
-      attend_tile<D>(st, ta, min(kAttnTile, t_end - tt), sl2, lane);
-      tt += kAttnTile;
-      if (tt >= t_end) break;
-      if (tt + kAttnTile < t_end) {
-        pages(tt + kAttnTile, p0, p1);
-        load_cache_tile<D>(a, g, p0, p1, lane, ta);
-      }
-      attend_tile<D>(st, tb, min(kAttnTile, t_end - tt), sl2, lane);
-      tt += kAttnTile;
-      if (tt >= t_end) break;
     }
   } else {
+    if (!active) return;
     for (int base = 0; base < r.kb; base += kAttnTile) {
       KvTile<D> t;
       load_block_tile<D>(a, g, r.q0, r.kb, base, lane, t);
       attend_tile<D>(st, t, min(kAttnTile, r.kb - base), sl2, lane);
     }
   }
+  if (!active) return;
 
   // normalised partial output and log2-sum-exp2 of the scaled scores
+  const int h = lane >> 5;
   float* po = a.part_o + static_cast<size_t>(item) * (D / 4) * kAttnRows * 4;
   const float l = st.l + xor_shuffle(st.l, 32);
   const float inv = 1.f / l;
   const int qi = 32 * wave + (lane & 31);
-  if (h == 0) a.part_lse[static_cast<size_t>(item) * kAttnRows + qi] = st.m * sl2 + log2f(l);
+  if (h == 0) a.part_lse[static_cast<size_t>(item) * kAttnRows + qi] = st.m + log2f(l);
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) {
 #pragma unroll
@@ -347,7 +459,7 @@ template <int D>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(attn_worklist, dim3(1), dim3(1024), 0, s, a);
   if (a.max_items > 0)
-    hipLaunchKernelGGL((attn_splitk<D>), dim3(a.max_items), dim3(128), 0, s, a);
+    hipLaunchKernelGGL((attn_splitk<D, kAttnStages>), dim3(a.max_items), dim3(128), 0, s, a);
   hipLaunchKernelGGL((attn_combine<D>), dim3(a.batch * a.hkv, D / 16), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -109,7 +109,8 @@ sd_status sd_draft_attn(const void* q, const void* k_blk, const void* v_blk, con
   if (batch < 1 || total_q < 0 || max_draft_k < 1 || num_pages < 1 || max_pages < 1 ||
       page_size != 16 || num_heads_kv < 1 || num_heads_q < num_heads_kv ||
       num_heads_q % num_heads_kv != 0 || (head_dim != 64 && head_dim != 128) ||
-      max_total_ctx < 0 || split_tokens < 0 || split_tokens % 64 != 0 || !isfinite(softmax_scale))
+      max_total_ctx < 0 || split_tokens < 0 || split_tokens % 64 != 0 ||
+      split_tokens > sd::kAttnMaxSplitPages * 16 || !isfinite(softmax_scale))
     return SD_ERR_SHAPE;
   const int32_t group = num_heads_q / num_heads_kv;
   if (static_cast<int64_t>(group) * max_draft_k > sd::kAttnRows) return SD_ERR_SHAPE;

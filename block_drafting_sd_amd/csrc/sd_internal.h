@@ -20,7 +20,7 @@ struct AttnArgs {
   uint16_t* out;
   int32_t batch, total_q, max_draft_k, num_pages, max_pages;
   int32_t hq, hkv, group;
-  int32_t split_tokens;   // prefix tokens per work item (multiple of 64)
+  int32_t split_tokens;   // prefix tokens per work item (multiple of 64, <= 8192)
   int32_t max_items;      // work items the partial buffers hold
   float scale_log2;       // softmax_scale * log2(e)
   int32_t* item_off;      // [batch + 1] first work item of each request
@@ -30,6 +30,8 @@ struct AttnArgs {
 
 constexpr int kAttnRows = 64;        // query rows per (request, kv head) item
 constexpr int kAttnTile = 32;        // keys per inner tile (two 16-token pages)
+constexpr int kAttnStages = 4;       // LDS ring stages of the prefix stream
+constexpr int kAttnMaxSplitPages = 512;   // split_tokens <= 512 * 16
 
 int64_t attn_max_items(int32_t batch, int32_t hkv, int64_t max_total_ctx,
                        int32_t split_tokens);

@@ -106,7 +106,7 @@ const char* sd_version(void);
  *   head_dim     64 or 128
  *   max_total_ctx  host upper bound on sum_b N_b (sizes the launch)
  *   split_tokens   prefix tokens per split-K work item; 0 lets the library
- *                  choose; otherwise a multiple of 64
+ *                  choose; otherwise a multiple of 64, at most 8192
  *   softmax_scale  usually 1/sqrt(head_dim)
  *   out      bf16 [total_q, Hq, D]
  * ------------------------------------------------------------------------ */
