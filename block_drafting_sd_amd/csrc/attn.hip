@@ -37,7 +37,6 @@
 
 #include <float.h>
 
-#include <type_traits>
 
 namespace sd {
 
@@ -215,59 +214,6 @@ __device__ __forceinline__ void attend_tile(AttnState<D>& st, const KvTile<D>& t
 }
 
 // ------------------------------------------------------- LDS-staged stream
-typedef __attribute__((address_space(3))) char lds_char;
-
-// One direct-to-LDS load: lane l's 16 bytes at `src` land at LDS byte
-// address lds + 16 l (lds wave-uniform, passed in m0).  The instruction's
-// immediate offset is left at 0: the hardware adds it to the LDS address as
-// well as to the global one.  Written as inline assembly so that the
-// compiler does not tie later LDS reads to it with a blanket wait for every
-// load in flight; the stream's waits are explicit (wait_vmcnt) instead.
-__device__ __forceinline__ void dma16(const uint16_t* src, uint32_t lds) {
-  // one wait state between the m0 write and the load that reads it
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      ::"v"(src), "s"(lds)
-      : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
-  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)(p))));
-}
-
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
-// Wait until at most N vector-memory operations of this wave are in flight.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Wait for the loads of the oldest stage when `ahead` newer stages (L loads
-// each) may stay in flight; ahead in [0, C].
-template <int L, int C>
-__device__ __forceinline__ void wait_stage(int ahead) {
-  if constexpr (C == 0) {
-    wait_vmcnt<0>();
-  } else {
-    if (ahead >= C) wait_vmcnt<C * L>();
-    else wait_stage<L, C - 1>(ahead);
-  }
-}
-
-// Workgroup barrier that the compiler may not move memory accesses across and
-// that, unlike __syncthreads(), does not first drain every load in flight.
-__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
 // Elements (uint16) of one stage: D/16 key chunks then D/16 value chunks of
 // 512 elements (1 KiB) each.
 template <int D>
@@ -457,11 +403,11 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
 
 template <int D>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(attn_worklist, dim3(1), dim3(1024), 0, s, a);
-  if (a.max_items > 0)
-    hipLaunchKernelGGL((attn_splitk<D, kAttnStages>), dim3(a.max_items), dim3(128), 0, s, a);
-  hipLaunchKernelGGL((attn_combine<D>), dim3(a.batch * a.hkv, D / 16), dim3(256), 0, s, a);
-  return hipGetLastError();
+  hipError_t e = launch_kernel(attn_worklist, dim3(1), dim3(1024), s, a);
+  if (e == hipSuccess && a.max_items > 0)
+    e = launch_kernel(attn_splitk<D, kAttnStages>, dim3(a.max_items), dim3(128), s, a);
+  if (e == hipSuccess) e = launch_kernel(attn_combine<D>, dim3(a.batch * a.hkv, D / 16), dim3(256), s, a);
+  return e;
 }
 
 }  // namespace

@@ -1,19 +1,27 @@
-// Drafter LM head: logits = hidden W^T on MFMA, fused with the draft
-// softmax statistics and Gumbel-max draft sampling ("LongSpark", sec. 2.1,
-// eq. (4) and App. A.1, Fig. 6: the frozen target vocabulary head produces
-// every slot's base logits in parallel and each slot is sampled
-// independently).
+// Drafter LM head: logits = hidden W^T on MFMA, then the draft softmax
+// statistics and Gumbel-max draft sampling ("LongSpark", sec. 2.1, eq. (4)
+// and App. A.1, Fig. 6: the frozen target vocabulary head produces every
+// slot's base logits in parallel and each slot is sampled independently).
 //
-// lm_gemm: one workgroup (4 waves) computes a 128-vocab x 128-row tile of
-// logits^T = W * hidden^T with MFMA 32x32x16 bf16 (fp32 accumulation); both
-// operands are H-contiguous and are staged through double-buffered LDS in
-// 64-wide K slices.  Each lane ends up owning one draft row and 32 vocab
-// entries, so the epilogue's row statistics are mostly in-lane: it stores the
-// fp32 logits, and writes per (row, vocab tile) the max, the sum of exp
-// relative to it and the best Gumbel-max candidate (Philox stream 0).
+// lm_gemm: one workgroup (4 waves, 2 x 2) computes a 128-vocab x 256-row
+// tile of logits^T = W * hidden^T with MFMA 32x32x16 bf16 (fp32
+// accumulation); each wave owns a 64 x 128 sub-tile (8 accumulator tiles).
+// Both operands are H-contiguous.  They stream through a ring of kNS LDS
+// stages of 32 hidden dims (8 KiB of W, 16 KiB of hidden per stage), filled by
+// direct-to-LDS loads: each 1 KiB wave load covers 16 rows x 64 bytes, so
+// global reads stay coalesced, and rows are stored with a 16-byte-chunk XOR
+// swizzle so the MFMA operand reads (32 rows, one chunk) are conflict-free.
+// The ring is small enough (72 KiB) for two workgroups to share a CU: each
+// SIMD then runs two waves whose barriers are independent, so one
+// workgroup's MFMAs cover the other's waits for loads and its epilogue.  At up
+// to 256 draft rows the whole W (1.2 GB) is read from HBM exactly once.
 // Tiles are ordered so that all row tiles of one vocab tile, and a compact
 // block of vocab tiles, run together on one XCD (blockIdx % 8 picks the XCD),
 // which keeps every W and hidden slice in that XCD's L2 across row tiles.
+// The epilogue stores the fp32 logits and writes per (row, vocab tile) the
+// max, the sum of exp relative to it and the best Gumbel-max candidate
+// (Philox stream 0); with two workgroups per CU its ALU work overlaps the
+// other workgroup's stream.
 //
 // lm_row_reduce: merges the per-tile statistics of a row into lse and the
 // draft token.
@@ -25,8 +33,21 @@
 namespace sd {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kLdk = kLmBK + 8;   // LDS row stride (elements); 144 B avoids bank conflicts
+constexpr int kThreads = 256;                       // every kernel: 4 waves
+constexpr int kNS = 3;                              // LDS stages
+constexpr int kWBytes = kLmBV * kLmBK * 2;          // W rows of one stage: 8 KiB
+constexpr int kHBytes = kLmBM * kLmBK * 2;          // hidden rows of one stage: 16 KiB
+constexpr int kStageBytes = kWBytes + kHBytes;      // 24 KiB; 3 stages let 2 workgroups share a CU
+constexpr int kWLoads = kWBytes / 1024 / 4;         // direct-to-LDS loads per wave per stage
+constexpr int kHLoads = kHBytes / 1024 / 4;
+constexpr int kLoadsPerWave = kWLoads + kHLoads;
+static_assert(kLmBV == 128 && kLmBM == 256 && kLmBK == 32, "stage layout assumes 128 x 256 tiles of 32 dims");
+static_assert(kWLoads == 2 && kHLoads == 4, "per wave: 2 W loads, 4 hidden loads");
+
+// 16-byte chunk c (of 4) of row r of a staged tile sits at byte
+// 64 r + 16 (c ^ swz(r)): eight consecutive rows of one chunk then fall in
+// eight different 16-byte bank groups.
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 
 __device__ __forceinline__ void row_owner(const LmArgs& a, int m, uint32_t& rid, uint32_t& pos) {
   // request b with q_off[b] <= m < q_off[b+1]
@@ -46,8 +67,9 @@ __device__ __forceinline__ void row_owner(const LmArgs& a, int m, uint32_t& rid,
   pos = static_cast<uint32_t>(m - a.q_off[lo] + 1);
 }
 
-__global__ __launch_bounds__(kThreads, 2) void lm_gemm(LmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (kLmBV + kLmBM) * kLdk];
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void lm_gemm(LmArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[kNS * kStageBytes];
   const int P = blockIdx.x;
   const int xcd = P & 7, slot = P >> 3;
   const int vt = (slot / a.n_mt) * 8 + xcd;
@@ -57,119 +79,134 @@ __global__ __launch_bounds__(kThreads, 2) void lm_gemm(LmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wv = wave & 1, wm = wave >> 1, h = lane >> 5;
 
-  // stage `buf`: W tile at smem + buf * stage, hidden tile right after it
-  constexpr int kStage = (kLmBV + kLmBM) * kLdk;
-  auto sA = [&](int buf) { return smem + buf * kStage; };
-  auto sB = [&](int buf) { return smem + buf * kStage + kLmBV * kLdk; };
-
-  u32x4 ra[4], rb[4];
-  auto gload = [&](int k0) {
+  // ------------------------------------------------ direct-to-LDS loads
+  // Wave w fetches W rows 32 w .. 32 w + 31 (loads q = 2 w, 2 w + 1) and
+  // hidden rows 64 w .. 64 w + 63 (loads q = 4 w .. 4 w + 3); load q covers
+  // rows 16 q .. 16 q + 15 of its tile and lane l fetches chunk
+  // (l & 3) ^ swz(row) of row 16 q + l / 4.  Rows past V (or M) read the last
+  // row instead and are never stored.
+  const uint16_t* src[kLoadsPerWave];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + kThreads * i, row = c >> 3, kc = c & 7;
-      const int v = v0 + row, m = m0 + row;
-      ra[i] = v < a.V ? *reinterpret_cast<const u32x4*>(a.w + static_cast<size_t>(v) * a.H + k0 + kc * 8)
-                      : u32x4{0u, 0u, 0u, 0u};
-      rb[i] = m < a.M ? *reinterpret_cast<const u32x4*>(a.hidden + static_cast<size_t>(m) * a.H + k0 + kc * 8)
-                      : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + kThreads * i, row = c >> 3, kc = c & 7;
-      store_u32x4(sA(buf) + row * kLdk + kc * 8, ra[i]);
-      store_u32x4(sB(buf) + row * kLdk + kc * 8, rb[i]);
-    }
+  for (int i = 0; i < kLoadsPerWave; ++i) {
+    const bool is_w = i < kWLoads;
+    const int q = is_w ? kWLoads * wave + i : kHLoads * wave + (i - kWLoads);
+    const int r = 16 * q + (lane >> 2);
+    const int c = (lane & 3) ^ swz(r);
+    src[i] = is_w ? a.w + static_cast<size_t>(min(v0 + r, a.V - 1)) * a.H + 8 * c
+                  : a.hidden + static_cast<size_t>(min(m0 + r, a.M - 1)) * a.H + 8 * c;
+  }
+  const uint32_t lds_ring = lds_addr(smem);
+  auto issue = [&](int kt) {
+    const uint32_t base = lds_ring + (kt % kNS) * kStageBytes;
+    static_for<0, kLoadsPerWave>([&](auto i) {
+      constexpr bool is_w = i < kWLoads;
+      const uint32_t dst = is_w ? base + (kWLoads * wave + i) * 1024
+                                : base + kWBytes + (kHLoads * wave + (i - kWLoads)) * 1024;
+      dma16(src[i] + kt * kLmBK, dst);
+    });
   };
 
-  f32x16 acc[2][2];
+  // ---------------------------------------------------- operand offsets
+  // A operand (W row 64 wv + 32 tv + l % 32) and B operand (hidden row
+  // 128 wm + 32 tm + l % 32), chunk 2 s + h of the stage's 32 dims.
+  const int rr = lane & 31;
+  const int sw = swz(rr);   // swz(32 k + rr) == swz(rr)
+  int offA[2], offB[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    offA[s] = (64 * wv + rr) * 64 + (((2 * s + h) ^ sw) << 4);
+    offB[s] = kWBytes + (128 * wm + rr) * 64 + (((2 * s + h) ^ sw) << 4);
+  }
+
+  f32x16 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
   const int nk = a.H / kLmBK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < kNS - 1; ++t)
+    if (t < nk) issue(t);
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * kLmBK);
+    // stage kt has landed; issued so far: stages up to kt + kNS - 2
+    wait_stage<kLoadsPerWave, kNS - 2>(nk - 1 - kt);
+    stage_barrier();
+    // refill the stage every wave finished reading last iteration
+    if (kt + kNS - 1 < nk) issue(kt + kNS - 1);
+    const char* st = smem + (kt % kNS) * kStageBytes;
 #pragma unroll
-    for (int s = 0; s < kLmBK / 16; ++s) {
-      bf16x8 af[2], bf[2];
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 af[2], bfr[4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int r = 64 * wv + 32 * t + (lane & 31);
-        af[t] = load_bf16x8(sA(buf) + r * kLdk + (2 * s + h) * 8);
-        const int cidx = 64 * wm + 32 * t + (lane & 31);
-        bf[t] = load_bf16x8(sB(buf) + cidx * kLdk + (2 * s + h) * 8);
-      }
+      for (int t = 0; t < 2; ++t)
+        af[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + offA[s] + t * 32 * 64));
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        bfr[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + offB[s] + t * 32 * 64));
 #pragma unroll
       for (int tv = 0; tv < 2; ++tv)
 #pragma unroll
-        for (int tm = 0; tm < 2; ++tm) acc[tv][tm] = mfma_32x32x16(af[tv], bf[tm], acc[tv][tm]);
+        for (int tm = 0; tm < 4; ++tm) acc[tv][tm] = mfma_32x32x16(af[tv], bfr[tm], acc[tv][tm]);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
   }
 
   // ---------------------------------------------------------------- epilogue
   // acc[tv][tm][i]: vocab v0 + 64 wv + 32 tv + 8 (i/4) + 4 h + i%4,
-  //                 row    m0 + 64 wm + 32 tm + lane%32
-  float* red = reinterpret_cast<float*>(smem);   // [2 (tm)][32][4] per wm, reused LDS
+  //                 row    m0 + 128 wm + 32 tm + lane%32
+  // Each lane holds 32 vocab entries of one row per row tile: it stores them
+  // and folds them into the row's (max, sum of exp, best Gumbel-max
+  // candidate) over this vocab tile; the two vocab waves (wv) merge through
+  // LDS (the ring is free once every wave is past the loop).
+  __syncthreads();
+  float4* red = reinterpret_cast<float4*>(smem);   // [wm][tm][32], written by wv = 1
   const bool vec_ok = (a.V & 3) == 0;
-#pragma unroll
-  for (int tm = 0; tm < 2; ++tm) {
-    const int m = m0 + 64 * wm + 32 * tm + (lane & 31);
+  static_for<0, 4>([&](auto TM) {
+    const int m = m0 + 128 * wm + 32 * TM + rr;
     const bool mok = m < a.M;
     uint32_t rid = 0, pos = 0;
     if (mok) row_owner(a, m, rid, pos);
     float mx = -FLT_MAX;
-#pragma unroll
-    for (int tv = 0; tv < 2; ++tv)
+    static_for<0, 2>([&](auto TV) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int v = v0 + 64 * wv + 32 * tv + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (v < a.V) mx = fmaxf(mx, acc[tv][tm][i]);
+        const int v = v0 + 64 * wv + 32 * TV + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (v < a.V) mx = fmaxf(mx, acc[TV][TM][i]);
       }
+    });
     float se = 0.f;
     Cand best{-FLT_MAX, 0x7fffffff};
+    if (mok) {
+      float* row = a.logits + static_cast<size_t>(m) * a.V;
+      static_for<0, 2>([&](auto TV) {
 #pragma unroll
-    for (int tv = 0; tv < 2; ++tv) {
-#pragma unroll
-      for (int ar = 0; ar < 4; ++ar) {
-        const int vb = v0 + 64 * wv + 32 * tv + 8 * ar + 4 * h;   // multiple of 4
-        const float z0 = acc[tv][tm][4 * ar], z1 = acc[tv][tm][4 * ar + 1];
-        const float z2 = acc[tv][tm][4 * ar + 2], z3 = acc[tv][tm][4 * ar + 3];
-        if (mok) {
-          float* dst = a.logits + static_cast<size_t>(m) * a.V + vb;
+        for (int ar = 0; ar < 4; ++ar) {
+          const int vb = v0 + 64 * wv + 32 * TV + 8 * ar + 4 * h;   // multiple of 4
+          const f32x4 z = {acc[TV][TM][4 * ar], acc[TV][TM][4 * ar + 1], acc[TV][TM][4 * ar + 2],
+                           acc[TV][TM][4 * ar + 3]};
           if (vec_ok && vb + 3 < a.V) {
-            *reinterpret_cast<f32x4*>(dst) = f32x4{z0, z1, z2, z3};
+            *reinterpret_cast<f32x4*>(row + vb) = z;
           } else {
-            if (vb < a.V) dst[0] = z0;
-            if (vb + 1 < a.V) dst[1] = z1;
-            if (vb + 2 < a.V) dst[2] = z2;
-            if (vb + 3 < a.V) dst[3] = z3;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (vb + e < a.V) row[vb + e] = z[e];
           }
           if (vb < a.V) {
             const u32x4 w = philox4x32_10(u32x4{static_cast<uint32_t>(vb >> 2), pos, rid, kStreamDraft},
                                           a.key0, a.key1);
-            const float zz[4] = {z0, z1, z2, z3};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               if (vb + e < a.V) {
-                se += __builtin_amdgcn_exp2f((zz[e] - mx) * kLog2e);
-                const float key = zz[e] + gumbel_from_bits(w[e]);
+                se += __builtin_amdgcn_exp2f((z[e] - mx) * kLog2e);
+                const float key = z[e] + gumbel_from_bits(w[e]);
                 if (better(key, vb + e, best.key, best.idx)) best = Cand{key, vb + e};
               }
             }
           }
         }
-      }
+      });
     }
-    // merge the two halves of the wave (same row, other vocab entries)
+    // the two halves of the wave hold the same row, other vocab entries
     {
       const float omx = xor_shuffle(mx, 32), ose = xor_shuffle(se, 32);
       const float nmx = fmaxf(mx, omx);
@@ -179,25 +216,18 @@ __global__ __launch_bounds__(kThreads, 2) void lm_gemm(LmArgs a) {
       const int oi = xor_shuffle(best.idx, 32);
       if (better(ok, oi, best.key, best.idx)) best = Cand{ok, oi};
     }
-    // merge the two vocab waves (wv = 0, 1) of this row block through LDS
-    float* slot4 = red + ((wm * 2 + tm) * 32 + (lane & 31)) * 4;
-    __syncthreads();
-    if (wv == 1 && h == 0) {
-      slot4[0] = mx;
-      slot4[1] = se;
-      slot4[2] = best.key;
-      slot4[3] = __int_as_float(best.idx);
-    }
+    float4* slot4 = red + (wm * 4 + TM) * 32 + rr;
+    if (wv == 1 && h == 0) *slot4 = make_float4(mx, se, best.key, __int_as_float(best.idx));
     __syncthreads();
     if (wv == 0 && h == 0 && mok) {
-      const float omx = slot4[0], ose = slot4[1], ok = slot4[2];
-      const int oi = __float_as_int(slot4[3]);
-      const float nmx = fmaxf(mx, omx);
-      se = se * __builtin_amdgcn_exp2f((mx - nmx) * kLog2e) + ose * __builtin_amdgcn_exp2f((omx - nmx) * kLog2e);
-      if (better(ok, oi, best.key, best.idx)) best = Cand{ok, oi};
+      const float4 o = *slot4;
+      const int oi = __float_as_int(o.w);
+      const float nmx = fmaxf(mx, o.x);
+      se = se * __builtin_amdgcn_exp2f((mx - nmx) * kLog2e) + o.y * __builtin_amdgcn_exp2f((o.x - nmx) * kLog2e);
+      if (better(o.z, oi, best.key, best.idx)) best = Cand{o.z, oi};
       a.part[static_cast<size_t>(m) * a.n_vt + vt] = make_float4(nmx, se, best.key, __int_as_float(best.idx));
     }
-  }
+  });
 }
 
 __global__ __launch_bounds__(kThreads) void lm_row_reduce(LmArgs a) {
@@ -229,9 +259,9 @@ __global__ __launch_bounds__(kThreads) void lm_row_reduce(LmArgs a) {
 
 hipError_t launch_lm_head(const LmArgs& a, hipStream_t s) {
   const int slots = (a.n_vt + 7) / 8 * a.n_mt;
-  hipLaunchKernelGGL(lm_gemm, dim3(slots * 8), dim3(kThreads), 0, s, a);
-  hipLaunchKernelGGL(lm_row_reduce, dim3(a.M), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  hipError_t e = launch_kernel(lm_gemm, dim3(slots * 8), dim3(kThreads), s, a);
+  if (e == hipSuccess) e = launch_kernel(lm_row_reduce, dim3(a.M), dim3(kThreads), s, a);
+  return e;
 }
 
 }  // namespace sd

@@ -163,12 +163,15 @@ sd_status sd_lm_head_probs(const void* hidden, const void* w_vocab, int32_t M, i
                            void* workspace, size_t workspace_bytes, void* stream) {
   if (!hidden || !w_vocab || !q_off || !req_id || !logits || !lse || !draft_tokens)
     return SD_ERR_NULL;
-  if (M < 1 || batch < 1 || V < 1 || H < sd::kLmBK || H > 65536 || H % sd::kLmBK != 0)
+  if (M < 1 || batch < 1 || V < 1 || H < sd::kLmHMultiple || H > 65536 ||
+      H % sd::kLmHMultiple != 0)
     return SD_ERR_SHAPE;
   if (!aligned16(hidden) || !aligned16(w_vocab) || !aligned16(logits)) return SD_ERR_SHAPE;
   const LmLayout L = lm_layout(M, V);
   if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return SD_ERR_WORKSPACE;
-  if (static_cast<int64_t>((L.n_vt + 7) / 8) * 8 * L.n_mt > (int64_t(1) << 31) - 1) return SD_ERR_SHAPE;
+  if (static_cast<int64_t>((L.n_vt + 7) / 8) * 8 * L.n_mt > (int64_t(1) << 31) - 1 ||
+      static_cast<int64_t>(M) * L.n_vt > (int64_t(1) << 31) - 1)
+    return SD_ERR_SHAPE;
   sd::LmArgs a;
   a.hidden = static_cast<const uint16_t*>(hidden);
   a.w = static_cast<const uint16_t*>(w_vocab);

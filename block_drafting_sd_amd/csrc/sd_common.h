@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace sd {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
@@ -158,5 +160,67 @@ __device__ Cand block_best(Cand c, float* shk, int* shi) {
     if (better(shk[i], shi[i], r.key, r.idx)) r = Cand{shk[i], shi[i]};
   return r;
 }
+
+
+// ------------------------------------------------- direct-to-LDS streaming
+// Kernels that stream operands from HBM into a ring of LDS stages use gfx950
+// direct-to-LDS loads: a load writes 16 bytes per lane straight into LDS, so
+// several stages can be in flight without holding them in registers.
+typedef __attribute__((address_space(3))) char lds_char;
+
+// One direct-to-LDS load: lane l's 16 bytes at `src` land at LDS byte
+// address lds + 16 l (lds wave-uniform, passed in m0).  The instruction's
+// immediate offset is left at 0: the hardware adds it to the LDS address as
+// well as to the global one.  Written as inline assembly so that the
+// compiler does not tie later LDS reads to it with a blanket wait for every
+// load in flight; the waits are explicit (wait_vmcnt) instead, so a kernel
+// using it issues no other vector-memory loads inside its streaming loop.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  lds = __builtin_amdgcn_readfirstlane(lds);   // an SGPR operand
+  // one wait state between the m0 write and the load that reads it
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      ::"v"(src), "s"(lds)
+      : "memory", "m0");
+}
+
+// LDS byte address of a pointer into a __shared__ array (wave-uniform).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_char*)(p))));
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait for the loads of the oldest stage when `ahead` newer stages (L loads
+// each) may stay in flight; ahead in [0, C].
+template <int L, int C>
+__device__ __forceinline__ void wait_stage(int ahead) {
+  if constexpr (C == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (ahead >= C) wait_vmcnt<C * L>();
+    else wait_stage<L, C - 1>(ahead);
+  }
+}
+
+// Workgroup barrier that the compiler may not move memory accesses across and
+// that, unlike __syncthreads(), does not first drain every load in flight.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 }  // namespace sd

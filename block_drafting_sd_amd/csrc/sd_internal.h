@@ -7,6 +7,15 @@
 
 namespace sd {
 
+// Launch `k(args)` and return that launch's own status.  (The thread's
+// last-error state is not consulted: it may hold a stale, unrelated status
+// such as hipErrorNotReady left by an event or stream query of the caller.)
+template <typename Arg>
+hipError_t launch_kernel(void (*k)(Arg), dim3 grid, dim3 block, hipStream_t s, Arg arg) {
+  void* argv[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, argv, 0, s);
+}
+
 // ----------------------------------------------------------- draft attention
 struct AttnArgs {
   const uint16_t* q;
@@ -53,8 +62,9 @@ struct LmArgs {
 };
 
 constexpr int kLmBV = 128;   // vocab rows per workgroup tile
-constexpr int kLmBM = 128;   // draft rows per workgroup tile
-constexpr int kLmBK = 64;    // hidden dims per pipeline stage
+constexpr int kLmBM = 256;   // draft rows per workgroup tile
+constexpr int kLmBK = 32;    // hidden dims per pipeline stage
+constexpr int kLmHMultiple = 64;   // H must be a multiple of this
 
 hipError_t launch_lm_head(const LmArgs& a, hipStream_t s);
 

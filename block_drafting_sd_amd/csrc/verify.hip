@@ -184,12 +184,12 @@ __global__ __launch_bounds__(kThreads) void verify_finalize(VerifyArgs a) {
 
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t s) {
   const int rows = a.R + (a.draft_lse ? 0 : a.total_q);
-  if (rows > 0)
-    hipLaunchKernelGGL(verify_rowstats, dim3(rows * a.n_chunks), dim3(kThreads), 0, s, a);
-  hipLaunchKernelGGL(verify_sample, dim3(a.batch * a.n_chunks), dim3(kThreads), 0, s, a);
-  hipLaunchKernelGGL(verify_finalize, dim3((a.batch + kThreads - 1) / kThreads), dim3(kThreads),
-                     0, s, a);
-  return hipGetLastError();
+  hipError_t e = hipSuccess;
+  if (rows > 0) e = launch_kernel(verify_rowstats, dim3(rows * a.n_chunks), dim3(kThreads), s, a);
+  if (e == hipSuccess) e = launch_kernel(verify_sample, dim3(a.batch * a.n_chunks), dim3(kThreads), s, a);
+  if (e == hipSuccess)
+    e = launch_kernel(verify_finalize, dim3((a.batch + kThreads - 1) / kThreads), dim3(kThreads), s, a);
+  return e;
 }
 
 }  // namespace sd

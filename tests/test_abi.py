@@ -50,7 +50,7 @@ def test_workspace_sizes(lib):
     n = lib.sd_draft_attn_workspace_size(16, 32, 8, 128, 16 * 131072, 0)
     assert n > 16 * 131072 // 8192 * 8 * 64 * 128 * 4
     assert lib.sd_draft_attn_workspace_size(0, 32, 8, 128, 1, 0) == 0
-    assert lib.sd_lm_head_workspace_size(256, 151936) >= 256 * (151936 // 128) * 16
+    assert lib.sd_lm_head_workspace_size(256, 151936) >= 256 * (-(-151936 // 128)) * 16
     assert lib.sd_lm_head_workspace_size(0, 10) == 0
     assert lib.sd_verify_workspace_size(16, 256, 272, 151936) > 0
     assert lib.sd_verify_workspace_size(16, 256, 0, 151936) == 0
