@@ -25,6 +25,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_sd_draft_attn_c2_n128k_b16.txt")
+ATTN_SOURCE = os.path.join(ROOT, "block_drafting_sd_amd", "csrc", "attn.hip")
 
 
 def log(msg):
@@ -69,6 +71,26 @@ def cpu_baseline(inp, n_req: int = 1):
                        f"attn {t1 - t0:.2f}s lm {t2 - t1:.2f}s verify {t3 - t2:.2f}s")}
 
 
+def measured_traffic():
+    """HBM bytes per sd_draft_attn call from the committed rocprofv3 PMC
+    summary (FETCH_SIZE + WRITE_SIZE of the call's kernels, scaled by the same
+    counters' reading for a device copy of known size), or None when the
+    attention source has changed since those counters were taken."""
+    import hashlib
+    try:
+        kv = {}
+        for line in open(TRAFFIC_SUMMARY):
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        src = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+        if kv.get("attn_source_sha256") != src:
+            return None
+        return int(float(kv["traffic_bytes_per_call"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def copy_calibration(gib: float):
     """A plain device copy of known size, for scaling PMC byte counters."""
     import torch
@@ -89,7 +111,8 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="workload index (default 2: 128K, batch 16)")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-requests", type=int, default=1)
+    ap.add_argument("--cpu-requests", type=int, default=16,
+                    help="requests of the workload the CPU oracle is timed on")
     ap.add_argument("--calibrate-copy", type=float, default=0.0,
                     help="GiB: also run a plain device copy of this size (PMC calibration)")
     args = ap.parse_args()
@@ -189,10 +212,10 @@ def main():
                    "num_heads_kv": c.num_heads_kv, "head_dim": c.head_dim,
                    "page_size": c.page_size, "hidden": c.hidden, "vocab": c.vocab,
                    "split_tokens": args.split_tokens or "auto"},
-        "roofline": {"kernel": "sd_draft_attn (attn_worklist + attn_splitk + attn_combine)",
+        "roofline": {"kernel": "sd_draft_attn call: attn_worklist + attn_splitk + attn_combine",
                      "bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "algorithmic_bytes": attn_bytes,
+                     "traffic": measured_traffic(), "algorithmic_bytes": attn_bytes,
                      "avg_ms": round(float(attn_ms.mean()), 4)},
         "breakdown_ms": {"attention": round(float(attn_ms.mean()), 4),
                          "lm_head": round(float(lm_ms.mean()), 4),
