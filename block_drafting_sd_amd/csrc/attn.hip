@@ -381,17 +381,37 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   const int first = a.item_off[b] + g * (r.ns + 1);
   const int n = min(r.ns + 1, a.max_items - first);
   if (n <= 0) return;
+  // Loads are issued eight partials at a time (indices clamped to the last
+  // partial, duplicates weighted zero) so their latencies overlap.
+  constexpr int U = 8;
+  const float* lse = a.part_lse + static_cast<size_t>(first) * kAttnRows + qi;
   float mx = -INFINITY;
-  for (int s = 0; s < n; ++s) mx = fmaxf(mx, a.part_lse[static_cast<size_t>(first + s) * kAttnRows + qi]);
+  for (int s0 = 0; s0 < n; s0 += U) {
+    float l[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) l[u] = lse[static_cast<size_t>(min(s0 + u, n - 1)) * kAttnRows];
+#pragma unroll
+    for (int u = 0; u < U; ++u) mx = fmaxf(mx, l[u]);
+  }
+  const float* po = a.part_o + ((static_cast<size_t>(first) * (D / 4) + d4) * kAttnRows + qi) * 4;
+  constexpr size_t kItemStride = static_cast<size_t>(D / 4) * kAttnRows * 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  for (int s = 0; s < n; ++s) {
-    const size_t it = static_cast<size_t>(first + s);
-    const float w = __builtin_amdgcn_exp2f(a.part_lse[it * kAttnRows + qi] - mx);
-    const f32x4 o = *reinterpret_cast<const f32x4*>(
-        a.part_o + ((it * (D / 4) + d4) * kAttnRows + qi) * 4);
-    acc += w * o;
-    wsum += w;
+  for (int s0 = 0; s0 < n; s0 += U) {
+    float l[U];
+    f32x4 o[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t it = static_cast<size_t>(min(s0 + u, n - 1));
+      l[u] = lse[it * kAttnRows];
+      o[u] = *reinterpret_cast<const f32x4*>(po + it * kItemStride);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = s0 + u < n ? __builtin_amdgcn_exp2f(l[u] - mx) : 0.f;
+      acc += w * o[u];
+      wsum += w;
+    }
   }
   acc *= 1.f / wsum;
   const int j = qi / a.group, hh = qi % a.group;

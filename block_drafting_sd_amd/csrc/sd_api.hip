@@ -58,16 +58,17 @@ LmLayout lm_layout(int32_t M, int32_t V) {
 
 // ---------------------------------------------------------------- verify
 struct VerifyLayout {
-  int32_t n_chunks;
+  int32_t n_chunks, n_schunks;
   size_t off_row, off_samp, total;
 };
 
 VerifyLayout verify_layout(int32_t batch, int32_t total_q, int32_t R, int32_t V) {
   VerifyLayout L;
   L.n_chunks = (V + sd::kVerifyChunk - 1) / sd::kVerifyChunk;
+  L.n_schunks = (V + sd::kSampleChunk - 1) / sd::kSampleChunk;
   L.off_row = 0;
   L.off_samp = align_up(static_cast<size_t>(R + total_q) * L.n_chunks * sizeof(float2));
-  L.total = L.off_samp + align_up(static_cast<size_t>(batch) * L.n_chunks * 2 * sizeof(float4));
+  L.total = L.off_samp + align_up(static_cast<size_t>(batch) * L.n_schunks * 2 * sizeof(float4));
   return L;
 }
 
@@ -209,7 +210,7 @@ sd_status sd_verify(const float* target_logits, const int32_t* t_off, const floa
   if (batch < 1 || total_q < 0 || total_target_rows < 1 || V < 1) return SD_ERR_SHAPE;
   const VerifyLayout L = verify_layout(batch, total_q, total_target_rows, V);
   if (static_cast<int64_t>(total_target_rows + total_q) * L.n_chunks > (int64_t(1) << 31) - 1 ||
-      static_cast<int64_t>(batch) * L.n_chunks > (int64_t(1) << 31) - 1)
+      static_cast<int64_t>(batch) * L.n_schunks > (int64_t(1) << 31) - 1)
     return SD_ERR_SHAPE;
   if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return SD_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
@@ -231,7 +232,7 @@ sd_status sd_verify(const float* target_logits, const int32_t* t_off, const floa
   a.R = total_target_rows;
   a.V = V;
   a.n_chunks = L.n_chunks;
-  a.chunk = sd::kVerifyChunk;
+  a.n_schunks = L.n_schunks;
   a.key0 = static_cast<uint32_t>(seed);
   a.key1 = static_cast<uint32_t>(seed >> 32);
   return from_hip(sd::launch_verify(a, static_cast<hipStream_t>(stream)));

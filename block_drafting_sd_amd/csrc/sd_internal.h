@@ -81,12 +81,13 @@ struct VerifyArgs {
   int32_t* next_token;      // [batch]
   float* accept_ratio;      // [total_q] or null
   float2* row_part;         // [(R + total_q) * n_chunks] (max, sumexp)
-  float4* samp_part;        // [batch * n_chunks * 2]
-  int32_t batch, total_q, R, V, n_chunks, chunk;
+  float4* samp_part;        // [batch * n_schunks * 2]
+  int32_t batch, total_q, R, V, n_chunks, n_schunks;
   uint32_t key0, key1;
 };
 
-constexpr int kVerifyChunk = 8192;   // vocab entries per workgroup
+constexpr int kVerifyChunk = 8192;   // vocab entries per row-statistics workgroup
+constexpr int kSampleChunk = 2048;   // vocab entries per sampling workgroup
 
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t s);
 

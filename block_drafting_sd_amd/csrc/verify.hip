@@ -3,15 +3,18 @@
 // budgets b_b <= K_b).
 //
 // Three launches, no host synchronisation:
-//   1. verify_rowstats  grid (rows x vocab chunks): per chunk (max, sum exp)
-//      of every target row (and of every draft row when no draft lse is
-//      given).  Streams the logits once: HBM-bound.
-//   2. verify_sample    grid (requests x vocab chunks): every workgroup of a
-//      request merges the row statistics it needs, evaluates all of the
+//   1. verify_rowstats  grid (rows x 8192-entry chunks): per chunk (max, sum
+//      exp) of every target row (and of every draft row when no draft lse is
+//      given).  Each thread issues its eight 16-byte loads at once, so the
+//      logits stream through in one pass: HBM-bound.
+//   2. verify_sample    grid (requests x 2048-entry chunks): every workgroup
+//      of a request merges the row statistics it needs, evaluates all of the
 //      request's ratio tests in parallel, takes the first rejection, and
 //      draws Gumbel-max candidates of its vocab chunk from the residual
-//      [p_j - q_j]_+ (and from p_j as the fallback), or from p_{b+1}.
-//   3. verify_finalize  one thread per request merges the chunk candidates.
+//      [p_j - q_j]_+ (and from p_j as the fallback), or from p_{b+1}.  Only
+//      one row per request is read, so the chunks are small to spread that
+//      row over many CUs.
+//   3. verify_finalize  one wavefront per request merges the chunk candidates.
 #include "sd_common.h"
 #include "sd_internal.h"
 
@@ -23,30 +26,62 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxVerify = 255;   // b_b handled per request
 
-// (max, sum exp(x - max)) of one vocab chunk of one row.
+// (max, sum exp(x - max)) of one vocab chunk of one row.  Thread t holds
+// entries 4 (t + 256 j) + e of the chunk.
 __global__ __launch_bounds__(kThreads) void verify_rowstats(VerifyArgs a) {
   __shared__ float sh[kThreads / 64];
+  constexpr int kGroups = kVerifyChunk / (4 * kThreads);
   const int row = blockIdx.x / a.n_chunks;
   const int c = blockIdx.x % a.n_chunks;
   const float* src = row < a.R ? a.target + static_cast<size_t>(row) * a.V
                                : a.draft + static_cast<size_t>(row - a.R) * a.V;
-  const int lo = c * a.chunk;
-  const int hi = min(a.V, lo + a.chunk);
+  const int lo = c * kVerifyChunk;
+  const bool vec_ok = (a.V & 3) == 0;
+  f32x4 x[kGroups];
+#pragma unroll
+  for (int j = 0; j < kGroups; ++j) {
+    const int v = lo + 4 * (threadIdx.x + kThreads * j);
+    if (vec_ok && v + 3 < a.V) {
+      x[j] = *reinterpret_cast<const f32x4*>(src + v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[j][e] = v + e < a.V ? src[v + e] : -INFINITY;
+    }
+  }
   float mx = -FLT_MAX;
-  for (int i = lo + threadIdx.x; i < hi; i += kThreads) mx = fmaxf(mx, src[i]);
+#pragma unroll
+  for (int j = 0; j < kGroups; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, x[j][e]);
   mx = block_reduce_max<kThreads>(mx, sh);
   float se = 0.f;
-  for (int i = lo + threadIdx.x; i < hi; i += kThreads)
-    se += __builtin_amdgcn_exp2f((src[i] - mx) * kLog2e);
+#pragma unroll
+  for (int j = 0; j < kGroups; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) se += __builtin_amdgcn_exp2f((x[j][e] - mx) * kLog2e);
   se = block_reduce_sum<kThreads>(se, sh);
   if (threadIdx.x == 0) a.row_part[blockIdx.x] = make_float2(mx, se);
 }
 
+// Log-normaliser of a row from its n chunk partials; the partials are read
+// eight at a time (clamped index, duplicates weighted zero) so the loads overlap.
 __device__ float merge_lse(const float2* part, int n) {
+  constexpr int U = 8;
   float mx = -FLT_MAX;
-  for (int i = 0; i < n; ++i) mx = fmaxf(mx, part[i].x);
   float s = 0.f;
-  for (int i = 0; i < n; ++i) s += part[i].y * __builtin_amdgcn_exp2f((part[i].x - mx) * kLog2e);
+  for (int i0 = 0; i0 < n; i0 += U) {
+    float2 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = part[min(i0 + u, n - 1)];
+    float m2 = mx;
+#pragma unroll
+    for (int u = 0; u < U; ++u) m2 = fmaxf(m2, v[u].x);
+    s *= __builtin_amdgcn_exp2f((mx - m2) * kLog2e);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      s += i0 + u < n ? v[u].y * __builtin_amdgcn_exp2f((v[u].x - m2) * kLog2e) : 0.f;
+    mx = m2;
+  }
   return mx + logf(s);
 }
 
@@ -58,8 +93,8 @@ __global__ __launch_bounds__(kThreads) void verify_sample(VerifyArgs a) {
   __shared__ float shk[kThreads / 64];
   __shared__ int shi[kThreads / 64];
 
-  const int b = blockIdx.x / a.n_chunks;
-  const int c = blockIdx.x % a.n_chunks;
+  const int b = blockIdx.x / a.n_schunks;
+  const int c = blockIdx.x % a.n_schunks;
   const int tid = threadIdx.x;
   const int t0 = clampi(a.t_off[b], 0, a.R);
   const int t1 = clampi(a.t_off[b + 1], t0, a.R);
@@ -122,25 +157,40 @@ __global__ __launch_bounds__(kThreads) void verify_sample(VerifyArgs a) {
   const float lse_p = s_lse_p[acc];
   const float lse_q = residual ? s_lse_q[acc] : 0.f;
 
-  // D: Gumbel-max candidates of this vocab chunk
+  // D: Gumbel-max candidates of this vocab chunk; thread t holds entries
+  // 4 (t + 256 j) + e of the chunk
   Cand best_r{-FLT_MAX, 0x7fffffff}, best_p{-FLT_MAX, 0x7fffffff};
   int any_pos = 0;
-  const int lo = c * a.chunk;
-  const int hi = min(a.V, lo + a.chunk);
-  for (int g = lo + 4 * tid; g < hi; g += 4 * kThreads) {
+  const int lo = c * kSampleChunk;
+  const bool vec_ok = (a.V & 3) == 0;
+#pragma unroll
+  for (int jj = 0; jj < kSampleChunk / (4 * kThreads); ++jj) {
+    const int g = lo + 4 * (tid + kThreads * jj);
+    if (g >= a.V) break;
+    f32x4 xv, zv;
+    if (vec_ok && g + 3 < a.V) {
+      xv = *reinterpret_cast<const f32x4*>(xrow + g);
+      if (residual) zv = *reinterpret_cast<const f32x4*>(zrow + g);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xv[e] = g + e < a.V ? xrow[g + e] : 0.f;
+        zv[e] = residual && g + e < a.V ? zrow[g + e] : 0.f;
+      }
+    }
     const u32x4 w = philox4x32_10(u32x4{static_cast<uint32_t>(g >> 2), static_cast<uint32_t>(j),
                                         rid, kStreamSample},
                                   a.key0, a.key1);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int v = g + e;
-      if (v < hi) {
+      if (v < a.V) {
         const float gn = gumbel_from_bits(w[e]);
-        const float x = xrow[v];
+        const float x = xv[e];
         const float kp = x + gn;
         if (better(kp, v, best_p.key, best_p.idx)) best_p = Cand{kp, v};
         if (residual) {
-          const float res = expf(x - lse_p) - expf(zrow[v] - lse_q);
+          const float res = expf(x - lse_p) - expf(zv[e] - lse_q);
           if (res > 0.f) {
             any_pos = 1;
             const float kr = logf(res) + gn;
@@ -160,24 +210,22 @@ __global__ __launch_bounds__(kThreads) void verify_sample(VerifyArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kThreads) void verify_finalize(VerifyArgs a) {
-  const int b = blockIdx.x * kThreads + threadIdx.x;
-  if (b >= a.batch) return;
-  const float4* p = a.samp_part + static_cast<size_t>(b) * a.n_chunks * 2;
-  bool any_pos = false;
-  for (int c = 0; c < a.n_chunks; ++c) any_pos |= p[2 * c].z != 0.f;
-  const int sel = any_pos ? 0 : 1;   // residual draw, else a draw from p
-  float bk = -FLT_MAX;
-  int bi = 0x7fffffff;
-  for (int c = 0; c < a.n_chunks; ++c) {
+// One wavefront per request: lanes read the chunk candidates in parallel.
+__global__ __launch_bounds__(64) void verify_finalize(VerifyArgs a) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  const float4* p = a.samp_part + static_cast<size_t>(b) * a.n_schunks * 2;
+  int any_pos = 0;
+  for (int c = lane; c < a.n_schunks; c += 64) any_pos |= p[2 * c].z != 0.f;
+  const int sel = __any(any_pos) ? 0 : 1;   // residual draw, else a draw from p
+  Cand best{-FLT_MAX, 0x7fffffff};
+  for (int c = lane; c < a.n_schunks; c += 64) {
     const float4 q = p[2 * c + sel];
     const int idx = __float_as_int(q.y);
-    if (idx >= 0 && better(q.x, idx, bk, bi)) {
-      bk = q.x;
-      bi = idx;
-    }
+    if (idx >= 0 && better(q.x, idx, best.key, best.idx)) best = Cand{q.x, idx};
   }
-  a.next_token[b] = bi == 0x7fffffff ? -1 : bi;
+  best = wave_best(best);
+  if (lane == 0) a.next_token[b] = best.idx == 0x7fffffff ? -1 : best.idx;
 }
 
 }  // namespace
@@ -186,9 +234,9 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t s) {
   const int rows = a.R + (a.draft_lse ? 0 : a.total_q);
   hipError_t e = hipSuccess;
   if (rows > 0) e = launch_kernel(verify_rowstats, dim3(rows * a.n_chunks), dim3(kThreads), s, a);
-  if (e == hipSuccess) e = launch_kernel(verify_sample, dim3(a.batch * a.n_chunks), dim3(kThreads), s, a);
+  if (e == hipSuccess) e = launch_kernel(verify_sample, dim3(a.batch * a.n_schunks), dim3(kThreads), s, a);
   if (e == hipSuccess)
-    e = launch_kernel(verify_finalize, dim3((a.batch + kThreads - 1) / kThreads), dim3(kThreads), s, a);
+    e = launch_kernel(verify_finalize, dim3(a.batch), dim3(64), s, a);
   return e;
 }
 
