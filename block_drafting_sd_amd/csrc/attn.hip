@@ -11,7 +11,12 @@
 //   query rows of (b, g) share one item, so every prefix KV byte is read from
 //   HBM exactly once.  Each item writes fp32 partial results (normalised
 //   output and log-sum-exp), which `attn_combine` merges with the log-sum-exp
-//   rule of "LongSpark", App. A.2, eq. (11).
+//   rule of "LongSpark", App. A.2, eq. (11).  The hkv items of one
+//   (request, split) are given neighbouring workgroup slots on one XCD
+//   (`locate_item`): they walk the same pages, whose per-head slices are
+//   adjacent in the cache, so each page is fetched as one contiguous block
+//   through one L2 and one set of address translations.  With a shuffled
+//   page table this is worth a few per cent of HBM bandwidth.
 //
 // Prefix items stream the cache through a ring of NS LDS stages of 32 keys
 // (two 16-token pages, 128*D bytes) filled by gfx950 direct-to-LDS loads
@@ -103,6 +108,45 @@ __global__ __launch_bounds__(1024) void attn_worklist(AttnArgs a) {
     __syncthreads();
   }
   if (threadIdx.x == 0) a.item_off[a.batch] = carry;
+}
+
+// Work item of a workgroup.  A unit is one (request, split); its hkv items
+// (one per kv head) read the same pages, whose per-head slices are adjacent
+// in the cache ([page][hkv][...]).  Workgroups are dealt to the 8 XCDs round
+// robin, so blockIdx x runs on XCD x % 8; the mapping below gives the hkv
+// items of a unit consecutive slots on one XCD: they run side by side, share
+// that XCD's L2 and address translations, and fetch each page as one
+// contiguous hkv-slice block.  Returns false past the last item.
+struct ItemLoc {
+  int b, g, sp, item;
+  ReqInfo r;
+};
+
+__device__ __forceinline__ bool locate_item(const AttnArgs& a, int block, ItemLoc& L) {
+  const int x = block & 7;
+  const int k = block >> 3;
+  const int u = (k / a.hkv) * 8 + x;       // unit
+  L.g = k % a.hkv;
+  const int total = min(a.item_off[a.batch], a.max_items);
+  if (u * a.hkv >= total) return false;
+  // request owning the unit: largest b with item_off[b] <= u * hkv
+  int lo = 0, hi = a.batch;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.item_off[mid] <= u * a.hkv) lo = mid;
+    else hi = mid;
+  }
+  L.b = lo;
+  L.r = request_info(a, lo);
+  L.sp = u - a.item_off[lo] / a.hkv;
+  L.item = a.item_off[lo] + L.g * (L.r.ns + 1) + L.sp;
+  return L.item < total;   // item_off beyond the buffers (lengths above max_total_ctx)
+}
+
+// Workgroups covering every item under locate_item's mapping.
+inline int attn_grid(const AttnArgs& a) {
+  const int units = a.max_items / a.hkv;
+  return (units + 7) / 8 * 8 * a.hkv;
 }
 
 // Operand registers of one 32-key tile.
@@ -260,6 +304,28 @@ __device__ __forceinline__ void read_stage(const uint16_t* stage, int lane, KvTi
       t.v[m][p] = load_bf16x8(stage + (D / 16 + p * (D / 32) + m) * 512 + lane * 8);
 }
 
+// Normalised partial output and log2-sum-exp2 of one 32-row half.
+template <int D>
+__device__ __forceinline__ void write_partial(const AttnArgs& a, const AttnState<D>& st, int item,
+                                              int half, int lane) {
+  const int h = lane >> 5;
+  float* po = a.part_o + static_cast<size_t>(item) * (D / 4) * kAttnRows * 4;
+  const float l = st.l + xor_shuffle(st.l, 32);
+  const float inv = 1.f / l;
+  const int qi = 32 * half + (lane & 31);
+  if (h == 0) a.part_lse[static_cast<size_t>(item) * kAttnRows + qi] = st.m + log2f(l);
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt) {
+#pragma unroll
+    for (int ar = 0; ar < 4; ++ar) {
+      const int d4 = 8 * mt + 2 * ar + h;
+      f32x4 v = {st.o[mt][4 * ar] * inv, st.o[mt][4 * ar + 1] * inv, st.o[mt][4 * ar + 2] * inv,
+                 st.o[mt][4 * ar + 3] * inv};
+      *reinterpret_cast<f32x4*>(po + (static_cast<size_t>(d4) * kAttnRows + qi) * 4) = v;
+    }
+  }
+}
+
 // One workgroup (two waves) per work item; wave w owns query rows
 // 32w .. 32w+31 of the item's (up to) 64 rows.
 template <int D, int NS>
@@ -268,23 +334,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(1024))) uint16_t s_kv[NS * stage_elems<D>()];
   __shared__ int s_pages[kAttnMaxSplitPages];
 
-  const int item = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int total = min(a.item_off[a.batch], a.max_items);
-  if (item >= total) return;
-  // request owning this item: largest b with item_off[b] <= item
-  int lo = 0, hi = a.batch;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.item_off[mid] <= item) lo = mid;
-    else hi = mid;
-  }
-  const int b = lo;
-  const ReqInfo r = request_info(a, b);
-  const int rel = item - a.item_off[b];
-  const int g = rel / (r.ns + 1);
-  const int sp = rel % (r.ns + 1);
+  ItemLoc L;
+  if (!locate_item(a, blockIdx.x, L)) return;
+  const int b = L.b, g = L.g, sp = L.sp, item = L.item;
+  const ReqInfo r = L.r;
   const int rows = a.group * r.kb;
   const bool active = 32 * wave < rows;   // this wave has query rows
   const float sl2 = a.scale_log2;
@@ -348,23 +403,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   if (!active) return;
 
-  // normalised partial output and log2-sum-exp2 of the scaled scores
-  const int h = lane >> 5;
-  float* po = a.part_o + static_cast<size_t>(item) * (D / 4) * kAttnRows * 4;
-  const float l = st.l + xor_shuffle(st.l, 32);
-  const float inv = 1.f / l;
-  const int qi = 32 * wave + (lane & 31);
-  if (h == 0) a.part_lse[static_cast<size_t>(item) * kAttnRows + qi] = st.m + log2f(l);
-#pragma unroll
-  for (int mt = 0; mt < D / 32; ++mt) {
-#pragma unroll
-    for (int ar = 0; ar < 4; ++ar) {
-      const int d4 = 8 * mt + 2 * ar + h;
-      f32x4 v = {st.o[mt][4 * ar] * inv, st.o[mt][4 * ar + 1] * inv, st.o[mt][4 * ar + 2] * inv,
-                 st.o[mt][4 * ar + 3] * inv};
-      *reinterpret_cast<f32x4*>(po + (static_cast<size_t>(d4) * kAttnRows + qi) * 4) = v;
-    }
-  }
+  write_partial<D>(a, st, item, wave, lane);
 }
 
 // Merge the partials of one (request, kv head) with the log-sum-exp rule and
@@ -425,7 +464,7 @@ template <int D>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
   hipError_t e = launch_kernel(attn_worklist, dim3(1), dim3(1024), s, a);
   if (e == hipSuccess && a.max_items > 0)
-    e = launch_kernel(attn_splitk<D, kAttnStages>, dim3(a.max_items), dim3(128), s, a);
+    e = launch_kernel(attn_splitk<D, kAttnStages>, dim3(attn_grid(a)), dim3(128), s, a);
   if (e == hipSuccess) e = launch_kernel(attn_combine<D>, dim3(a.batch * a.hkv, D / 16), dim3(256), s, a);
   return e;
 }
