@@ -41,7 +41,11 @@ def lm_head_tensors(inp: StepInputs, device) -> Dict[str, torch.Tensor]:
                 req_id=i32(inp.req_id.view(np.int32), device))
 
 
-def verify_tensors(inp: StepInputs, device) -> Dict[str, torch.Tensor]:
+def verify_tensors(inp: StepInputs, device, target: np.ndarray = None) -> Dict[str, torch.Tensor]:
+    """Verification inputs; ``target`` overrides the workload's own target
+    logits (needed for the drafter-plus-noise workload, whose target is built
+    from drafter logits by ``StepInputs.target_from_drafter``)."""
     b = inp.budgets
-    return dict(target_logits=f32(inp.target_logits, device), t_off=i32(b.t_off, device),
+    tgt = inp.target_logits if target is None else target
+    return dict(target_logits=f32(tgt, device), t_off=i32(b.t_off, device),
                 q_off=i32(b.q_off, device), req_id=i32(inp.req_id.view(np.int32), device))
