@@ -1,6 +1,6 @@
 """Block-parallel speculative draft-and-verify step for AMD MI355X (gfx950).
 
-Thin Python binding over the C ABI declared in ``include/sd.h``; the three
+Thin Python binding over the C ABI declared in ``include/sd.h``; the
 functions keep the C names.  PyTorch supplies device memory and the stream;
 arguments are checked for dtype / contiguity / device and passed as raw
 pointers.  All computation happens in ``libsd_amd.so``.
@@ -14,7 +14,10 @@ import torch
 
 from ._lib import LIB_PATH, SdError, check, load  # noqa: F401
 
-__all__ = ["sd_draft_attn", "sd_lm_head_probs", "sd_verify", "sd_version",
+SD_MASK_NONE, SD_MASK_CAUSAL = 0, 1
+
+__all__ = ["sd_draft_attn", "sd_summary_update", "sd_lm_head_probs", "sd_verify", "sd_version",
+           "SD_MASK_NONE", "SD_MASK_CAUSAL",
            "draft_attn_workspace_size", "lm_head_workspace_size",
            "verify_workspace_size", "SdError", "load"]
 
@@ -74,7 +77,9 @@ def _workspace(ws, nbytes, device):
 
 def sd_draft_attn(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_len, q_off, *,
                   max_draft_k: int, max_total_ctx: int, softmax_scale: Optional[float] = None,
-                  split_tokens: int = 0, out=None, workspace=None, stream=None):
+                  split_tokens: int = 0, block_mask: int = SD_MASK_NONE, window: int = 0,
+                  summary_keys=None, summary_values=None, out=None, workspace=None,
+                  stream=None):
     """Draft-block attention; see ``sd_draft_attn`` in include/sd.h."""
     lib = load()
     dev = q.device
@@ -96,13 +101,57 @@ def sd_draft_attn(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_len, q_off,
     workspace = _workspace(workspace, nbytes, dev)
     if out is None:
         out = torch.empty_like(q)
+    n_summary = 0
+    if summary_keys is not None or summary_values is not None:
+        _req(summary_keys, "summary_keys", _BF16, dev)
+        _req(summary_values, "summary_values", _F32, dev)
+        n_summary = summary_keys.shape[1]
+        if tuple(summary_keys.shape) != (hkv, n_summary, D) or \
+                tuple(summary_values.shape) != (batch, hkv, n_summary, D):
+            raise ValueError("summary_keys must be [Hkv, S, D] and summary_values [batch, Hkv, S, D]")
     st = lib.sd_draft_attn(_ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(k_cache), _ptr(v_cache),
                            _ptr(page_table), _ptr(ctx_len), _ptr(q_off), batch, total_q,
                            max_draft_k, num_pages, max_pages, page_size, hq, hkv, D,
                            int(max_total_ctx), int(split_tokens), float(softmax_scale),
+                           int(block_mask), int(window), _ptr(summary_keys),
+                           _ptr(summary_values), n_summary,
                            _ptr(out), _ptr(workspace), workspace.numel(), _stream_handle(stream))
     check("sd_draft_attn", st)
     return out
+
+
+def sd_summary_update(summary_queries, k_cache, v_cache, page_table, ctx_len, accepted_len,
+                      summary_values, summary_lse, *, softmax_scale: Optional[float] = None,
+                      stream=None):
+    """Fold retained target KV rows into the context summary (in place); see
+    ``sd_summary_update`` in include/sd.h.  ``accepted_len=None`` initialises
+    the summary from each request's whole prefix."""
+    lib = load()
+    dev = summary_queries.device
+    _req(summary_queries, "summary_queries", _BF16, dev)
+    _req(k_cache, "k_cache", _BF16, dev)
+    _req(v_cache, "v_cache", _BF16, dev)
+    _req(page_table, "page_table", _I32, dev)
+    _req(ctx_len, "ctx_len", _I32, dev)
+    if accepted_len is not None:
+        _req(accepted_len, "accepted_len", _I32, dev)
+    _req(summary_values, "summary_values", _F32, dev)
+    _req(summary_lse, "summary_lse", _F32, dev)
+    hkv, n_summary, D = summary_queries.shape
+    num_pages, _, _, page_size, _ = k_cache.shape
+    batch, max_pages = page_table.shape
+    if tuple(summary_values.shape) != (batch, hkv, n_summary, D) or \
+            tuple(summary_lse.shape) != (batch, hkv, n_summary):
+        raise ValueError("summary_values must be [batch, Hkv, S, D] and summary_lse [batch, Hkv, S]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    st = lib.sd_summary_update(_ptr(summary_queries), _ptr(k_cache), _ptr(v_cache),
+                               _ptr(page_table), _ptr(ctx_len), _ptr(accepted_len), batch,
+                               num_pages, max_pages, page_size, hkv, D, n_summary,
+                               float(softmax_scale), _ptr(summary_values), _ptr(summary_lse),
+                               _stream_handle(stream))
+    check("sd_summary_update", st)
+    return summary_values, summary_lse
 
 
 def sd_lm_head_probs(hidden, w_vocab, q_off, req_id, seed: int, *, logits=None, lse=None,

@@ -59,25 +59,32 @@ int32_t attn_split_tokens(int32_t hkv, int64_t max_total_ctx, int32_t requested)
 
 int64_t attn_max_items(int32_t batch, int32_t hkv, int64_t max_total_ctx,
                        int32_t split_tokens) {
-  // sum_b (ceil(N_b / S) + 1) <= sum_b N_b / S + 2 * batch
-  return static_cast<int64_t>(hkv) * (max_total_ctx / split_tokens + 2 * static_cast<int64_t>(batch));
+  // sum_b (ceil(N_b / S) + 2) <= sum_b N_b / S + 3 * batch (a window only
+  // shortens the streamed range)
+  return static_cast<int64_t>(hkv) * (max_total_ctx / split_tokens + 3 * static_cast<int64_t>(batch));
 }
 
 namespace {
 
 struct ReqInfo {
   int n;        // prefix length N_b (clamped)
+  int n0;       // first prefix token attended (N_b - W with a window, else 0)
+  int a0;       // n0 rounded down to a page: the streamed range is [a0, n)
   int q0;       // first query row
   int kb;       // draft rows K_b (clamped)
   int ns;       // prefix splits
+  int per;      // items per KV head: ns prefix splits, the block, the summary
 };
 
 __device__ __forceinline__ ReqInfo request_info(const AttnArgs& a, int b) {
   ReqInfo r;
   r.n = clampi(a.ctx_len[b], 0, a.max_pages * 16);
+  r.n0 = a.window > 0 ? max(0, r.n - a.window) : 0;
+  r.a0 = r.n0 & ~15;
   r.q0 = clampi(a.q_off[b], 0, a.total_q);
   r.kb = min(clampi(a.q_off[b + 1], r.q0, a.total_q) - r.q0, a.max_draft_k);
-  r.ns = (r.n + a.split_tokens - 1) / a.split_tokens;
+  r.ns = (r.n - r.a0 + a.split_tokens - 1) / a.split_tokens;
+  r.per = r.ns + 1 + (a.n_summary > 0 ? 1 : 0);
   return r;
 }
 
@@ -92,7 +99,7 @@ __global__ __launch_bounds__(1024) void attn_worklist(AttnArgs a) {
     int v = 0;
     if (b < a.batch) {
       const ReqInfo r = request_info(a, b);
-      v = r.kb > 0 ? a.hkv * (r.ns + 1) : 0;
+      v = r.kb > 0 ? a.hkv * r.per : 0;
     }
     sh[threadIdx.x] = v;
     __syncthreads();
@@ -110,7 +117,8 @@ __global__ __launch_bounds__(1024) void attn_worklist(AttnArgs a) {
   if (threadIdx.x == 0) a.item_off[a.batch] = carry;
 }
 
-// Work item of a workgroup.  A unit is one (request, split); its hkv items
+// Work item of a workgroup.  A unit is one (request, split) -- a prefix split,
+// the draft block or the summary; its hkv items
 // (one per kv head) read the same pages, whose per-head slices are adjacent
 // in the cache ([page][hkv][...]).  Workgroups are dealt to the 8 XCDs round
 // robin, so blockIdx x runs on XCD x % 8; the mapping below gives the hkv
@@ -139,7 +147,7 @@ __device__ __forceinline__ bool locate_item(const AttnArgs& a, int block, ItemLo
   L.b = lo;
   L.r = request_info(a, lo);
   L.sp = u - a.item_off[lo] / a.hkv;
-  L.item = a.item_off[lo] + L.g * (L.r.ns + 1) + L.sp;
+  L.item = a.item_off[lo] + L.g * L.r.per + L.sp;
   return L.item < total;   // item_off beyond the buffers (lengths above max_total_ctx)
 }
 
@@ -194,6 +202,40 @@ __device__ __forceinline__ void load_block_tile(const AttnArgs& a, int g, int q0
   }
 }
 
+// Summary entries as keys and values ("LongSpark", sec. 2.2, eq. (6)): keys
+// are the summary queries U [hkv][S][D] (bf16), values the request's summary
+// values Z [batch][hkv][S][D] (fp32, rounded to bf16 like every other value
+// row); tile keys kappa = base .. base+31.
+template <int D>
+__device__ __forceinline__ void load_summary_tile(const AttnArgs& a, int b, int g, int base,
+                                                  int lane, KvTile<D>& t) {
+  const int h = lane >> 5;
+  int sel, slot;
+  tile_row_key(lane & 31, sel, slot);
+  const int kap = base + 16 * sel + slot;
+  const bool ok = kap < a.n_summary;
+  const uint16_t* kr = a.sum_k + (static_cast<size_t>(g) * a.n_summary + (ok ? kap : 0)) * D;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) t.k[s] = ok ? load_bf16x8(kr + 8 * (2 * s + h)) : zero_bf16x8();
+  const float* vr = a.sum_v + (static_cast<size_t>(b) * a.hkv + g) * a.n_summary * D;
+#pragma unroll
+  for (int m = 0; m < D / 32; ++m) {
+    const int d = 32 * m + (lane & 31);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k2 = base + 16 * p + 8 * h + e;
+        const uint16_t bits = k2 < a.n_summary ? f32_to_bf16_bits(vr[static_cast<size_t>(k2) * D + d])
+                                               : uint16_t(0);
+        v[e] = __builtin_bit_cast(__bf16, bits);
+      }
+      t.v[m][p] = v;
+    }
+  }
+}
+
 template <int D>
 struct AttnState {
   bf16x8 q[D / 16];          // B operands Q^T of this wave's 32 query rows
@@ -207,23 +249,24 @@ struct AttnState {
 // runs only a handful of times per work item.
 constexpr float kRescaleLog2 = 8.f;
 
-// One 32-key tile: scores, online softmax, P V.  `valid` = number of keys of
-// the tile that exist (keys past it are masked).  st.m is a running upper
+// One 32-key tile: scores, online softmax, P V.  Keys lo .. hi-1 of the tile
+// take part (per lane: a causal block mask gives every query its own hi);
+// the rest are masked.  st.m is a running upper
 // bound on nothing: it is the reference point of the exponentials, raised to
 // the tile maximum only when that exceeds it by more than kRescaleLog2 (the
 // softmax is invariant to the choice; "LongSpark", App. A.2, eq. (11)).
 template <int D>
-__device__ __forceinline__ void attend_tile(AttnState<D>& st, const KvTile<D>& t, int valid,
+__device__ __forceinline__ void attend_tile(AttnState<D>& st, const KvTile<D>& t, int lo, int hi,
                                             float sl2, int lane) {
   const int h = lane >> 5;
   f32x16 s = {};
 #pragma unroll
   for (int k = 0; k < D / 16; ++k) s = mfma_32x32x16(t.k[k], st.q[k], s);
-  if (valid < kAttnTile) {
+  if (lo > 0 || hi < kAttnTile) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = 16 * (i >> 3) + 8 * h + (i & 7);
-      if (key >= valid) s[i] = -INFINITY;
+      if (key < lo || key >= hi) s[i] = -INFINITY;
     }
   }
   float mx = s[0];
@@ -361,8 +404,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   if (sp < r.ns) {
-    // prefix split: tokens [t_begin, t_end), 32 per stage
-    const int t_begin = sp * a.split_tokens;
+    // prefix split: tokens [t_begin, t_end), 32 per stage; tokens before n0
+    // (outside the window) are masked
+    const int t_begin = r.a0 + sp * a.split_tokens;
     const int t_end = min(r.n, t_begin + a.split_tokens);
     const int n_pages = (t_end - t_begin + 15) >> 4;
     const int* pt = a.page_table + static_cast<size_t>(b) * a.max_pages + (t_begin >> 4);
@@ -390,15 +434,28 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (active) {
         KvTile<D> kv;
         read_stage<D>(s_kv + (t % NS) * stage_elems<D>(), lane, kv);
-        attend_tile<D>(st, kv, min(kAttnTile, t_end - t_begin - t * kAttnTile), sl2, lane);
+        const int first = t_begin + t * kAttnTile;
+        attend_tile<D>(st, kv, max(0, r.n0 - first), min(kAttnTile, t_end - first), sl2, lane);
       }
     }
-  } else {
+  } else if (sp == r.ns) {
+    // the draft block; with the causal mask, block row j sees block keys 0..j
     if (!active) return;
+    const int qi = 32 * wave + (lane & 31);
+    const int j = qi / a.group;
     for (int base = 0; base < r.kb; base += kAttnTile) {
       KvTile<D> t;
       load_block_tile<D>(a, g, r.q0, r.kb, base, lane, t);
-      attend_tile<D>(st, t, min(kAttnTile, r.kb - base), sl2, lane);
+      const int hi = min(kAttnTile, r.kb - base);
+      attend_tile<D>(st, t, 0, a.block_mask ? min(hi, j - base + 1) : hi, sl2, lane);
+    }
+  } else {
+    // the summary entries
+    if (!active) return;
+    for (int base = 0; base < a.n_summary; base += kAttnTile) {
+      KvTile<D> t;
+      load_summary_tile<D>(a, b, g, base, lane, t);
+      attend_tile<D>(st, t, 0, min(kAttnTile, a.n_summary - base), sl2, lane);
     }
   }
   if (!active) return;
@@ -417,8 +474,8 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   const int d4 = blockIdx.y * 4 + (threadIdx.x >> 6);
   const ReqInfo r = request_info(a, b);
   if (r.kb <= 0 || qi >= a.group * r.kb) return;
-  const int first = a.item_off[b] + g * (r.ns + 1);
-  const int n = min(r.ns + 1, a.max_items - first);
+  const int first = a.item_off[b] + g * r.per;
+  const int n = min(r.per, a.max_items - first);
   if (n <= 0) return;
   // Loads are issued eight partials at a time (indices clamped to the last
   // partial, duplicates weighted zero) so their latencies overlap.

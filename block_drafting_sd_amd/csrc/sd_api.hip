@@ -104,9 +104,16 @@ sd_status sd_draft_attn(const void* q, const void* k_blk, const void* v_blk, con
                         int32_t num_pages, int32_t max_pages, int32_t page_size,
                         int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
                         int64_t max_total_ctx, int32_t split_tokens, float softmax_scale,
+                        int32_t block_mask, int32_t window, const void* summary_keys,
+                        const float* summary_values, int32_t n_summary,
                         void* out, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k_blk || !v_blk || !k_cache || !v_cache || !page_table || !ctx_len || !q_off || !out)
     return SD_ERR_NULL;
+  if (n_summary > 0 && (!summary_keys || !summary_values)) return SD_ERR_NULL;
+  if ((block_mask != SD_MASK_NONE && block_mask != SD_MASK_CAUSAL) || window < 0 || n_summary < 0 ||
+      n_summary > sd::kAttnMaxSummary || !(softmax_scale > 0.f))
+    return SD_ERR_SHAPE;
+  if (n_summary > 0 && !aligned16(summary_keys)) return SD_ERR_SHAPE;
   if (batch < 1 || total_q < 0 || max_draft_k < 1 || num_pages < 1 || max_pages < 1 ||
       page_size != 16 || num_heads_kv < 1 || num_heads_q < num_heads_kv ||
       num_heads_q % num_heads_kv != 0 || (head_dim != 64 && head_dim != 128) ||
@@ -144,6 +151,11 @@ sd_status sd_draft_attn(const void* q, const void* k_blk, const void* v_blk, con
   a.hq = num_heads_q;
   a.hkv = num_heads_kv;
   a.group = group;
+  a.block_mask = block_mask;
+  a.window = window;
+  a.sum_k = n_summary > 0 ? static_cast<const uint16_t*>(summary_keys) : nullptr;
+  a.sum_v = n_summary > 0 ? summary_values : nullptr;
+  a.n_summary = n_summary;
   a.split_tokens = L.split;
   a.max_items = static_cast<int32_t>(L.max_items);
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
@@ -151,6 +163,42 @@ sd_status sd_draft_attn(const void* q, const void* k_blk, const void* v_blk, con
   a.part_lse = reinterpret_cast<float*>(ws + L.off_lse);
   a.part_o = reinterpret_cast<float*>(ws + L.off_o);
   return from_hip(sd::launch_draft_attn(a, head_dim, static_cast<hipStream_t>(stream)));
+}
+
+sd_status sd_summary_update(const void* summary_queries, const void* k_cache, const void* v_cache,
+                            const int32_t* page_table, const int32_t* ctx_len,
+                            const int32_t* accepted_len, int32_t batch, int32_t num_pages,
+                            int32_t max_pages, int32_t page_size, int32_t num_heads_kv,
+                            int32_t head_dim, int32_t n_summary, float softmax_scale,
+                            float* summary_values, float* summary_lse, void* stream) {
+  if (!summary_queries || !k_cache || !v_cache || !page_table || !ctx_len || !summary_values ||
+      !summary_lse)
+    return SD_ERR_NULL;
+  if (batch < 1 || num_pages < 1 || max_pages < 1 || page_size != 16 || num_heads_kv < 1 ||
+      (head_dim != 64 && head_dim != 128) || n_summary < 1 || n_summary > sd::kSummaryMax ||
+      !(softmax_scale > 0.f) || !isfinite(softmax_scale))
+    return SD_ERR_SHAPE;
+  if (static_cast<int64_t>(max_pages) * page_size > (int64_t(1) << 30)) return SD_ERR_SHAPE;
+  if (static_cast<int64_t>(batch) * max_pages > (int64_t(1) << 31) - 1 ||
+      static_cast<int64_t>(batch) * num_heads_kv > (int64_t(1) << 31) - 1)
+    return SD_ERR_SHAPE;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return SD_ERR_SHAPE;
+  sd::SummaryArgs a;
+  a.u = static_cast<const uint16_t*>(summary_queries);
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.page_table = page_table;
+  a.ctx_len = ctx_len;
+  a.accepted = accepted_len;
+  a.z = summary_values;
+  a.c = summary_lse;
+  a.batch = batch;
+  a.hkv = num_heads_kv;
+  a.n_summary = n_summary;
+  a.num_pages = num_pages;
+  a.max_pages = max_pages;
+  a.scale = softmax_scale;
+  return from_hip(sd::launch_summary(a, head_dim, static_cast<hipStream_t>(stream)));
 }
 
 size_t sd_lm_head_workspace_size(int32_t M, int32_t V) {

@@ -29,6 +29,11 @@ struct AttnArgs {
   uint16_t* out;
   int32_t batch, total_q, max_draft_k, num_pages, max_pages;
   int32_t hq, hkv, group;
+  int32_t block_mask;     // 0: bidirectional inside the block; 1: causal inside the block
+  int32_t window;         // 0: the whole prefix; W > 0: only its last W tokens
+  const uint16_t* sum_k;  // [hkv][n_summary][D] summary keys, or null
+  const float* sum_v;     // [batch][hkv][n_summary][D] summary values
+  int32_t n_summary;      // 0 when there is no summary
   int32_t split_tokens;   // prefix tokens per work item (multiple of 64, <= 8192)
   int32_t max_items;      // work items the partial buffers hold
   float scale_log2;       // softmax_scale * log2(e)
@@ -41,11 +46,30 @@ constexpr int kAttnRows = 64;        // query rows per (request, kv head) item
 constexpr int kAttnTile = 32;        // keys per inner tile (two 16-token pages)
 constexpr int kAttnStages = 4;       // LDS ring stages of the prefix stream
 constexpr int kAttnMaxSplitPages = 512;   // split_tokens <= 512 * 16
+constexpr int kAttnMaxSummary = 64;  // summary entries per KV head
 
 int64_t attn_max_items(int32_t batch, int32_t hkv, int64_t max_total_ctx,
                        int32_t split_tokens);
 int32_t attn_split_tokens(int32_t hkv, int64_t max_total_ctx, int32_t requested);
 hipError_t launch_draft_attn(const AttnArgs& a, int head_dim, hipStream_t s);
+
+// ------------------------------------------------------------ context summary
+struct SummaryArgs {
+  const uint16_t* u;          // [hkv][n_summary][D] summary queries
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* page_table;  // [batch][max_pages]
+  const int32_t* ctx_len;     // [batch]
+  const int32_t* accepted;    // [batch], or null to initialise from the prefix
+  float* z;                   // [batch][hkv][n_summary][D]
+  float* c;                   // [batch][hkv][n_summary]
+  int32_t batch, hkv, n_summary, num_pages, max_pages;
+  float scale;
+};
+
+constexpr int kSummaryMax = 64;   // summary entries per KV head
+
+hipError_t launch_summary(const SummaryArgs& a, int head_dim, hipStream_t s);
 
 // ------------------------------------------------------------------ LM head
 struct LmArgs {

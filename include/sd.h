@@ -4,6 +4,8 @@
  *
  * The step has three parts, one entry point each:
  *   sd_draft_attn     draft-block attention over the target's paged KV cache
+ *                     (whole prefix, or recent window + context summary)
+ *   sd_summary_update fold newly retained target KV rows into the summary
  *   sd_lm_head_probs  drafter LM head, softmax statistics, draft sampling
  *   sd_verify         lossless speculative-sampling verification
  *
@@ -55,6 +57,12 @@ enum {
   SD_ERR_DEVICE = 5     /* no gfx950 device is current                       */
 };
 
+/* Attention among the draft block's own rows (sd_draft_attn block_mask). */
+enum {
+  SD_MASK_NONE = 0,     /* bidirectional: every block row sees every block row */
+  SD_MASK_CAUSAL = 1    /* block row j sees block rows 0..j                    */
+};
+
 /* Static description of a status code (never NULL). */
 const char* sd_status_str(sd_status s);
 
@@ -77,12 +85,25 @@ const char* sd_version(void);
  *
  * For request b with prefix length N_b = ctx_len[b] and K_b = q_off[b+1] -
  * q_off[b] draft rows, every query head h (KV head g = h / (Hq / Hkv)) of
- * every draft row r computes, with one softmax and NO mask,
- *     out[r, h] = softmax(s) . [V_prefix(g); v_blk[q_off[b]..q_off[b+1]-1, g]]
- *     s = softmax_scale * q[r, h] . [K_prefix(g); k_blk[rows of b, g]]
- * where K_prefix / V_prefix are the N_b cached rows of head g in logical
- * token order.  Scores, softmax and accumulation are fp32; out is rounded to
- * bf16 (nearest even).
+ * every draft row r computes, with one softmax,
+ *     out[r, h] = softmax(s) . [V_prefix(g); v_blk[rows of b, g]; Z_b(g)]
+ *     s = softmax_scale * q[r, h] . [K_prefix(g); k_blk[rows of b, g]; U(g)]
+ * where K_prefix / V_prefix are the cached rows of head g in logical token
+ * order: all N_b of them (window = 0), or only the last min(W, N_b)
+ * (window = W > 0).  U(g) / Z_b(g) are the n_summary context-summary keys and
+ * values (absent when n_summary = 0).  With block_mask = SD_MASK_NONE there
+ * is no mask; with SD_MASK_CAUSAL block row j (j = r - q_off[b]) sees block
+ * keys 0..j only (prefix and summary keys stay visible).  Scores, softmax
+ * and accumulation are fp32; summary values enter rounded to bf16 (nearest
+ * even) like every other value row; out is rounded to bf16 (nearest even).
+ *
+ * Variants: the recent window plus summary is the fixed-size context of
+ * "LongSpark", sec. 2.2, eq. (6) (block; recent window of W target KV rows;
+ * summary queries as keys and summary values as values, under one
+ * normalisation); the causal block mask and a window are the attention of
+ * "H-Spec", sec. 3.3.2 (causal over the block, target KV as prefix context,
+ * a sliding window over the prefix; here one window shared by the block's
+ * rows).
  *
  * Arguments
  *   q        bf16 [total_q, Hq, D]   draft queries, request b owns rows
@@ -107,7 +128,13 @@ const char* sd_version(void);
  *   max_total_ctx  host upper bound on sum_b N_b (sizes the launch)
  *   split_tokens   prefix tokens per split-K work item; 0 lets the library
  *                  choose; otherwise a multiple of 64, at most 8192
- *   softmax_scale  usually 1/sqrt(head_dim)
+ *   softmax_scale  > 0, usually 1/sqrt(head_dim)
+ *   block_mask     SD_MASK_NONE or SD_MASK_CAUSAL
+ *   window         0 (whole prefix) or W > 0 (the last W prefix tokens)
+ *   summary_keys   bf16 [Hkv, n_summary, D] (U), or NULL when n_summary = 0
+ *   summary_values fp32 [batch, Hkv, n_summary, D] (Z_b, as kept by
+ *                  sd_summary_update), or NULL when n_summary = 0
+ *   n_summary      0 .. 64
  *   out      bf16 [total_q, Hq, D]
  * ------------------------------------------------------------------------ */
 size_t sd_draft_attn_workspace_size(int32_t batch, int32_t num_heads_q,
@@ -122,8 +149,53 @@ sd_status sd_draft_attn(const void* q, const void* k_blk, const void* v_blk,
                         int32_t max_pages, int32_t page_size,
                         int32_t num_heads_q, int32_t num_heads_kv,
                         int32_t head_dim, int64_t max_total_ctx,
-                        int32_t split_tokens, float softmax_scale, void* out,
+                        int32_t split_tokens, float softmax_scale,
+                        int32_t block_mask, int32_t window,
+                        const void* summary_keys, const float* summary_values,
+                        int32_t n_summary, void* out,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * sd_summary_update -- maintain the global context summary.
+ *
+ * Defined by: "LongSpark", sec. 2.2, eq. (5) (for fixed summary queries U,
+ * the summary values are the attention of U over all retained target KV
+ * rows) and App. A.2, eqs. (10)-(11) (per query, the summary value Z and
+ * log-normaliser c of a set of rows; two disjoint sets merge as
+ * c = log(e^c_a + e^c_b), Z = e^(c_a - c) Z_a + e^(c_b - c) Z_b; after
+ * verification at most K + 1 new rows are folded in; an empty set leaves the
+ * state unchanged).
+ *
+ * For every request b and KV head g, with s_it = softmax_scale * U[g, i] . k_t
+ * over cache rows t of head g:
+ *   accepted_len == NULL: initialise from the whole prefix, rows 0..N_b-1
+ *     (N_b = ctx_len[b]); N_b = 0 gives the empty state (c = -inf, Z = 0).
+ *   accepted_len != NULL: fold rows N_b .. N_b + accepted_len[b] (the
+ *     committed token and the a_b accepted drafts, which the target's
+ *     verification pass has already written to the cache) into the stored
+ *     state; a stored c = -inf is the empty state.
+ * Arithmetic is fp32 (online softmax over the new rows, then the merge).
+ *
+ * Arguments
+ *   summary_queries bf16 [Hkv, n_summary, D]  U (fixed, shared by requests)
+ *   k_cache, v_cache, page_table, num_pages, max_pages, page_size
+ *                   as for sd_draft_attn (rows are read in place)
+ *   ctx_len         int32 [batch]  N_b before the new rows
+ *   accepted_len    int32 [batch]  a_b (e.g. from sd_verify), or NULL
+ *   n_summary       1 .. 64
+ *   softmax_scale   > 0, usually 1/sqrt(head_dim)
+ *   summary_values  fp32 [batch, Hkv, n_summary, D]  Z, updated in place
+ *   summary_lse     fp32 [batch, Hkv, n_summary]     c, updated in place
+ * No workspace.  One workgroup per (request, KV head).
+ * ------------------------------------------------------------------------ */
+sd_status sd_summary_update(const void* summary_queries, const void* k_cache,
+                            const void* v_cache, const int32_t* page_table,
+                            const int32_t* ctx_len, const int32_t* accepted_len,
+                            int32_t batch, int32_t num_pages, int32_t max_pages,
+                            int32_t page_size, int32_t num_heads_kv,
+                            int32_t head_dim, int32_t n_summary,
+                            float softmax_scale, float* summary_values,
+                            float* summary_lse, void* stream);
 
 /* ------------------------------------------------------------------------
  * sd_lm_head_probs -- drafter LM head, softmax statistics, draft sampling.

@@ -18,6 +18,21 @@ its own row included.
   prefix, so the cache and the block arrive post-RoPE: "H-Spec", sec. 3.3.2.
 * Full prefix (no window): the prefix-reading drafters the pages compare
   against read the whole prefix ("LongSpark", sec. 1 and Fig. 1).
+
+Variants (keyword arguments of ``draft_attn``):
+
+* ``window=W``: only the last W prefix rows are keys and values -- the
+  recent window of the fixed-cost drafter ("LongSpark", sec. 2.2, eq. (6)),
+  and the sliding window of "H-Spec", sec. 3.3.2, read here as one window
+  shared by all rows of the block.
+* ``summary_keys`` / ``summary_values``: the context summary enters as extra
+  rows, summary queries as keys and summary values as values, under the
+  same normalisation ("LongSpark", sec. 2.2, eq. (6)).  The values enter
+  rounded to bf16 like every other value row (a reading: the pages do not fix
+  the precision the attention consumes them in).
+* ``block_mask="causal"``: block row j sees block rows 0..j only; prefix and
+  summary rows stay visible ("H-Spec", sec. 3.3.2, causal attention over the
+  masked block with the target KV as prefix context).
 * Scores are q.k / sqrt(d): "LongSpark", App. A.2, eq. (10).
 * Query head h reads KV head h // (Hq / Hkv) (grouped-query attention; the
   pages do not spell out the mapping).
@@ -78,12 +93,34 @@ def lse_merge(z_a, lse_a, z_b, lse_b):
     return wa * z_a + wb * z_b, lse
 
 
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """Round float32 values to bfloat16 bit patterns, nearest even (finite
+    inputs)."""
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def masked_attention(q, k, v, scale, visible):
+    """Softmax attention of ``q [m, D]`` over the keys ``k [n, D]`` that
+    ``visible [m, n]`` (bool) marks for each row; masked keys get weight 0."""
+    s = np.where(visible, (q @ k.T) * scale, -np.inf)
+    mx = s.max(axis=1, keepdims=True)
+    w = np.exp(s - mx)
+    return (w @ v) / w.sum(axis=1, keepdims=True)
+
+
 def draft_attn(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_len, q_off,
-               num_heads_kv: int, softmax_scale: float, requests=None):
+               num_heads_kv: int, softmax_scale: float, requests=None,
+               block_mask: str = "none", window: int = 0, summary_keys=None,
+               summary_values=None):
     """Attention output ``[total_q, Hq, D]`` (float64) for every draft row.
 
-    Inputs are the bf16 bit patterns the kernel receives.  ``requests``
-    restricts the work to a subset of requests (other rows stay NaN)."""
+    Inputs are the bf16 bit patterns the kernel receives (``summary_values``
+    is fp32 ``[batch, Hkv, S, D]``, ``summary_keys`` bf16 bits
+    ``[Hkv, S, D]``).  ``requests`` restricts the work to a subset of
+    requests (other rows stay NaN)."""
+    assert block_mask in ("none", "causal")
     total_q, Hq, D = q.shape
     G = Hq // num_heads_kv
     out = np.full((total_q, Hq, D), np.nan)
@@ -92,13 +129,25 @@ def draft_attn(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_len, q_off,
         r0, r1 = int(q_off[b]), int(q_off[b + 1])
         if r1 == r0:
             continue
+        kb = r1 - r0
         n = int(ctx_len[b])
+        n0 = max(0, n - window) if window > 0 else 0
         for g in range(num_heads_kv):
             kp, vp = gather_prefix(k_cache, v_cache, page_table[b], n, g)
-            k_all = bf16_bits_to_f64(np.concatenate([kp, k_blk[r0:r1, g]], 0))
-            v_all = bf16_bits_to_f64(np.concatenate([vp, v_blk[r0:r1, g]], 0))
+            ks = [kp[n0:], k_blk[r0:r1, g]]
+            vs = [vp[n0:], v_blk[r0:r1, g]]
+            n_sum = 0
+            if summary_keys is not None:
+                n_sum = summary_keys.shape[1]
+                ks.append(summary_keys[g])
+                vs.append(f32_to_bf16_bits(summary_values[b, g]))
+            k_all = bf16_bits_to_f64(np.concatenate(ks, 0))
+            v_all = bf16_bits_to_f64(np.concatenate(vs, 0))
+            n_pre = n - n0
+            visible = np.ones((kb, n_pre + kb + n_sum), bool)
+            if block_mask == "causal":
+                visible[:, n_pre:n_pre + kb] = np.tril(np.ones((kb, kb), bool))
             for h in range(g * G, (g + 1) * G):
-                z, _ = attention_lse(bf16_bits_to_f64(q[r0:r1, h]), k_all,
-                                     v_all, softmax_scale)
-                out[r0:r1, h] = z
+                out[r0:r1, h] = masked_attention(bf16_bits_to_f64(q[r0:r1, h]), k_all,
+                                                 v_all, softmax_scale, visible)
     return out

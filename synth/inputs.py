@@ -35,6 +35,7 @@ from .configs import StepConfig
 TAG_CTX, TAG_KB, TAG_VB, TAG_PERM, TAG_K, TAG_V = 1, 2, 3, 4, 5, 6
 TAG_Q, TAG_KBLK, TAG_VBLK, TAG_HID, TAG_W, TAG_TGT = 7, 8, 9, 10, 11, 12
 TAG_SIGMA, TAG_REQ, TAG_SEED, TAG_NOISE, TAG_TOK = 13, 14, 15, 16, 17
+TAG_SUMQ, TAG_SUMV, TAG_VMAP = 18, 19, 20
 
 PAGES_PER_CHUNK = 256
 W_ROWS_PER_CHUNK = 4096
@@ -383,3 +384,29 @@ class StepInputs:
         c = self.cfg
         return (_rng(c.seed, TAG_TOK, 1).standard_normal(
             (self.total_q, c.vocab)) * sigma).astype(np.float32)
+
+    # ------------------------------------------------------ context summary
+    def summary_queries(self, n_summary: int = 16) -> np.ndarray:
+        """Seeded stand-in for the learned summary queries U: bf16 bits
+        ``[Hkv, n_summary, D]`` drawn N(0, 1) like the cached keys."""
+        c = self.cfg
+        return _normal_bf16(_rng(c.seed, TAG_SUMQ, n_summary),
+                            (c.num_heads_kv, n_summary, c.head_dim), 1.0)
+
+    def summary_values(self, n_summary: int = 16) -> np.ndarray:
+        """Seeded fp32 ``[B, Hkv, n_summary, D]`` standing in for a summary
+        state when only the draft attention is exercised (an attention
+        output over N(0, 1) values is a convex combination of them, so its
+        entries are drawn N(0, 0.1^2))."""
+        c = self.cfg
+        return (_rng(c.seed, TAG_SUMV, n_summary).standard_normal(
+            (c.batch, c.num_heads_kv, n_summary, c.head_dim)) * 0.1).astype(np.float32)
+
+    # ------------------------------------------------------ pruned vocabulary
+    def pruned_vocab(self, v_draft: int) -> np.ndarray:
+        """Seeded stand-in for a pruned drafter vocabulary: ``v_draft``
+        distinct target token ids (int32, ascending), the rows of the target
+        LM head the drafter predicts over."""
+        c = self.cfg
+        ids = _rng(c.seed, TAG_VMAP, v_draft).choice(c.vocab, size=v_draft, replace=False)
+        return np.sort(ids).astype(np.int32)

@@ -60,13 +60,15 @@ def _attn(lib, **kw):
     a = dict(q=FAKE, k_blk=FAKE, v_blk=FAKE, k_cache=FAKE, v_cache=FAKE, page_table=FAKE,
              ctx_len=FAKE, q_off=FAKE, batch=2, total_q=8, max_draft_k=4, num_pages=10,
              max_pages=5, page_size=16, hq=8, hkv=2, d=128, max_total_ctx=100, split=0,
-             scale=0.088, out=FAKE, ws=FAKE, ws_bytes=1 << 40, stream=None)
+             scale=0.088, mask=0, window=0, sum_k=None, sum_v=None, n_sum=0, out=FAKE, ws=FAKE,
+             ws_bytes=1 << 40, stream=None)
     a.update(kw)
     return lib.sd_draft_attn(a["q"], a["k_blk"], a["v_blk"], a["k_cache"], a["v_cache"],
                              a["page_table"], a["ctx_len"], a["q_off"], a["batch"],
                              a["total_q"], a["max_draft_k"], a["num_pages"], a["max_pages"],
                              a["page_size"], a["hq"], a["hkv"], a["d"], a["max_total_ctx"],
-                             a["split"], a["scale"], a["out"], a["ws"], a["ws_bytes"],
+                             a["split"], a["scale"], a["mask"], a["window"], a["sum_k"],
+                             a["sum_v"], a["n_sum"], a["out"], a["ws"], a["ws_bytes"],
                              a["stream"])
 
 
@@ -74,12 +76,35 @@ def _attn(lib, **kw):
     (dict(q=None), 1), (dict(page_table=None), 1), (dict(out=None), 1),
     (dict(batch=0), 2), (dict(page_size=32), 2), (dict(d=96), 2), (dict(hq=6, hkv=4), 2),
     (dict(max_draft_k=17), 2),            # group 4 * 17 > 64 query rows
-    (dict(split=100), 2), (dict(scale=float("inf")), 2), (dict(q=ODD), 2),
+    (dict(split=100), 2), (dict(scale=float("inf")), 2), (dict(scale=0.0), 2), (dict(q=ODD), 2),
+    (dict(mask=2), 2), (dict(window=-1), 2), (dict(n_sum=65, sum_k=FAKE, sum_v=FAKE), 2),
+    (dict(n_sum=16), 1), (dict(n_sum=16, sum_k=FAKE), 1), (dict(n_sum=16, sum_k=ODD, sum_v=FAKE), 2),
     (dict(ws=None), 3), (dict(ws_bytes=10), 3),
     (dict(total_q=0), 0),                 # nothing to do: returns before launching
+    (dict(total_q=0, mask=1, window=256, n_sum=16, sum_k=FAKE, sum_v=FAKE), 0),
 ])
 def test_draft_attn_validation(lib, kw, status):
     assert _attn(lib, **kw) == status
+
+
+def _sum(lib, **kw):
+    a = dict(u=FAKE, k_cache=FAKE, v_cache=FAKE, page_table=FAKE, ctx_len=FAKE, acc=FAKE,
+             batch=2, num_pages=10, max_pages=5, page_size=16, hkv=2, d=128, n_sum=16,
+             scale=0.088, z=FAKE, c=FAKE)
+    a.update(kw)
+    return lib.sd_summary_update(a["u"], a["k_cache"], a["v_cache"], a["page_table"],
+                                 a["ctx_len"], a["acc"], a["batch"], a["num_pages"],
+                                 a["max_pages"], a["page_size"], a["hkv"], a["d"], a["n_sum"],
+                                 a["scale"], a["z"], a["c"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(u=None), 1), (dict(z=None), 1), (dict(c=None), 1), (dict(ctx_len=None), 1),
+    (dict(batch=0), 2), (dict(d=96), 2), (dict(n_sum=0), 2), (dict(n_sum=65), 2),
+    (dict(page_size=8), 2), (dict(scale=-1.0), 2), (dict(k_cache=ODD), 2),
+])
+def test_summary_update_validation(lib, kw, status):
+    assert _sum(lib, **kw) == status
 
 
 def _lm(lib, **kw):

@@ -1,0 +1,188 @@
+"""GPU parity of the attention variants and the context summary.
+
+* causal block mask, recent window, summary rows (and all three together):
+  attention outputs within 1e-2 max-abs and relative L2 < 1e-2 of the oracle;
+* the summary state kept by sd_summary_update (initialisation from a whole
+  prefix, then a fold of a_b + 1 new rows): fp32 arithmetic over at most a
+  few thousand rows here, compared with the oracle's fp64 definition within
+  max-abs 1e-4 on Z (entries of size ~0.1..1) and 1e-4 relative on c;
+* the fixed-cost context of the 128K workload (window 256 + 16 summary
+  entries) at full size, on sampled requests.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_drafting_sd_amd as sd
+from oracle import attention as oa, compare, summary as osum
+from synth import StepInputs, device as sdev
+from synth.configs import C1_32K, C2_128K
+
+from gpu_common import DEV, bits, log, requires_gpu
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+Z_ATOL = 1e-4
+C_RTOL = 1e-4
+
+
+def _cfg(**kw):
+    base = dict(name="variants", batch=5, ctx=("list", (0, 1, 37, 160, 1000)),
+                draft_k=("list", (3, 1, 16, 5, 8)), verify="full", num_heads_q=8,
+                num_heads_kv=2, head_dim=128, hidden=64, vocab=64, seed=5151)
+    base.update(kw)
+    return C1_32K.with_(**base)
+
+
+def _gpu_attn(inp, t=None, split_tokens=0, **kw):
+    t = sdev.attention_tensors(inp, DEV) if t is None else t
+    b = inp.budgets
+    out = sd.sd_draft_attn(t["q"], t["k_blk"], t["v_blk"], t["k_cache"], t["v_cache"],
+                           t["page_table"], t["ctx_len"], t["q_off"],
+                           max_draft_k=int(b.draft_k.max()), max_total_ctx=inp.max_total_ctx,
+                           split_tokens=split_tokens, **kw)
+    torch.cuda.synchronize()
+    return bits(out)
+
+
+def _oracle_attn(inp, requests=None, **kw):
+    b = inp.budgets
+    return oa.draft_attn(inp.q, inp.k_blk, inp.v_blk, inp.k_cache, inp.v_cache, inp.page_table,
+                         b.ctx_len, b.q_off, inp.cfg.num_heads_kv, inp.softmax_scale,
+                         requests=requests, **kw)
+
+
+def _check(got, ref, rows=None, tag=""):
+    rep = compare.attention_report(got, ref, rows=rows)
+    log(f"{tag} {rep}")
+    assert rep["ok"] and rep["rel_l2"] < 1e-2
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("split", [0, 64])
+def test_causal_block(head_dim, split):
+    inp = StepInputs(_cfg(head_dim=head_dim))
+    got = _gpu_attn(inp, split_tokens=split, block_mask=sd.SD_MASK_CAUSAL)
+    _check(got, _oracle_attn(inp, block_mask="causal"), tag=f"causal D={head_dim} split={split}")
+
+
+def test_causal_block_mha_two_block_tiles():
+    # G = 1 and K_b up to 40: the block spans two 32-key tiles
+    inp = StepInputs(_cfg(num_heads_q=2, num_heads_kv=2, head_dim=64,
+                          draft_k=("list", (40, 33, 1, 32, 17)), seed=77))
+    got = _gpu_attn(inp, block_mask=sd.SD_MASK_CAUSAL)
+    _check(got, _oracle_attn(inp, block_mask="causal"), tag="causal mha")
+
+
+@pytest.mark.parametrize("window", [1, 16, 50, 256, 2048])
+def test_recent_window(window):
+    inp = StepInputs(_cfg())
+    got = _gpu_attn(inp, split_tokens=64, window=window)
+    _check(got, _oracle_attn(inp, window=window), tag=f"window {window}")
+
+
+@pytest.mark.parametrize("n_summary", [16, 40])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fixed_cost_context(n_summary, causal):
+    inp = StepInputs(_cfg(head_dim=64 if n_summary == 40 else 128))
+    u, z = inp.summary_queries(n_summary), inp.summary_values(n_summary)
+    t = sdev.attention_tensors(inp, DEV)
+    mask = sd.SD_MASK_CAUSAL if causal else sd.SD_MASK_NONE
+    got = _gpu_attn(inp, t=t, window=256, block_mask=mask,
+                    summary_keys=sdev.bf16(u, DEV), summary_values=sdev.f32(z, DEV))
+    ref = _oracle_attn(inp, window=256, block_mask="causal" if causal else "none",
+                       summary_keys=u, summary_values=z)
+    _check(got, ref, tag=f"fixed-cost S={n_summary} causal={causal}")
+
+
+def _gpu_summary(inp, u, ctx, acc=None, state=None):
+    t = sdev.attention_tensors(inp, DEV)
+    B, hkv, S, D = inp.cfg.batch, inp.cfg.num_heads_kv, u.shape[1], u.shape[2]
+    if state is None:
+        z = torch.full((B, hkv, S, D), float("nan"), device=DEV)
+        c = torch.full((B, hkv, S), float("nan"), device=DEV)
+    else:
+        z, c = state
+    sd.sd_summary_update(sdev.bf16(u, DEV), t["k_cache"], t["v_cache"], t["page_table"],
+                         sdev.i32(ctx, DEV), None if acc is None else sdev.i32(acc, DEV), z, c)
+    torch.cuda.synchronize()
+    return z, c
+
+
+def _check_summary(z, c, Zr, Cr, tag):
+    zg, cg = z.cpu().numpy().astype(np.float64), c.cpu().numpy().astype(np.float64)
+    empty = Cr == -np.inf
+    assert np.all(cg[empty] == -np.inf) and np.all(zg[empty] == 0)
+    dz = np.abs(zg - Zr).max()
+    dc = np.abs(cg[~empty] - Cr[~empty]) / np.maximum(1.0, np.abs(Cr[~empty]))
+    log(f"{tag}: Z max-abs {dz:.3g}, c max-rel {dc.max() if dc.size else 0:.3g}")
+    assert dz <= Z_ATOL and (dc.size == 0 or dc.max() <= C_RTOL)
+
+
+@pytest.mark.parametrize("head_dim,n_summary", [(128, 16), (64, 64)])
+def test_summary_init_then_fold(head_dim, n_summary):
+    # every round appends a_b + 1 >= 1 rows; the first request starts empty
+    inp = StepInputs(_cfg(head_dim=head_dim, batch=5, ctx=("list", (1, 2, 37, 160, 1000)),
+                          draft_k=("list", (16, 16, 16, 16, 16))))
+    b = inp.budgets
+    u = inp.summary_queries(n_summary)
+    hkv, scale = inp.cfg.num_heads_kv, inp.softmax_scale
+    # the last a_b + 1 rows of each prefix are the new rows of the round
+    acc = np.array([0, 0, 5, 16, 9], np.int32)
+    old = (b.ctx_len - acc - 1).astype(np.int32)
+    Z0, C0 = osum.summary_init(u, inp.k_cache, inp.v_cache, inp.page_table, old, hkv, scale)
+    z, c = _gpu_summary(inp, u, old)
+    _check_summary(z, c, Z0, C0, f"init D={head_dim} S={n_summary}")
+    # fold from the GPU's own state: the oracle folds into the same fp32 state
+    Zs = z.cpu().numpy().astype(np.float64)
+    Cs = c.cpu().numpy().astype(np.float64)
+    Z1, C1 = osum.summary_update(u, inp.k_cache, inp.v_cache, inp.page_table, old, acc, Zs, Cs,
+                                 hkv, scale)
+    z, c = _gpu_summary(inp, u, old, acc, state=(z, c))
+    _check_summary(z, c, Z1, C1, f"fold D={head_dim} S={n_summary}")
+    # and the result is the summary of every row (eq. (5))
+    Zf, Cf = osum.summary_init(u, inp.k_cache, inp.v_cache, inp.page_table,
+                               b.ctx_len.astype(np.int32), hkv, scale)
+    _check_summary(z, c, Zf, Cf, "fold == summary of all rows")
+
+
+def test_summary_then_attention_chain():
+    inp = StepInputs(_cfg())
+    u = inp.summary_queries(16)
+    z, c = _gpu_summary(inp, u, inp.budgets.ctx_len)
+    got = _gpu_attn(inp, window=256, summary_keys=sdev.bf16(u, DEV), summary_values=z)
+    ref = _oracle_attn(inp, window=256, summary_keys=u, summary_values=z.cpu().numpy())
+    _check(got, ref, tag="summary -> attention")
+
+
+def test_fixed_cost_full_size_128k():
+    cfg = C2_128K
+    inp = StepInputs(cfg)
+    u = inp.summary_queries(16)
+    t = sdev.attention_tensors(inp, DEV)
+    b = inp.budgets
+    B, hkv, D = cfg.batch, cfg.num_heads_kv, cfg.head_dim
+    z = torch.empty((B, hkv, 16, D), device=DEV)
+    c = torch.empty((B, hkv, 16), device=DEV)
+    uu = sdev.bf16(u, DEV)
+    sd.sd_summary_update(uu, t["k_cache"], t["v_cache"], t["page_table"], t["ctx_len"], None, z, c)
+    out = sd.sd_draft_attn(t["q"], t["k_blk"], t["v_blk"], t["k_cache"], t["v_cache"],
+                           t["page_table"], t["ctx_len"], t["q_off"],
+                           max_draft_k=int(b.draft_k.max()), max_total_ctx=inp.max_total_ctx,
+                           window=256, summary_keys=uu, summary_values=z)
+    torch.cuda.synchronize()
+    reqs = [0, B - 1]
+    zr = np.zeros((B, hkv, 16, D))
+    cr = np.zeros((B, hkv, 16))
+    for r in reqs:
+        kl, vl = inp.logical_kv(r)
+        for g in range(hkv):
+            zr[r, g], cr[r, g] = osum.summary_of_rows(u[g], kl[:, g], vl[:, g], inp.softmax_scale)
+    zg, cg = z.cpu().numpy(), c.cpu().numpy()
+    dz = max(np.abs(zg[r] - zr[r]).max() for r in reqs)
+    dc = max((np.abs(cg[r] - cr[r]) / np.maximum(1, np.abs(cr[r]))).max() for r in reqs)
+    log(f"128K summary init: Z max-abs {dz:.3g}, c max-rel {dc:.3g}")
+    assert dz <= 1e-3 and dc <= C_RTOL   # 131072 fp32 terms per entry
+    rows = np.concatenate([np.arange(b.q_off[r], b.q_off[r + 1]) for r in reqs])
+    ref = _oracle_attn(inp, requests=reqs, window=256, summary_keys=u, summary_values=zg)
+    _check(bits(out), ref, rows=rows, tag="128K fixed-cost attention")
