@@ -154,18 +154,24 @@ def sd_summary_update(summary_queries, k_cache, v_cache, page_table, ctx_len, ac
     return summary_values, summary_lse
 
 
-def sd_lm_head_probs(hidden, w_vocab, q_off, req_id, seed: int, *, logits=None, lse=None,
-                     draft_tokens=None, workspace=None, stream=None
+def sd_lm_head_probs(hidden, w_vocab, q_off, req_id, seed: int, *, vocab_map=None,
+                     greedy: bool = False, logits=None, lse=None, draft_tokens=None,
+                     workspace=None, stream=None
                      ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """LM head + softmax statistics + draft sampling; see include/sd.h."""
+    """LM head + softmax statistics + draft sampling; see include/sd.h.
+    ``vocab_map`` (int32 [V_draft] target ids) prunes the drafter's
+    vocabulary; ``greedy`` draws the argmax."""
     lib = load()
     dev = hidden.device
     _req(hidden, "hidden", _BF16, dev)
     _req(w_vocab, "w_vocab", _BF16, dev)
     _req(q_off, "q_off", _I32, dev)
     _req(req_id, "req_id", _U32, dev)
+    if vocab_map is not None:
+        _req(vocab_map, "vocab_map", _I32, dev)
     M, H = hidden.shape
-    V = w_vocab.shape[0]
+    w_rows = w_vocab.shape[0]
+    V = w_rows if vocab_map is None else vocab_map.numel()
     batch = q_off.numel() - 1
     if logits is None:
         logits = torch.empty(M, V, dtype=torch.float32, device=dev)
@@ -176,17 +182,21 @@ def sd_lm_head_probs(hidden, w_vocab, q_off, req_id, seed: int, *, logits=None, 
     nbytes = lib.sd_lm_head_workspace_size(M, V)
     workspace = _workspace(workspace, nbytes, dev)
     st = lib.sd_lm_head_probs(_ptr(hidden), _ptr(w_vocab), M, H, V, _ptr(q_off), batch,
-                              _ptr(req_id), int(seed) & ((1 << 64) - 1), _ptr(logits),
-                              _ptr(lse), _ptr(draft_tokens), _ptr(workspace), workspace.numel(),
+                              _ptr(req_id), int(seed) & ((1 << 64) - 1), _ptr(vocab_map),
+                              w_rows, int(bool(greedy)), _ptr(logits), _ptr(lse),
+                              _ptr(draft_tokens), _ptr(workspace), workspace.numel(),
                               _stream_handle(stream))
     check("sd_lm_head_probs", st)
     return logits, lse, draft_tokens
 
 
 def sd_verify(target_logits, t_off, draft_logits, draft_lse, draft_tokens, q_off, req_id,
-              seed: int, *, accepted_len=None, next_token=None, accept_ratio=None,
-              want_ratio: bool = True, workspace=None, stream=None):
+              seed: int, *, draft_vocab_inv=None, greedy: bool = False, accepted_len=None,
+              next_token=None, accept_ratio=None, want_ratio: bool = True, workspace=None,
+              stream=None):
     """Speculative-sampling verification; see include/sd.h.
+    ``draft_vocab_inv`` (int32 [V]: drafter entry of each target id or -1)
+    declares a pruned drafter vocabulary; ``greedy`` verifies at temperature 0.
     Returns (accepted_len, next_token, accept_ratio or None)."""
     lib = load()
     dev = target_logits.device
@@ -209,8 +219,12 @@ def sd_verify(target_logits, t_off, draft_logits, draft_lse, draft_tokens, q_off
         accept_ratio = torch.empty(total_q, dtype=torch.float32, device=dev)
     nbytes = lib.sd_verify_workspace_size(batch, total_q, R, V)
     workspace = _workspace(workspace, nbytes, dev)
+    v_draft = draft_logits.shape[1] if draft_logits.dim() == 2 else V
+    if draft_vocab_inv is not None:
+        _req(draft_vocab_inv, "draft_vocab_inv", _I32, dev)
     st = lib.sd_verify(_ptr(target_logits), _ptr(t_off), _ptr(draft_logits), _ptr(draft_lse),
-                       _ptr(draft_tokens), _ptr(q_off), batch, total_q, R, V, _ptr(req_id),
+                       _ptr(draft_tokens), _ptr(q_off), batch, total_q, R, V,
+                       _ptr(draft_vocab_inv), v_draft, int(bool(greedy)), _ptr(req_id),
                        int(seed) & ((1 << 64) - 1), _ptr(accepted_len), _ptr(next_token),
                        _ptr(accept_ratio), _ptr(workspace), workspace.numel(),
                        _stream_handle(stream))

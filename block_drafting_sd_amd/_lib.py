@@ -30,10 +30,10 @@ SIGNATURES = {
                                  _i32, _i32, _i32, _f32, _vp, _vp, _vp]),
     "sd_lm_head_workspace_size": (_sz, [_i32, _i32]),
     "sd_lm_head_probs": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _u64,
-                                _vp, _vp, _vp, _vp, _sz, _vp]),
+                                _vp, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sd_verify_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
     "sd_verify": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
-                         _vp, _u64, _vp, _vp, _vp, _vp, _sz, _vp]),
+                         _vp, _i32, _i32, _vp, _u64, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 
 _LIB = None

@@ -92,7 +92,8 @@ void lm_gemm(LmArgs a) {
     const int q = is_w ? kWLoads * wave + i : kHLoads * wave + (i - kWLoads);
     const int r = 16 * q + (lane >> 2);
     const int c = (lane & 3) ^ swz(r);
-    src[i] = is_w ? a.w + static_cast<size_t>(min(v0 + r, a.V - 1)) * a.H + 8 * c
+    const int wr = min(v0 + r, a.V - 1);   // drafter vocab entry -> row of W
+    src[i] = is_w ? a.w + static_cast<size_t>(a.vmap ? clampi(a.vmap[wr], 0, a.w_rows - 1) : wr) * a.H + 8 * c
                   : a.hidden + static_cast<size_t>(min(m0 + r, a.M - 1)) * a.H + 8 * c;
   }
   const uint32_t lds_ring = lds_addr(smem);
@@ -192,13 +193,16 @@ void lm_gemm(LmArgs a) {
               if (vb + e < a.V) row[vb + e] = z[e];
           }
           if (vb < a.V) {
-            const u32x4 w = philox4x32_10(u32x4{static_cast<uint32_t>(vb >> 2), pos, rid, kStreamDraft},
-                                          a.key0, a.key1);
+            // Gumbel-max keys; greedy decoding ranks the logits themselves
+            const u32x4 w = a.greedy ? u32x4{0u, 0u, 0u, 0u}
+                                     : philox4x32_10(u32x4{static_cast<uint32_t>(vb >> 2), pos, rid,
+                                                           kStreamDraft},
+                                                     a.key0, a.key1);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               if (vb + e < a.V) {
                 se += __builtin_amdgcn_exp2f((z[e] - mx) * kLog2e);
-                const float key = z[e] + gumbel_from_bits(w[e]);
+                const float key = a.greedy ? z[e] : z[e] + gumbel_from_bits(w[e]);
                 if (better(key, vb + e, best.key, best.idx)) best = Cand{key, vb + e};
               }
             }
@@ -251,7 +255,8 @@ __global__ __launch_bounds__(kThreads) void lm_row_reduce(LmArgs a) {
   best = block_best<kThreads>(best, shk, shi);
   if (threadIdx.x == 0) {
     a.lse[m] = mx + logf(se);
-    a.tokens[m] = best.idx;
+    const int t = clampi(best.idx, 0, a.V - 1);
+    a.tokens[m] = a.vmap ? clampi(a.vmap[t], 0, a.w_rows - 1) : t;
   }
 }
 

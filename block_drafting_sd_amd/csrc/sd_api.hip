@@ -67,7 +67,7 @@ VerifyLayout verify_layout(int32_t batch, int32_t total_q, int32_t R, int32_t V)
   L.n_chunks = (V + sd::kVerifyChunk - 1) / sd::kVerifyChunk;
   L.n_schunks = (V + sd::kSampleChunk - 1) / sd::kSampleChunk;
   L.off_row = 0;
-  L.off_samp = align_up(static_cast<size_t>(R + total_q) * L.n_chunks * sizeof(float2));
+  L.off_samp = align_up(static_cast<size_t>(R + total_q) * L.n_chunks * sizeof(float4));
   L.total = L.off_samp + align_up(static_cast<size_t>(batch) * L.n_schunks * 2 * sizeof(float4));
   return L;
 }
@@ -208,12 +208,13 @@ size_t sd_lm_head_workspace_size(int32_t M, int32_t V) {
 
 sd_status sd_lm_head_probs(const void* hidden, const void* w_vocab, int32_t M, int32_t H, int32_t V,
                            const int32_t* q_off, int32_t batch, const uint32_t* req_id,
-                           uint64_t seed, float* logits, float* lse, int32_t* draft_tokens,
+                           uint64_t seed, const int32_t* vocab_map, int32_t w_rows,
+                           int32_t greedy, float* logits, float* lse, int32_t* draft_tokens,
                            void* workspace, size_t workspace_bytes, void* stream) {
   if (!hidden || !w_vocab || !q_off || !req_id || !logits || !lse || !draft_tokens)
     return SD_ERR_NULL;
   if (M < 1 || batch < 1 || V < 1 || H < sd::kLmHMultiple || H > 65536 ||
-      H % sd::kLmHMultiple != 0)
+      H % sd::kLmHMultiple != 0 || (greedy != 0 && greedy != 1) || (vocab_map && w_rows < 1))
     return SD_ERR_SHAPE;
   if (!aligned16(hidden) || !aligned16(w_vocab) || !aligned16(logits)) return SD_ERR_SHAPE;
   const LmLayout L = lm_layout(M, V);
@@ -230,6 +231,9 @@ sd_status sd_lm_head_probs(const void* hidden, const void* w_vocab, int32_t M, i
   a.lse = lse;
   a.tokens = draft_tokens;
   a.part = static_cast<float4*>(workspace);
+  a.vmap = vocab_map;
+  a.w_rows = vocab_map ? w_rows : V;
+  a.greedy = greedy;
   a.M = M;
   a.H = H;
   a.V = V;
@@ -249,13 +253,17 @@ size_t sd_verify_workspace_size(int32_t batch, int32_t total_q, int32_t total_ta
 sd_status sd_verify(const float* target_logits, const int32_t* t_off, const float* draft_logits,
                     const float* draft_lse, const int32_t* draft_tokens, const int32_t* q_off,
                     int32_t batch, int32_t total_q, int32_t total_target_rows, int32_t V,
+                    const int32_t* draft_vocab_inv, int32_t v_draft, int32_t greedy,
                     const uint32_t* req_id, uint64_t seed, int32_t* accepted_len,
                     int32_t* next_token, float* accept_ratio, void* workspace,
                     size_t workspace_bytes, void* stream) {
   if (!target_logits || !t_off || !q_off || !req_id || !accepted_len || !next_token)
     return SD_ERR_NULL;
   if (total_q > 0 && (!draft_logits || !draft_tokens)) return SD_ERR_NULL;
-  if (batch < 1 || total_q < 0 || total_target_rows < 1 || V < 1) return SD_ERR_SHAPE;
+  if (draft_vocab_inv && total_q > 0 && !draft_lse) return SD_ERR_NULL;
+  if (batch < 1 || total_q < 0 || total_target_rows < 1 || V < 1 || (greedy != 0 && greedy != 1) ||
+      (draft_vocab_inv && v_draft < 1))
+    return SD_ERR_SHAPE;
   const VerifyLayout L = verify_layout(batch, total_q, total_target_rows, V);
   if (static_cast<int64_t>(total_target_rows + total_q) * L.n_chunks > (int64_t(1) << 31) - 1 ||
       static_cast<int64_t>(batch) * L.n_schunks > (int64_t(1) << 31) - 1)
@@ -267,13 +275,16 @@ sd_status sd_verify(const float* target_logits, const int32_t* t_off, const floa
   a.t_off = t_off;
   a.draft = draft_logits;
   a.draft_lse = draft_lse;
+  a.vinv = draft_vocab_inv;
+  a.v_draft = draft_vocab_inv ? v_draft : V;
+  a.greedy = greedy;
   a.tokens = draft_tokens;
   a.q_off = q_off;
   a.req_id = req_id;
   a.accepted = accepted_len;
   a.next_token = next_token;
   a.accept_ratio = accept_ratio;
-  a.row_part = reinterpret_cast<float2*>(ws + L.off_row);
+  a.row_part = reinterpret_cast<float4*>(ws + L.off_row);
   a.samp_part = reinterpret_cast<float4*>(ws + L.off_samp);
   a.batch = batch;
   a.total_q = total_q;

@@ -81,6 +81,9 @@ struct LmArgs {
   float* lse;               // [M]
   int32_t* tokens;          // [M]
   float4* part;             // [M][n_vt] (max, sumexp, best key, best index)
+  const int32_t* vmap;      // [V] W row of each drafter vocab entry, or null (identity)
+  int32_t w_rows;           // rows of w (bound for vmap entries)
+  int32_t greedy;           // 1: tokens are argmax of the logits (no uniforms)
   int32_t M, H, V, batch, n_vt, n_mt;
   uint32_t key0, key1;
 };
@@ -96,15 +99,18 @@ hipError_t launch_lm_head(const LmArgs& a, hipStream_t s);
 struct VerifyArgs {
   const float* target;      // [R, V]
   const int32_t* t_off;     // [batch + 1]
-  const float* draft;       // [total_q, V]
+  const float* draft;       // [total_q, v_draft]
   const float* draft_lse;   // [total_q] or null
+  const int32_t* vinv;      // [V] drafter vocab entry of each target entry (-1: none), or null
+  int32_t v_draft;          // row length of draft (V unless the drafter vocab is pruned)
+  int32_t greedy;           // 1: temperature 0 on both sides
   const int32_t* tokens;    // [total_q]
   const int32_t* q_off;     // [batch + 1]
   const uint32_t* req_id;   // [batch]
   int32_t* accepted;        // [batch]
   int32_t* next_token;      // [batch]
   float* accept_ratio;      // [total_q] or null
-  float2* row_part;         // [(R + total_q) * n_chunks] (max, sumexp)
+  float4* row_part;         // [(R + total_q) * n_chunks] (max, sumexp, argmax, -)
   float4* samp_part;        // [batch * n_schunks * 2]
   int32_t batch, total_q, R, V, n_chunks, n_schunks;
   uint32_t key0, key1;

@@ -1,6 +1,10 @@
 // Speculative-sampling verification ("LongSpark", sec. 2.1, eqs. (1)-(2) and
 // the bonus-token rule after eq. (2); "ForeSpark", sec. 4.4 for verify
-// budgets b_b <= K_b).
+// budgets b_b <= K_b).  Variants: temperature 0 on both sides (p_j and q_j
+// one-hot at their argmax: accept iff y_j = argmax p_j, correction or bonus
+// = argmax p_j; "LongSpark", App. D.1 and "H-Spec", sec. 4 evaluate greedy
+// decoding) and a pruned drafter vocabulary (q_j is zero outside it; "H-Spec",
+// App. B.2).
 //
 // Three launches, no host synchronisation:
 //   1. verify_rowstats  grid (rows x 8192-entry chunks): per chunk (max, sum
@@ -26,67 +30,83 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxVerify = 255;   // b_b handled per request
 
-// (max, sum exp(x - max)) of one vocab chunk of one row.  Thread t holds
-// entries 4 (t + 256 j) + e of the chunk.
+// (max, sum exp(x - max), first index of the max) of one vocab chunk of one
+// row.  Thread t holds entries 4 (t + 256 j) + e of the chunk.
 __global__ __launch_bounds__(kThreads) void verify_rowstats(VerifyArgs a) {
   __shared__ float sh[kThreads / 64];
+  __shared__ float shk[kThreads / 64];
+  __shared__ int shi[kThreads / 64];
   constexpr int kGroups = kVerifyChunk / (4 * kThreads);
   const int row = blockIdx.x / a.n_chunks;
   const int c = blockIdx.x % a.n_chunks;
-  const float* src = row < a.R ? a.target + static_cast<size_t>(row) * a.V
-                               : a.draft + static_cast<size_t>(row - a.R) * a.V;
+  const bool tgt = row < a.R;
+  const int len = tgt ? a.V : a.v_draft;
+  const float* src = tgt ? a.target + static_cast<size_t>(row) * a.V
+                         : a.draft + static_cast<size_t>(row - a.R) * a.v_draft;
   const int lo = c * kVerifyChunk;
-  const bool vec_ok = (a.V & 3) == 0;
+  const bool vec_ok = (len & 3) == 0;
   f32x4 x[kGroups];
 #pragma unroll
   for (int j = 0; j < kGroups; ++j) {
     const int v = lo + 4 * (threadIdx.x + kThreads * j);
-    if (vec_ok && v + 3 < a.V) {
+    if (vec_ok && v + 3 < len) {
       x[j] = *reinterpret_cast<const f32x4*>(src + v);
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[j][e] = v + e < a.V ? src[v + e] : -INFINITY;
+      for (int e = 0; e < 4; ++e) x[j][e] = v + e < len ? src[v + e] : -INFINITY;
     }
   }
-  float mx = -FLT_MAX;
+  Cand best{-FLT_MAX, 0x7fffffff};
 #pragma unroll
   for (int j = 0; j < kGroups; ++j)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, x[j][e]);
-  mx = block_reduce_max<kThreads>(mx, sh);
+    for (int e = 0; e < 4; ++e) {
+      const int v = lo + 4 * (threadIdx.x + kThreads * j) + e;
+      if (v < len && better(x[j][e], v, best.key, best.idx)) best = Cand{x[j][e], v};
+    }
+  best = block_best<kThreads>(best, shk, shi);
+  const float mx = best.key;
   float se = 0.f;
 #pragma unroll
   for (int j = 0; j < kGroups; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) se += __builtin_amdgcn_exp2f((x[j][e] - mx) * kLog2e);
   se = block_reduce_sum<kThreads>(se, sh);
-  if (threadIdx.x == 0) a.row_part[blockIdx.x] = make_float2(mx, se);
+  if (threadIdx.x == 0) a.row_part[blockIdx.x] = make_float4(mx, se, __int_as_float(best.idx), 0.f);
 }
 
-// Log-normaliser of a row from its n chunk partials; the partials are read
-// eight at a time (clamped index, duplicates weighted zero) so the loads overlap.
-__device__ float merge_lse(const float2* part, int n) {
+// Log-normaliser and first argmax of a row from its n chunk partials; the
+// partials are read eight at a time (clamped index, duplicates weighted zero)
+// so the loads overlap.
+__device__ float merge_row(const float4* part, int n, int& amax) {
   constexpr int U = 8;
   float mx = -FLT_MAX;
   float s = 0.f;
+  Cand best{-FLT_MAX, 0x7fffffff};
   for (int i0 = 0; i0 < n; i0 += U) {
-    float2 v[U];
+    float4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) v[u] = part[min(i0 + u, n - 1)];
     float m2 = mx;
 #pragma unroll
-    for (int u = 0; u < U; ++u) m2 = fmaxf(m2, v[u].x);
+    for (int u = 0; u < U; ++u) {
+      m2 = fmaxf(m2, v[u].x);
+      const int idx = __float_as_int(v[u].z);
+      if (i0 + u < n && better(v[u].x, idx, best.key, best.idx)) best = Cand{v[u].x, idx};
+    }
     s *= __builtin_amdgcn_exp2f((mx - m2) * kLog2e);
 #pragma unroll
     for (int u = 0; u < U; ++u)
       s += i0 + u < n ? v[u].y * __builtin_amdgcn_exp2f((v[u].x - m2) * kLog2e) : 0.f;
     mx = m2;
   }
+  amax = best.idx;
   return mx + logf(s);
 }
 
 __global__ __launch_bounds__(kThreads) void verify_sample(VerifyArgs a) {
   __shared__ float s_lse_p[kMaxVerify + 1];
+  __shared__ int s_amax_p[kMaxVerify + 1];
   __shared__ float s_lse_q[kMaxVerify];
   __shared__ int s_ok[kMaxVerify + 1];
   __shared__ int s_a;
@@ -113,21 +133,32 @@ __global__ __launch_bounds__(kThreads) void verify_sample(VerifyArgs a) {
 
   // A: log-normalisers of the rows this request may touch
   for (int i = tid; i <= nv; i += kThreads)
-    s_lse_p[i] = merge_lse(a.row_part + static_cast<size_t>(t0 + i) * a.n_chunks, a.n_chunks);
-  for (int i = tid; i < nv; i += kThreads)
+    s_lse_p[i] = merge_row(a.row_part + static_cast<size_t>(t0 + i) * a.n_chunks, a.n_chunks,
+                           s_amax_p[i]);
+  for (int i = tid; i < nv; i += kThreads) {
+    int unused;
     s_lse_q[i] = a.draft_lse ? a.draft_lse[q0 + i]
-                             : merge_lse(a.row_part + static_cast<size_t>(a.R + q0 + i) * a.n_chunks,
-                                         a.n_chunks);
+                             : merge_row(a.row_part + static_cast<size_t>(a.R + q0 + i) * a.n_chunks,
+                                         a.n_chunks, unused);
+  }
   __syncthreads();
 
-  // B: every ratio test in parallel (eq. (1)): r_j = min(1, p_j(y_j)/q_j(y_j))
+  // B: every ratio test in parallel (eq. (1)): r_j = min(1, p_j(y_j)/q_j(y_j));
+  // at temperature 0 both distributions are one-hot and r_j = [y_j = argmax p_j]
   for (int i = tid; i < nv; i += kThreads) {
     const int j = i + 1;
     const int y = clampi(a.tokens[q0 + i], 0, a.V - 1);
-    const float lp = a.target[static_cast<size_t>(t0 + i) * a.V + y] - s_lse_p[i];
-    const float lq = a.draft[static_cast<size_t>(q0 + i) * a.V + y] - s_lse_q[i];
     float r = 1.f;
-    if (expf(lq) > 0.f) r = fminf(1.f, expf(lp - lq));
+    if (a.greedy) {
+      r = y == s_amax_p[i] ? 1.f : 0.f;
+    } else {
+      const int iy = a.vinv ? a.vinv[y] : y;   // y in the drafter's vocabulary
+      const float lp = a.target[static_cast<size_t>(t0 + i) * a.V + y] - s_lse_p[i];
+      const float lq = iy >= 0 && iy < a.v_draft
+                           ? a.draft[static_cast<size_t>(q0 + i) * a.v_draft + iy] - s_lse_q[i]
+                           : -INFINITY;
+      if (expf(lq) > 0.f) r = fminf(1.f, expf(lp - lq));
+    }
     const u32x4 w = philox4x32_10(u32x4{0u, static_cast<uint32_t>(j), rid, kStreamAccept},
                                   a.key0, a.key1);
     s_ok[i] = accept_from_bits(w[0]) < r;
@@ -150,10 +181,10 @@ __global__ __launch_bounds__(kThreads) void verify_sample(VerifyArgs a) {
   }
   __syncthreads();
   const int acc = s_a;
-  const bool residual = acc < nv;
+  const bool residual = !a.greedy && acc < nv;
   const int j = acc + 1;                      // position of the drawn token
   const float* xrow = a.target + static_cast<size_t>(t0 + acc) * a.V;
-  const float* zrow = a.draft + static_cast<size_t>(q0 + acc) * a.V;
+  const float* zrow = a.draft + static_cast<size_t>(q0 + acc) * a.v_draft;
   const float lse_p = s_lse_p[acc];
   const float lse_q = residual ? s_lse_q[acc] : 0.f;
 
@@ -170,22 +201,31 @@ __global__ __launch_bounds__(kThreads) void verify_sample(VerifyArgs a) {
     f32x4 xv, zv;
     if (vec_ok && g + 3 < a.V) {
       xv = *reinterpret_cast<const f32x4*>(xrow + g);
-      if (residual) zv = *reinterpret_cast<const f32x4*>(zrow + g);
+      if (residual && !a.vinv) zv = *reinterpret_cast<const f32x4*>(zrow + g);
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         xv[e] = g + e < a.V ? xrow[g + e] : 0.f;
-        zv[e] = residual && g + e < a.V ? zrow[g + e] : 0.f;
+        zv[e] = residual && !a.vinv && g + e < a.V ? zrow[g + e] : 0.f;
       }
     }
-    const u32x4 w = philox4x32_10(u32x4{static_cast<uint32_t>(g >> 2), static_cast<uint32_t>(j),
-                                        rid, kStreamSample},
-                                  a.key0, a.key1);
+    if (residual && a.vinv) {
+      // q is zero outside the drafter's vocabulary
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int iz = g + e < a.V ? a.vinv[g + e] : -1;
+        zv[e] = iz >= 0 && iz < a.v_draft ? zrow[iz] : -INFINITY;
+      }
+    }
+    const u32x4 w = a.greedy ? u32x4{0u, 0u, 0u, 0u}
+                             : philox4x32_10(u32x4{static_cast<uint32_t>(g >> 2),
+                                                   static_cast<uint32_t>(j), rid, kStreamSample},
+                                             a.key0, a.key1);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int v = g + e;
       if (v < a.V) {
-        const float gn = gumbel_from_bits(w[e]);
+        const float gn = a.greedy ? 0.f : gumbel_from_bits(w[e]);
         const float x = xv[e];
         const float kp = x + gn;
         if (better(kp, v, best_p.key, best_p.idx)) best_p = Cand{kp, v};

@@ -208,19 +208,33 @@ sd_status sd_summary_update(const void* summary_queries, const void* k_cache,
  * drafting" (block-parallel drafting is one forward pass then one sampling
  * step).
  *
- * For every row m < M:  logits[m, v] = sum_k hidden[m, k] * w_vocab[v, k]
- * (bf16 products, fp32 accumulation), lse[m] = log sum_v exp(logits[m, v]),
- * draft_tokens[m] = argmax_v (logits[m, v] - log(-log u_v)) with the stream-0
- * uniforms of (request b, position j = m - q_off[b] + 1).  The draft
- * distribution is q_m = exp(logits[m, :] - lse[m]).
+ * For every row m < M and drafter vocabulary entry v < V, with W_v the row
+ * w_vocab[v] (or w_vocab[vocab_map[v]] when the drafter's vocabulary is
+ * pruned):  logits[m, v] = sum_k hidden[m, k] * W_v[k] (bf16 products, fp32
+ * accumulation), lse[m] = log sum_v exp(logits[m, v]), and the drawn entry
+ * v* = argmax_v (logits[m, v] - log(-log u_v)) with the stream-0 uniforms of
+ * (request b, position j = m - q_off[b] + 1), or v* = argmax_v logits[m, v]
+ * when greedy = 1 (temperature 0; no uniforms).  draft_tokens[m] = v*, or
+ * vocab_map[v*] (a target token id) when the vocabulary is pruned.  The
+ * draft distribution is q_m = exp(logits[m, :] - lse[m]) over the V entries.
+ *
+ * Variants: a pruned drafter vocabulary restricts drafting to a subset of
+ * the target's vocabulary, reading those rows of the target's head in place
+ * ("H-Spec", App. B.2); greedy decoding is the temperature-0 setting the
+ * pages also evaluate ("LongSpark", App. D.1).
  *
  * Arguments
  *   hidden   bf16 [M, H]  final draft states after the target's final norm
- *   w_vocab  bf16 [V, H]  the target's LM head (nn.Linear layout), in place
+ *   w_vocab  bf16 [w_rows, H] the target's LM head (nn.Linear layout), in
+ *            place; [V, H] when vocab_map is NULL
  *   M >= 1, H a multiple of 64 (<= 65536), 1 <= V < 2^31
  *   q_off    int32 [batch+1] row offsets of the requests (as for attention);
  *            rows outside [0, q_off[batch]) use position m + 1 of request 0
  *   req_id   uint32 [batch]  Philox counter word of each request
+ *   vocab_map int32 [V] target token id of each drafter entry (0 <= id <
+ *            w_rows), or NULL (the drafter predicts over all V rows)
+ *   w_rows   rows of w_vocab when vocab_map is given (ignored otherwise)
+ *   greedy   0 (sample) or 1 (argmax; the smallest index wins a tie)
  *   logits   fp32 [M, V] out;  lse fp32 [M] out;  draft_tokens int32 [M] out
  * ------------------------------------------------------------------------ */
 size_t sd_lm_head_workspace_size(int32_t M, int32_t V);
@@ -228,8 +242,9 @@ size_t sd_lm_head_workspace_size(int32_t M, int32_t V);
 sd_status sd_lm_head_probs(const void* hidden, const void* w_vocab, int32_t M,
                            int32_t H, int32_t V, const int32_t* q_off,
                            int32_t batch, const uint32_t* req_id,
-                           uint64_t seed, float* logits, float* lse,
-                           int32_t* draft_tokens, void* workspace,
+                           uint64_t seed, const int32_t* vocab_map,
+                           int32_t w_rows, int32_t greedy, float* logits,
+                           float* lse, int32_t* draft_tokens, void* workspace,
                            size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
@@ -255,13 +270,28 @@ sd_status sd_lm_head_probs(const void* hidden, const void* w_vocab, int32_t M,
  * p_{b_b+1}.  Draws use the stream-2 uniforms of position j (b_b + 1 for the
  * bonus).  Probabilities are evaluated in fp32.
  *
+ * Variants: with a pruned drafter vocabulary q_j is zero outside it (its
+ * entry for target token v is draft_logits[.., draft_vocab_inv[v]], absent
+ * when that is -1), which keeps verification lossless ("H-Spec", App. B.2).
+ * With greedy = 1 both sides are at temperature 0: p_j and q_j are one-hot
+ * at their argmax, so y_j is accepted iff it is the first argmax of
+ * target_logits row j, and next_token is the first argmax of the first
+ * rejected row, or of row b_b + 1 (the limit of the rules above; no
+ * uniforms).
+ *
  * Arguments
  *   target_logits fp32 [total_target_rows, V]
  *   t_off    int32 [batch+1], 0 <= b_b = t_off[b+1] - t_off[b] - 1 <= K_b
- *   draft_logits  fp32 [total_q, V]  (as written by sd_lm_head_probs)
- *   draft_lse     fp32 [total_q] or NULL (then computed here)
- *   draft_tokens  int32 [total_q]
+ *   draft_logits  fp32 [total_q, V], or [total_q, v_draft] with a pruned
+ *                 vocabulary (as written by sd_lm_head_probs)
+ *   draft_lse     fp32 [total_q] or NULL (then computed here; required with
+ *                 a pruned vocabulary)
+ *   draft_tokens  int32 [total_q]  target token ids
  *   q_off    int32 [batch+1]  as for sd_lm_head_probs
+ *   draft_vocab_inv int32 [V] drafter entry of each target token, -1 if
+ *            outside the drafter's vocabulary; NULL when it is not pruned
+ *   v_draft  drafter vocabulary size (ignored when draft_vocab_inv is NULL)
+ *   greedy   0 (speculative sampling) or 1 (temperature 0)
  *   req_id   uint32 [batch], seed: as for sd_lm_head_probs
  *   accepted_len int32 [batch] out;  next_token int32 [batch] out
  *   accept_ratio fp32 [total_q] out or NULL: r_j at every tested position,
@@ -274,7 +304,8 @@ sd_status sd_verify(const float* target_logits, const int32_t* t_off,
                     const float* draft_logits, const float* draft_lse,
                     const int32_t* draft_tokens, const int32_t* q_off,
                     int32_t batch, int32_t total_q, int32_t total_target_rows,
-                    int32_t V, const uint32_t* req_id, uint64_t seed,
+                    int32_t V, const int32_t* draft_vocab_inv, int32_t v_draft,
+                    int32_t greedy, const uint32_t* req_id, uint64_t seed,
                     int32_t* accepted_len, int32_t* next_token,
                     float* accept_ratio, void* workspace,
                     size_t workspace_bytes, void* stream);

@@ -24,14 +24,18 @@ from .philox import STREAM_DRAFT, gumbel_uniforms
 
 
 def lm_head_logits(hidden: np.ndarray, w_vocab: np.ndarray,
-                   rows=None, v_chunk: int = 8192) -> np.ndarray:
-    """``z = hidden @ W^T`` in float64 from bf16 bit patterns.  The vocab is
-    processed in chunks only to bound memory; each entry is one dot product."""
+                   rows=None, v_chunk: int = 8192, vocab_map=None) -> np.ndarray:
+    """``z = hidden @ W^T`` in float64 from bf16 bit patterns.  With a pruned
+    drafter vocabulary (``vocab_map``: target id of each drafter entry) W is
+    those rows of the target's head, in map order ("H-Spec", App. B.2).  The
+    vocab is processed in chunks only to bound memory; each entry is one dot
+    product."""
     h = bf16_bits_to_f64(hidden if rows is None else hidden[rows])
-    V = w_vocab.shape[0]
+    ids = np.arange(w_vocab.shape[0]) if vocab_map is None else np.asarray(vocab_map, np.int64)
+    V = len(ids)
     z = np.empty((h.shape[0], V))
     for lo in range(0, V, v_chunk):
-        z[:, lo:lo + v_chunk] = h @ bf16_bits_to_f64(w_vocab[lo:lo + v_chunk]).T
+        z[:, lo:lo + v_chunk] = h @ bf16_bits_to_f64(w_vocab[ids[lo:lo + v_chunk]]).T
     return z
 
 
@@ -60,17 +64,34 @@ def gumbel_argmax(log_w: np.ndarray, u: np.ndarray):
     return idx, float(top2[1] - top2[0])
 
 
+def argmax_with_gap(x: np.ndarray):
+    """First index of the maximum, and the gap between the two largest
+    entries (inf for a single entry)."""
+    idx = int(np.argmax(x))
+    if len(x) < 2:
+        return idx, np.inf
+    top2 = np.partition(x, -2)[-2:]
+    return idx, float(top2[1] - top2[0])
+
+
 def draft_tokens(z: np.ndarray, row_req: np.ndarray, row_pos: np.ndarray,
-                 req_id: np.ndarray, seed: int):
-    """Gumbel-max sample of ``softmax(z_r)`` for each row ``r``.  ``row_req``
-    gives the request of each row and ``row_pos`` its 1-based position."""
+                 req_id: np.ndarray, seed: int, greedy: bool = False, vocab_map=None):
+    """Gumbel-max sample of ``softmax(z_r)`` for each row ``r`` (the argmax
+    of ``z_r`` at temperature 0, ``greedy``).  ``row_req`` gives the request
+    of each row and ``row_pos`` its 1-based position.  With a pruned
+    vocabulary the drawn entry is reported as its target id."""
     M, V = z.shape
     tok = np.empty(M, np.int32)
     gap = np.empty(M)
     for r in range(M):
-        u = gumbel_uniforms(seed, int(req_id[row_req[r]]), int(row_pos[r]),
-                            STREAM_DRAFT, V)
-        tok[r], gap[r] = gumbel_argmax(z[r], u)
+        if greedy:
+            tok[r], gap[r] = argmax_with_gap(z[r])
+        else:
+            u = gumbel_uniforms(seed, int(req_id[row_req[r]]), int(row_pos[r]),
+                                STREAM_DRAFT, V)
+            tok[r], gap[r] = gumbel_argmax(z[r], u)
+    if vocab_map is not None:
+        tok = np.asarray(vocab_map, np.int32)[tok]
     return tok, gap
 
 

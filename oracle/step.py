@@ -21,20 +21,22 @@ from . import attention, lm_head, verify
 NEAR_TIE = 1e-5
 
 
-def run_lm_head(hidden, w_vocab, q_off, req_id, seed, rows=None):
+def run_lm_head(hidden, w_vocab, q_off, req_id, seed, rows=None, greedy=False, vocab_map=None):
     """Logits, lse, draft tokens and Gumbel gaps for all rows (or ``rows``)."""
     req, pos = lm_head.row_owner(q_off)
-    z = lm_head.lm_head_logits(hidden, w_vocab, rows=rows)
+    z = lm_head.lm_head_logits(hidden, w_vocab, rows=rows, vocab_map=vocab_map)
     sel = np.arange(len(req)) if rows is None else np.asarray(rows)
     lse = lm_head.logsumexp_rows(z)
-    tok, gap = lm_head.draft_tokens(z, req[sel], pos[sel], req_id, seed)
+    tok, gap = lm_head.draft_tokens(z, req[sel], pos[sel], req_id, seed, greedy=greedy,
+                                    vocab_map=vocab_map)
     return dict(rows=sel, logits=z, lse=lse, tokens=tok, gap=gap)
 
 
 def run_verify(target_logits, t_off, draft_logits, draft_tokens, q_off,
-               req_id, seed, requests=None):
+               req_id, seed, requests=None, greedy=False, draft_vocab_inv=None):
     return verify.verify(target_logits, t_off, draft_logits, draft_tokens,
-                         q_off, req_id, seed, requests=requests)
+                         q_off, req_id, seed, requests=requests, greedy=greedy,
+                         draft_vocab_inv=draft_vocab_inv)
 
 
 def run_attention(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_len,

@@ -26,6 +26,16 @@ Readings where the pages are silent:
   from ``p_j``;
 * draws use Gumbel-max with Philox uniforms of stream 2 at position j (or
   b + 1 for the bonus token), see ``oracle.philox``.
+
+Variants:
+* pruned drafter vocabulary ("H-Spec", App. B.2): the drafter's softmax is
+  over a subset of the target vocabulary and q_j is zero outside it; the
+  rules above are unchanged, so verification stays lossless.
+* temperature 0 on both sides ("LongSpark", App. D.1; "H-Spec", sec. 4):
+  p_j and q_j are one-hot at their argmax (smallest index on ties), so r_j is
+  1 when y_j is the argmax of target row j and 0 otherwise, the residual
+  [p_j - q_j]_+ is the one-hot of that argmax and the bonus is the argmax of
+  row b + 1 -- the rules above applied to one-hot distributions.
 """
 from __future__ import annotations
 
@@ -33,7 +43,7 @@ from typing import Callable, List, Sequence, Tuple
 
 import numpy as np
 
-from .lm_head import gumbel_argmax, softmax_rows
+from .lm_head import argmax_with_gap, gumbel_argmax, softmax_rows
 from .philox import STREAM_SAMPLE, accept_uniform, gumbel_uniforms
 
 
@@ -77,8 +87,37 @@ def verify_request(p_rows: Sequence, q_rows: Sequence, y: Sequence,
     return n_verify, sample(p_rows[n_verify], n_verify + 1), tests
 
 
+def greedy_request(x_rows: Sequence, y: Sequence, n_verify: int):
+    """Temperature-0 verification of one request from its target logit rows
+    ``x_rows`` (b + 1 rows) and drafts ``y``.  Returns ``(accepted,
+    next_token, gaps)`` with the top-2 logit gap of every row consulted."""
+    gaps = []
+    for j in range(1, n_verify + 1):
+        a, g = argmax_with_gap(x_rows[j - 1])
+        gaps.append(g)
+        if int(y[j - 1]) != a:
+            return j - 1, a, gaps
+    a, g = argmax_with_gap(x_rows[n_verify])
+    gaps.append(g)
+    return n_verify, a, gaps
+
+
+def draft_rows_full_vocab(draft_logits, draft_vocab_inv, V: int):
+    """Draft distributions over the target vocabulary: softmax over the
+    drafter's entries, zero for target tokens outside its vocabulary."""
+    q_d = softmax_rows(np.asarray(draft_logits, np.float64))
+    if draft_vocab_inv is None:
+        return q_d
+    inv = np.asarray(draft_vocab_inv, np.int64)
+    q = np.zeros((q_d.shape[0], V))
+    inside = inv >= 0
+    q[:, inside] = q_d[:, inv[inside]]
+    return q
+
+
 def verify(target_logits: np.ndarray, t_off, draft_logits: np.ndarray,
-           draft_tokens, q_off, req_id, seed: int, requests=None):
+           draft_tokens, q_off, req_id, seed: int, requests=None, greedy: bool = False,
+           draft_vocab_inv=None):
     """Verification of every request (or of ``requests``).
 
     ``target_logits`` holds ``b_b + 1`` rows per request (rows ``t_off[b]``..),
@@ -98,12 +137,20 @@ def verify(target_logits: np.ndarray, t_off, draft_logits: np.ndarray,
         t0, t1 = int(t_off[b]), int(t_off[b + 1])
         nv = t1 - t0 - 1
         q0 = int(q_off[b])
+        y = np.asarray(draft_tokens[q0:q0 + nv])
+        if greedy:
+            a, c, gaps = greedy_request(target_logits[t0:t1].astype(np.float64), y, nv)
+            acc[b], nxt[b] = a, c
+            tests_all[b] = []
+            tested = gaps if a < nv else gaps[:-1]   # rows whose argmax decided a test
+            margin[b] = min(tested) if tested else np.inf
+            gap[b] = gaps[-1]
+            continue
         p_rows = softmax_rows(target_logits[t0:t1].astype(np.float64))
         if nv > 0:
-            q_rows = softmax_rows(draft_logits[q0:q0 + nv].astype(np.float64))
+            q_rows = draft_rows_full_vocab(draft_logits[q0:q0 + nv], draft_vocab_inv, V)
         else:
             q_rows = np.zeros((0, V))
-        y = np.asarray(draft_tokens[q0:q0 + nv])
         rid = int(req_id[b])
         last = {}
 

@@ -109,16 +109,19 @@ def test_summary_update_validation(lib, kw, status):
 
 def _lm(lib, **kw):
     a = dict(hidden=FAKE, w=FAKE, M=16, H=256, V=1024, q_off=FAKE, batch=1, req=FAKE, seed=1,
-             logits=FAKE, lse=FAKE, tok=FAKE, ws=FAKE, ws_bytes=1 << 40)
+             vmap=None, w_rows=0, greedy=0, logits=FAKE, lse=FAKE, tok=FAKE, ws=FAKE,
+             ws_bytes=1 << 40)
     a.update(kw)
     return lib.sd_lm_head_probs(a["hidden"], a["w"], a["M"], a["H"], a["V"], a["q_off"],
-                                a["batch"], a["req"], a["seed"], a["logits"], a["lse"],
-                                a["tok"], a["ws"], a["ws_bytes"], None)
+                                a["batch"], a["req"], a["seed"], a["vmap"], a["w_rows"],
+                                a["greedy"], a["logits"], a["lse"], a["tok"], a["ws"],
+                                a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(hidden=None), 1), (dict(req=None), 1), (dict(tok=None), 1),
     (dict(M=0), 2), (dict(H=100), 2), (dict(H=0), 2), (dict(V=0), 2), (dict(logits=ODD), 2),
+    (dict(greedy=2), 2), (dict(vmap=FAKE, w_rows=0), 2),
     (dict(ws=None), 3), (dict(ws_bytes=1), 3),
 ])
 def test_lm_head_validation(lib, kw, status):
@@ -127,17 +130,20 @@ def test_lm_head_validation(lib, kw, status):
 
 def _vf(lib, **kw):
     a = dict(target=FAKE, t_off=FAKE, draft=FAKE, lse=None, tok=FAKE, q_off=FAKE, batch=2,
-             total_q=8, R=10, V=1024, req=FAKE, seed=3, acc=FAKE, nxt=FAKE, ratio=None,
-             ws=FAKE, ws_bytes=1 << 40)
+             total_q=8, R=10, V=1024, vinv=None, v_draft=0, greedy=0, req=FAKE, seed=3,
+             acc=FAKE, nxt=FAKE, ratio=None, ws=FAKE, ws_bytes=1 << 40)
     a.update(kw)
     return lib.sd_verify(a["target"], a["t_off"], a["draft"], a["lse"], a["tok"], a["q_off"],
-                         a["batch"], a["total_q"], a["R"], a["V"], a["req"], a["seed"],
-                         a["acc"], a["nxt"], a["ratio"], a["ws"], a["ws_bytes"], None)
+                         a["batch"], a["total_q"], a["R"], a["V"], a["vinv"], a["v_draft"],
+                         a["greedy"], a["req"], a["seed"], a["acc"], a["nxt"], a["ratio"],
+                         a["ws"], a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(target=None), 1), (dict(acc=None), 1), (dict(draft=None), 1),
     (dict(batch=0), 2), (dict(R=0), 2), (dict(V=0), 2),
+    (dict(greedy=-1), 2), (dict(vinv=FAKE, v_draft=100), 1),        # pruned needs draft_lse
+    (dict(vinv=FAKE, v_draft=0, lse=FAKE), 2),
     (dict(ws=None), 3), (dict(ws_bytes=5), 3),
 ])
 def test_verify_validation(lib, kw, status):

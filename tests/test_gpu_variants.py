@@ -7,14 +7,18 @@
   few thousand rows here, compared with the oracle's fp64 definition within
   max-abs 1e-4 on Z (entries of size ~0.1..1) and 1e-4 relative on c;
 * the fixed-cost context of the 128K workload (window 256 + 16 summary
-  entries) at full size, on sampled requests.
+  entries) at full size, on sampled requests;
+* temperature-0 drafting and verification and the pruned drafter vocabulary:
+  probabilities within 1e-5, tokens and accepted lengths exact except
+  audited near-ties (as in the main parity suite), including the 128K
+  workload's LM head with 32,000 drafter tokens.
 """
 import numpy as np
 import pytest
 import torch
 
 import block_drafting_sd_amd as sd
-from oracle import attention as oa, compare, summary as osum
+from oracle import attention as oa, compare, step as ostep, summary as osum, verify as overify
 from synth import StepInputs, device as sdev
 from synth.configs import C1_32K, C2_128K
 
@@ -186,3 +190,116 @@ def test_fixed_cost_full_size_128k():
     rows = np.concatenate([np.arange(b.q_off[r], b.q_off[r + 1]) for r in reqs])
     ref = _oracle_attn(inp, requests=reqs, window=256, summary_keys=u, summary_values=zg)
     _check(bits(out), ref, rows=rows, tag="128K fixed-cost attention")
+
+
+# ------------------------------------------------- temperature 0, pruned vocab
+
+
+def _lm_cfg(**kw):
+    base = dict(name="lm_variants", batch=3, ctx=("list", (16, 16, 16)),
+                draft_k=("list", (16, 5, 16)), verify="full", num_heads_q=8, num_heads_kv=2,
+                head_dim=64, hidden=256, vocab=4100, seed=9090)
+    base.update(kw)
+    return C1_32K.with_(**base)
+
+
+def _gpu_lm(inp, **kw):
+    t = sdev.lm_head_tensors(inp, DEV)
+    z, lse, tok = sd.sd_lm_head_probs(t["hidden"], t["w_vocab"], t["q_off"], t["req_id"],
+                                      inp.philox_seed, **kw)
+    torch.cuda.synchronize()
+    return z, lse, tok
+
+
+@pytest.mark.parametrize("pruned", [False, True])
+@pytest.mark.parametrize("greedy", [False, True])
+def test_lm_head_greedy_and_pruned(greedy, pruned):
+    inp = StepInputs(_lm_cfg())
+    vmap = inp.pruned_vocab(1000) if pruned else None
+    z, lse, tok = _gpu_lm(inp, greedy=greedy,
+                          vocab_map=None if vmap is None else sdev.i32(vmap, DEV))
+    b = inp.budgets
+    ref = ostep.run_lm_head(inp.hidden, inp.w_vocab, b.q_off, inp.req_id, inp.philox_seed,
+                            greedy=greedy, vocab_map=vmap)
+    rep = compare.lm_head_report(z.cpu().numpy(), lse.cpu().numpy(), tok.cpu().numpy(), ref)
+    log(f"lm head greedy={greedy} pruned={pruned}: {rep}")
+    assert rep["ok"] and rep["logit_max_abs"] < 1e-5
+
+
+def _verify_inputs(inp, rng, vd=None):
+    """Seeded draft logits / tokens: a fraction of the tokens is the target
+    row's argmax so that temperature-0 tests accept some drafts."""
+    b = inp.budgets
+    V = inp.cfg.vocab
+    x = inp.target_logits
+    vmap = None if vd is None else inp.pruned_vocab(vd)
+    z = (rng.standard_normal((inp.total_q, V if vd is None else vd)) * 1.5).astype(np.float32)
+    tok = np.empty(inp.total_q, np.int32)
+    for r in range(inp.cfg.batch):
+        q0, t0 = int(b.q_off[r]), int(b.t_off[r])
+        for j in range(int(b.q_off[r + 1]) - q0):
+            row = x[t0 + min(j, int(b.t_off[r + 1]) - t0 - 1)]
+            if rng.random() < 0.8 and (vmap is None or np.argmax(row) in vmap):
+                tok[q0 + j] = int(np.argmax(row))
+            else:
+                tok[q0 + j] = int(rng.integers(0, V)) if vmap is None else int(rng.choice(vmap))
+    return z, tok, vmap
+
+
+@pytest.mark.parametrize("mode", ["greedy", "pruned", "greedy_pruned"])
+def test_verify_greedy_and_pruned(mode):
+    inp = StepInputs(_lm_cfg(batch=24, ctx=16, draft_k=(16, 7, 1), verify="uniform",
+                             vocab=20000, seed=3131))
+    b = inp.budgets
+    greedy = mode.startswith("greedy")
+    rng = np.random.default_rng(12)
+    z, tok, vmap = _verify_inputs(inp, rng, vd=5000 if "pruned" in mode else None)
+    inv = None
+    if vmap is not None:
+        inv = np.full(inp.cfg.vocab, -1, np.int32)
+        inv[vmap] = np.arange(len(vmap), dtype=np.int32)
+    zd = z.astype(np.float64)
+    lse = (zd.max(1) + np.log(np.exp(zd - zd.max(1, keepdims=True)).sum(1))).astype(np.float32)
+    t = sdev.verify_tensors(inp, DEV)
+    acc, nxt, _ = sd.sd_verify(t["target_logits"], t["t_off"], sdev.f32(z, DEV),
+                               sdev.f32(lse, DEV), sdev.i32(tok, DEV), t["q_off"], t["req_id"],
+                               inp.philox_seed, greedy=greedy,
+                               draft_vocab_inv=None if inv is None else sdev.i32(inv, DEV))
+    torch.cuda.synchronize()
+    ref = overify.verify(inp.target_logits, b.t_off, z, tok, b.q_off, inp.req_id,
+                         inp.philox_seed, greedy=greedy, draft_vocab_inv=inv)
+    rep = compare.verify_report(acc.cpu().numpy(), nxt.cpu().numpy(), ref, range(inp.cfg.batch))
+    log(f"verify {mode}: {rep}")
+    assert rep["ok"]
+    if greedy:
+        assert 0 < rep["mean_accepted"]
+
+
+def test_pruned_vocab_full_size_128k_shapes():
+    # the LM head of the 128K workload with the drafter restricted to 32,000
+    # target tokens, then verification against the full target vocabulary
+    cfg = C2_128K.with_(ctx=16)
+    inp = StepInputs(cfg)
+    b = inp.budgets
+    vmap = inp.pruned_vocab(32000)
+    inv = np.full(cfg.vocab, -1, np.int32)
+    inv[vmap] = np.arange(32000, dtype=np.int32)
+    z, lse, tok = _gpu_lm(inp, vocab_map=sdev.i32(vmap, DEV))
+    rows = np.array([0, 1, 17, 100, inp.total_q - 1])
+    ref = ostep.run_lm_head(inp.hidden, inp.w_vocab, b.q_off, inp.req_id, inp.philox_seed,
+                            rows=rows, vocab_map=vmap)
+    rep = compare.lm_head_report(z.cpu().numpy(), lse.cpu().numpy(), tok.cpu().numpy(), ref)
+    log(f"pruned LM head 256 x 4096 x 32000: {rep}")
+    assert rep["ok"]
+    assert np.all(np.isin(tok.cpu().numpy(), vmap))
+    t = sdev.verify_tensors(inp, DEV)
+    acc, nxt, _ = sd.sd_verify(t["target_logits"], t["t_off"], z, lse, tok, t["q_off"],
+                               t["req_id"], inp.philox_seed, draft_vocab_inv=sdev.i32(inv, DEV))
+    torch.cuda.synchronize()
+    reqs = [0, 7, cfg.batch - 1]
+    ref_v = overify.verify(inp.target_logits, b.t_off, z.cpu().numpy(), tok.cpu().numpy(),
+                           b.q_off, inp.req_id, inp.philox_seed, requests=reqs,
+                           draft_vocab_inv=inv)
+    rv = compare.verify_report(acc.cpu().numpy(), nxt.cpu().numpy(), ref_v, reqs)
+    log(f"pruned verify at 151936: {rv}")
+    assert rv["ok"]

@@ -1,4 +1,6 @@
-"""Pins for the oracle's attention variants and the context summary.
+"""Pins for the oracle's variants: attention (causal block, window, summary
+rows), the context summary, temperature-0 verification and the pruned
+drafter vocabulary.
 
 Attention variants are checked against PyTorch's scaled_dot_product_attention
 in float64 on the *logical* keys and values (regenerated from their seeds,
@@ -6,14 +8,19 @@ not read from the paged caches) with an explicit boolean mask, or with
 ``is_causal``; the summary against the same routine (its definition,
 "LongSpark" sec. 2.2 eq. (5)), against torch.logsumexp, against the union of
 two folded parts (App. A.2 eq. (11) must reproduce eq. (10) over the union)
-and against a closed form.
+and against a closed form.  Temperature-0 verification is checked against the
+general rules applied to one-hot distributions, greedy drafting against
+torch.argmax, and the pruned vocabulary against the full-vocabulary path with
+-inf logits outside the subset and against columns of the full head.
 """
 import numpy as np
 import pytest
 import torch
 
 from oracle import attention as oa
+from oracle import lm_head as olm
 from oracle import summary as osum
+from oracle import verify as ov
 from synth import StepInputs
 from synth.configs import C1_32K
 
@@ -192,3 +199,81 @@ def test_update_equals_summary_of_all_rows():
             z, c = osum.summary_of_rows(u[g], kl[:, g], vl[:, g], inp.softmax_scale)
             np.testing.assert_allclose(Z1[r, g], z, rtol=0, atol=1e-12)
             np.testing.assert_allclose(C1[r, g], c, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------- temperature 0, pruned vocab
+
+
+def _one_hot(i, V):
+    e = np.zeros(V)
+    e[i] = 1.0
+    return e
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_greedy_verify_is_the_rules_on_one_hot_distributions(seed):
+    rng = np.random.default_rng(seed)
+    V, K = 7, 5
+    for _ in range(40):
+        nv = int(rng.integers(0, K + 1))
+        x = rng.integers(-3, 4, (nv + 1, V)).astype(np.float64)   # ties happen
+        amax = [int(np.flatnonzero(r == r.max())[0]) for r in x]
+        y = [amax[j] if rng.random() < 0.6 else int(rng.integers(0, V)) for j in range(nv)]
+        a, c, _ = ov.greedy_request(x, y, nv)
+        # the general algorithm with p_j, q_j one-hot at their argmax
+        p_rows = [_one_hot(m, V) for m in amax]
+        q_rows = [_one_hot(t, V) for t in y]
+        a2, c2, _ = ov.verify_request(p_rows, q_rows, y, nv, lambda j: 0.5,
+                                      lambda w, j: int(np.flatnonzero(np.asarray(w) > 0)[0]))
+        assert (a, c) == (a2, c2)
+
+
+def test_greedy_draft_tokens_are_torch_argmax():
+    rng = np.random.default_rng(1)
+    z = rng.integers(-5, 6, (50, 33)).astype(np.float64)       # many ties
+    req = np.zeros(50, np.int64)
+    pos = np.arange(1, 51)
+    tok, _ = olm.draft_tokens(z, req, pos, np.array([3], np.uint32), 11, greedy=True)
+    np.testing.assert_array_equal(tok, torch.argmax(torch.from_numpy(z), dim=1).numpy())
+
+
+def test_pruned_draft_rows_embed_the_subset_softmax():
+    rng = np.random.default_rng(2)
+    V, Vd = 40, 9
+    vmap = np.sort(rng.choice(V, Vd, replace=False))
+    inv = np.full(V, -1)
+    inv[vmap] = np.arange(Vd)
+    z = rng.standard_normal((4, Vd))
+    q = ov.draft_rows_full_vocab(z, inv, V)
+    np.testing.assert_allclose(q.sum(1), 1.0, rtol=0, atol=1e-15)
+    outside = np.setdiff1d(np.arange(V), vmap)
+    assert np.all(q[:, outside] == 0)
+    np.testing.assert_allclose(q[:, vmap], torch.softmax(torch.from_numpy(z), 1).numpy(),
+                               rtol=0, atol=1e-15)
+
+
+def test_pruned_verify_equals_full_vocab_with_minus_inf_logits():
+    inp = StepInputs(_cfg(vocab=96, draft_k=("list", (3, 16, 5, 8))))
+    b = inp.budgets
+    vmap = inp.pruned_vocab(40)
+    inv = np.full(96, -1, np.int32)
+    inv[vmap] = np.arange(40)
+    rng = np.random.default_rng(3)
+    z = rng.standard_normal((inp.total_q, 40)) * 2
+    y = vmap[rng.integers(0, 40, inp.total_q)]
+    x = inp.target_logits
+    got = ov.verify(x, b.t_off, z, y, b.q_off, inp.req_id, inp.philox_seed, draft_vocab_inv=inv)
+    z_full = np.full((inp.total_q, 96), -np.inf)
+    z_full[:, vmap] = z
+    ref = ov.verify(x, b.t_off, z_full, y, b.q_off, inp.req_id, inp.philox_seed)
+    np.testing.assert_array_equal(got["accepted"], ref["accepted"])
+    np.testing.assert_array_equal(got["next_token"], ref["next_token"])
+
+
+def test_pruned_lm_head_logits_are_columns_of_the_full_head():
+    inp = StepInputs(_cfg(vocab=96))
+    vmap = inp.pruned_vocab(40)
+    z = olm.lm_head_logits(inp.hidden, inp.w_vocab, vocab_map=vmap)
+    h = torch.from_numpy(oa.bf16_bits_to_f64(inp.hidden))
+    w = torch.from_numpy(oa.bf16_bits_to_f64(inp.w_vocab))
+    np.testing.assert_allclose(z, (h @ w.T).numpy()[:, vmap], rtol=0, atol=1e-12)
