@@ -33,43 +33,71 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(inp, n_req: int = 1, target=None):
+PATHS = {
+    # the whole prefix, bidirectional block (the prefix-reading drafters)
+    "full": dict(),
+    # "LongSpark" fixed-cost context: recent window of 256 target KV rows and
+    # 16 summary entries per KV head (App. B.1), summary folded every step
+    "fixed": dict(window=256, n_summary=16),
+    # "H-Spec": causal block over a 2048-token window, drafter vocabulary
+    # pruned to 32,000 target tokens (sec. 3.3.2, App. B.2)
+    "hspec": dict(causal_block=True, window=2048, draft_vocab=32000),
+}
+
+
+def cpu_baseline(inp, n_req: int, target, opts, extra):
     """The oracle as it stands, on the first ``n_req`` requests of the workload
-    (attention over all KV heads, LM head rows, verification); scaled to
-    drafted+verified tokens/s."""
+    (attention over all KV heads, LM head rows, verification and, on the
+    fixed-cost path, the summary fold); scaled to drafted+verified tokens/s."""
     import numpy as np
-    from oracle import step as ostep, verify as overify
+    from oracle import step as ostep, summary as osum, verify as overify
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
     b = inp.budgets
+    c = inp.cfg
     reqs = list(range(n_req))
     rows = np.concatenate([np.arange(b.q_off[r], b.q_off[r + 1]) for r in reqs])
+    kw = dict(block_mask="causal" if opts.causal_block else "none", window=opts.window)
+    if opts.n_summary:   # summary of the prefix before the step (state, untimed)
+        Z, C = osum.summary_init(extra["u"], inp.k_cache,
+                                 inp.v_cache, inp.page_table[:n_req], extra["ctx_prev"][:n_req],
+                                 c.num_heads_kv, inp.softmax_scale)
+        Zf = np.zeros((c.batch,) + Z.shape[1:], np.float32)
+        Zf[:n_req] = Z
+        kw.update(summary_keys=extra["u"], summary_values=Zf)
     t0 = time.perf_counter()
-    ostep.run_attention(inp.q, inp.k_blk, inp.v_blk, inp.k_cache, inp.v_cache, inp.page_table,
-                        b.ctx_len, b.q_off, inp.cfg.num_heads_kv, inp.softmax_scale,
-                        requests=reqs)
+    from oracle import attention as oattn
+    oattn.draft_attn(inp.q, inp.k_blk, inp.v_blk, inp.k_cache, inp.v_cache, inp.page_table,
+                     b.ctx_len, b.q_off, c.num_heads_kv, inp.softmax_scale, requests=reqs, **kw)
     t1 = time.perf_counter()
     lm = ostep.run_lm_head(inp.hidden, inp.w_vocab, b.q_off, inp.req_id, inp.philox_seed,
-                           rows=rows)
+                           rows=rows, greedy=opts.greedy, vocab_map=extra.get("vmap"))
     t2 = time.perf_counter()
-    full_z = np.zeros((inp.total_q, inp.cfg.vocab), np.float64)
+    full_z = np.zeros((inp.total_q, lm["logits"].shape[1]), np.float64)
     full_z[rows] = lm["logits"]
     tok = np.zeros(inp.total_q, np.int32)
     tok[rows] = lm["tokens"]
     tgt = inp.target_logits if target is None else target
-    overify.verify(tgt, b.t_off, full_z, tok, b.q_off, inp.req_id,
-                   inp.philox_seed, requests=reqs)
+    res = overify.verify(tgt, b.t_off, full_z, tok, b.q_off, inp.req_id, inp.philox_seed,
+                         requests=reqs, greedy=opts.greedy, draft_vocab_inv=extra.get("vinv"))
     t3 = time.perf_counter()
+    if opts.n_summary:
+        osum.summary_update(extra["u"], inp.k_cache, inp.v_cache, inp.page_table[:n_req],
+                            extra["ctx_prev"][:n_req], res["accepted"][:n_req], Z, C,
+                            c.num_heads_kv, inp.softmax_scale)
+    t4 = time.perf_counter()
     tokens = int(sum(b.draft_k[r] for r in reqs))
-    return {"value": tokens / (t3 - t0), "unit": "tokens/s", "cores": int(threads),
+    return {"value": tokens / (t4 - t0), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": (f"{n_req} of {inp.cfg.batch} requests: attention over all "
-                       f"{inp.cfg.num_heads_kv} KV heads at N={int(b.ctx_len[0])}, LM head on "
-                       f"{len(rows)} rows x {inp.cfg.vocab}, verification; "
-                       f"attn {t1 - t0:.2f}s lm {t2 - t1:.2f}s verify {t3 - t2:.2f}s")}
+            "sample": (f"{n_req} of {c.batch} requests: attention over all "
+                       f"{c.num_heads_kv} KV heads at N={int(b.ctx_len[0])}, LM head on "
+                       f"{len(rows)} rows x {lm['logits'].shape[1]}, verification"
+                       + (", summary fold" if opts.n_summary else "") +
+                       f"; attn {t1 - t0:.2f}s lm {t2 - t1:.2f}s verify {t3 - t2:.2f}s"
+                       + (f" fold {t4 - t3:.2f}s" if opts.n_summary else ""))}
 
 
 def measured_traffic():
@@ -116,6 +144,11 @@ def main():
                     help="requests of the workload the CPU oracle is timed on")
     ap.add_argument("--calibrate-copy", type=float, default=0.0,
                     help="GiB: also run a plain device copy of this size (PMC calibration)")
+    ap.add_argument("--path", choices=sorted(PATHS), default="full",
+                    help="attention context: full prefix (default), LongSpark fixed-cost "
+                         "(window 256 + 16 summary entries), H-Spec (causal block, window "
+                         "2048, 32,000-token drafter vocabulary)")
+    ap.add_argument("--greedy", action="store_true", help="temperature 0 on both sides")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -129,7 +162,7 @@ def main():
     import torch
 
     import block_drafting_sd_amd as sd
-    from block_drafting_sd_amd.step import DraftVerifyStep, StepShape
+    from block_drafting_sd_amd.step import DraftVerifyStep, StepOptions, StepShape
     from synth import StepInputs, by_index, device as sdev
 
     sd.load()
@@ -147,8 +180,23 @@ def main():
                       num_heads_kv=cfg.num_heads_kv, head_dim=cfg.head_dim, hidden=cfg.hidden,
                       vocab=cfg.vocab, max_total_ctx=inp.max_total_ctx,
                       max_draft_k=int(b.draft_k.max()), split_tokens=args.split_tokens)
-    step = DraftVerifyStep(shape, dev)
+    opts = StepOptions(greedy=args.greedy, **PATHS[args.path])
+    step = DraftVerifyStep(shape, dev, opts)
     seed = inp.philox_seed
+    extra = {}
+    if opts.n_summary:
+        # the fold appends rows ctx_len_prev .. ctx_len_prev + a_b: the last
+        # K_max + 1 rows of each prefix stand in for the round's new rows
+        extra["u"] = inp.summary_queries(opts.n_summary)
+        extra["ctx_prev"] = np.maximum(b.ctx_len - (int(b.draft_k.max()) + 1), 0).astype(np.int32)
+        t["summary_keys"] = sdev.bf16(extra["u"], dev)
+        t["ctx_len_prev"] = sdev.i32(extra["ctx_prev"], dev)
+    if opts.draft_vocab:
+        extra["vmap"] = inp.pruned_vocab(opts.draft_vocab)
+        extra["vinv"] = np.full(cfg.vocab, -1, np.int32)
+        extra["vinv"][extra["vmap"]] = np.arange(opts.draft_vocab, dtype=np.int32)
+        t["vocab_map"] = sdev.i32(extra["vmap"], dev)
+        t["vocab_inv"] = sdev.i32(extra["vinv"], dev)
     if cfg.target[0] == "normal":
         t.update(sdev.verify_tensors(inp, dev))
     else:
@@ -163,12 +211,14 @@ def main():
     if args.calibrate_copy > 0:
         copy_calibration(args.calibrate_copy)
 
+    if opts.n_summary:
+        step.summary_init(t)       # state before the first step (untimed)
     for i in range(args.warmup):
         step.run(t, seed + i)
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -180,6 +230,9 @@ def main():
         e[2].record()
         step.verify(t, seed + 1000 + i)
         e[3].record()
+        if opts.n_summary:
+            step.summary_fold(t)
+        e[4].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     log(f"[bench] timed {args.steps} steps in {elapsed:.3f}s")
@@ -187,19 +240,26 @@ def main():
     attn_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     lm_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
     ver_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    fold_ms = np.array([e[3].elapsed_time(e[4]) for e in ev])
     tokens_per_step = int(b.draft_k.sum())
     ms_per_step = elapsed * 1e3 / args.steps
     value = tokens_per_step * args.steps / elapsed
     emitted = int(step.accepted.sum().item()) + cfg.batch
 
     c = cfg
-    kv_bytes = int(b.ctx_len.astype(np.int64).sum()) * c.num_heads_kv * c.head_dim * 2 * 2
+    n_read = b.ctx_len.astype(np.int64)
+    if opts.window:
+        n_read = np.minimum(n_read, opts.window)
+    kv_bytes = int(n_read.sum()) * c.num_heads_kv * c.head_dim * 2 * 2
     blk_bytes = inp.total_q * c.num_heads_kv * c.head_dim * 2 * 2
     q_out_bytes = 2 * inp.total_q * c.num_heads_q * c.head_dim * 2
-    attn_bytes = kv_bytes + blk_bytes + q_out_bytes
+    sum_bytes = (c.num_heads_kv * opts.n_summary * c.head_dim * (2 + 4 * c.batch)
+                 if opts.n_summary else 0)
+    attn_bytes = kv_bytes + blk_bytes + q_out_bytes + sum_bytes
     attn_avg_s = float(attn_ms.mean()) * 1e-3
     attn_gbs = attn_bytes / attn_avg_s / 1e9
-    lm_flops = 2.0 * inp.total_q * c.hidden * c.vocab
+    v_draft = opts.draft_vocab or c.vocab
+    lm_flops = 2.0 * inp.total_q * c.hidden * v_draft
     lm_tflops = lm_flops / (float(lm_ms.mean()) * 1e-3) / 1e12
 
     out = {
@@ -219,25 +279,43 @@ def main():
                    "draft_k": int(b.draft_k.max()), "num_heads_q": c.num_heads_q,
                    "num_heads_kv": c.num_heads_kv, "head_dim": c.head_dim,
                    "page_size": c.page_size, "hidden": c.hidden, "vocab": c.vocab,
-                   "split_tokens": args.split_tokens or "auto"},
+                   "split_tokens": args.split_tokens or "auto", "path": args.path,
+                   "greedy": bool(args.greedy), "window": opts.window,
+                   "summary_entries": opts.n_summary, "causal_block": opts.causal_block,
+                   "draft_vocab": v_draft},
         "roofline": {"kernel": "sd_draft_attn call: attn_worklist + attn_splitk + attn_combine",
                      "bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(), "algorithmic_bytes": attn_bytes,
+                     "traffic": measured_traffic() if args.path == "full" and args.config == 2
+                     else None,
+                     "algorithmic_bytes": attn_bytes,
                      "avg_ms": round(float(attn_ms.mean()), 4)},
         "breakdown_ms": {"attention": round(float(attn_ms.mean()), 4),
                          "lm_head": round(float(lm_ms.mean()), 4),
-                         "verify": round(float(ver_ms.mean()), 4)},
+                         "verify": round(float(ver_ms.mean()), 4),
+                         "summary_fold": round(float(fold_ms.mean()), 4)},
+        "breakdown_p10_p90_ms": {k: [round(float(np.percentile(v, 10)), 4),
+                                     round(float(np.percentile(v, 90)), 4)]
+                                 for k, v in (("attention", attn_ms), ("lm_head", lm_ms),
+                                              ("verify", ver_ms))},
         "lm_head": {"tflops": round(lm_tflops, 1),
                     "frac_mfma_bf16": round(lm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                    "w_hbm_gbs": round(c.vocab * c.hidden * 2 / (float(lm_ms.mean()) * 1e-3) / 1e9, 1)},
+                    "w_hbm_gbs": round(v_draft * c.hidden * 2 / (float(lm_ms.mean()) * 1e-3) / 1e9, 1)},
         "emitted_tokens_per_step_last": emitted,
+        # one drafter attention layer per step is timed; projections for the
+        # 3 attention modules of "H-Spec" and the 5 draft layers of "LongSpark"
+        "projection_tokens_per_s": {
+            f"{L}_layers": round(tokens_per_step / ((L * float(attn_ms.mean()) + float(lm_ms.mean())
+                                                      + float(ver_ms.mean())
+                                                      + float(fold_ms.mean())) * 1e-3), 1)
+            for L in (3, 5)},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(
             inp, args.cpu_requests,
-            None if cfg.target[0] == "normal" else t["target_logits"].cpu().numpy())
+            None if cfg.target[0] == "normal" else t["target_logits"].cpu().numpy(),
+            opts, extra)
     print(json.dumps(out), flush=True)
 
 

@@ -1,9 +1,15 @@
 """One draft-and-verify step with preallocated outputs and workspaces.
 
-Runs the three C-ABI calls back to back on one stream: draft-block attention,
-LM head + draft sampling, verification ("LongSpark", sec. 2.1 and App. A.1,
-Fig. 6).  The drafter layers between attention and the LM head need trained
-weights and are outside the step, so the LM head consumes given draft states.
+Runs the C-ABI calls back to back on one stream: draft-block attention, LM
+head + draft sampling, verification ("LongSpark", sec. 2.1 and App. A.1,
+Fig. 6) and, on the fixed-cost context path, the fold of the retained rows
+into the context summary ("LongSpark", sec. 2.2 and App. A.2).  The drafter
+layers between attention and the LM head need trained weights and are outside
+the step, so the LM head consumes given draft states.
+
+``StepOptions`` selects the variants the calls take as parameters: causal
+block mask, recent window, summary entries, pruned drafter vocabulary,
+temperature 0.
 """
 from __future__ import annotations
 
@@ -12,8 +18,9 @@ from typing import Dict, Optional
 
 import torch
 
-from . import (draft_attn_workspace_size, lm_head_workspace_size, sd_draft_attn,
-               sd_lm_head_probs, sd_verify, verify_workspace_size)
+from . import (SD_MASK_CAUSAL, SD_MASK_NONE, draft_attn_workspace_size,
+               lm_head_workspace_size, sd_draft_attn, sd_lm_head_probs, sd_summary_update,
+               sd_verify, verify_workspace_size)
 
 
 @dataclass
@@ -31,15 +38,32 @@ class StepShape:
     split_tokens: int = 0
 
 
+@dataclass
+class StepOptions:
+    causal_block: bool = False   # causal mask among the draft block's rows
+    window: int = 0              # 0: whole prefix; W: the last W prefix tokens
+    n_summary: int = 0           # context-summary entries per KV head (0: none)
+    draft_vocab: int = 0         # 0: full vocabulary; else the pruned drafter's size
+    greedy: bool = False         # temperature 0 on both sides
+
+
 class DraftVerifyStep:
-    def __init__(self, shape: StepShape, device):
+    """``t`` (the step's device inputs) holds the attention, LM-head and
+    verification tensors; with summary entries also ``summary_keys``
+    [Hkv, S, D] and ``ctx_len_prev`` (prefix lengths before the rows the fold
+    appends); with a pruned vocabulary ``vocab_map`` [V_d] and ``vocab_inv``
+    [V]."""
+
+    def __init__(self, shape: StepShape, device, options: Optional[StepOptions] = None):
         s = shape
-        self.shape = s
+        o = options or StepOptions()
+        self.shape, self.options = s, o
         dev = torch.device(device)
         self.device = dev
+        vd = o.draft_vocab or s.vocab
         self.attn_out = torch.empty(s.total_q, s.num_heads_q, s.head_dim, dtype=torch.bfloat16,
                                     device=dev)
-        self.logits = torch.empty(s.total_q, s.vocab, dtype=torch.float32, device=dev)
+        self.logits = torch.empty(s.total_q, vd, dtype=torch.float32, device=dev)
         self.lse = torch.empty(s.total_q, dtype=torch.float32, device=dev)
         self.tokens = torch.empty(s.total_q, dtype=torch.int32, device=dev)
         self.accepted = torch.empty(s.batch, dtype=torch.int32, device=dev)
@@ -49,33 +73,62 @@ class DraftVerifyStep:
         self.ws_attn = torch.empty(max(256, draft_attn_workspace_size(
             s.batch, s.num_heads_q, s.num_heads_kv, s.head_dim, s.max_total_ctx,
             s.split_tokens)), **u8)
-        self.ws_lm = torch.empty(max(256, lm_head_workspace_size(s.total_q, s.vocab)), **u8)
+        self.ws_lm = torch.empty(max(256, lm_head_workspace_size(s.total_q, vd)), **u8)
+        if o.n_summary:
+            self.summary_values = torch.zeros(s.batch, s.num_heads_kv, o.n_summary, s.head_dim,
+                                              dtype=torch.float32, device=dev)
+            self.summary_lse = torch.full((s.batch, s.num_heads_kv, o.n_summary), float("-inf"),
+                                          dtype=torch.float32, device=dev)
         self.ws_verify = torch.empty(max(256, verify_workspace_size(
             s.batch, s.total_q, s.total_target_rows, s.vocab)), **u8)
 
+    def summary_init(self, t: Dict[str, torch.Tensor], stream=None):
+        """Summary of every request's prefix before the step's new rows."""
+        return sd_summary_update(t["summary_keys"], t["k_cache"], t["v_cache"], t["page_table"],
+                                 t["ctx_len_prev"], None, self.summary_values, self.summary_lse,
+                                 stream=stream)
+
     def attention(self, t: Dict[str, torch.Tensor], stream=None):
-        s = self.shape
+        s, o = self.shape, self.options
+        summ = dict(summary_keys=t["summary_keys"], summary_values=self.summary_values) \
+            if o.n_summary else {}
         return sd_draft_attn(t["q"], t["k_blk"], t["v_blk"], t["k_cache"], t["v_cache"],
                              t["page_table"], t["ctx_len"], t["q_off"],
                              max_draft_k=s.max_draft_k, max_total_ctx=s.max_total_ctx,
-                             split_tokens=s.split_tokens, out=self.attn_out,
-                             workspace=self.ws_attn, stream=stream)
+                             split_tokens=s.split_tokens,
+                             block_mask=SD_MASK_CAUSAL if o.causal_block else SD_MASK_NONE,
+                             window=o.window, out=self.attn_out, workspace=self.ws_attn,
+                             stream=stream, **summ)
 
     def lm_head(self, t: Dict[str, torch.Tensor], seed: int, stream=None):
+        o = self.options
         return sd_lm_head_probs(t["hidden"], t["w_vocab"], t["q_off"], t["req_id"], seed,
-                                logits=self.logits, lse=self.lse, draft_tokens=self.tokens,
-                                workspace=self.ws_lm, stream=stream)
+                                vocab_map=t["vocab_map"] if o.draft_vocab else None,
+                                greedy=o.greedy, logits=self.logits, lse=self.lse,
+                                draft_tokens=self.tokens, workspace=self.ws_lm, stream=stream)
 
     def verify(self, t: Dict[str, torch.Tensor], seed: int, stream=None):
+        o = self.options
         return sd_verify(t["target_logits"], t["t_off"], self.logits, self.lse, self.tokens,
-                         t["q_off"], t["req_id"], seed, accepted_len=self.accepted,
+                         t["q_off"], t["req_id"], seed,
+                         draft_vocab_inv=t["vocab_inv"] if o.draft_vocab else None,
+                         greedy=o.greedy, accepted_len=self.accepted,
                          next_token=self.next_token, accept_ratio=self.ratio,
                          workspace=self.ws_verify, stream=stream)
+
+    def summary_fold(self, t: Dict[str, torch.Tensor], stream=None):
+        """Fold the committed token and the accepted drafts (rows
+        ctx_len_prev .. ctx_len_prev + accepted) into the summary."""
+        return sd_summary_update(t["summary_keys"], t["k_cache"], t["v_cache"], t["page_table"],
+                                 t["ctx_len_prev"], self.accepted, self.summary_values,
+                                 self.summary_lse, stream=stream)
 
     def run(self, t: Dict[str, torch.Tensor], seed: int, stream=None):
         self.attention(t, stream)
         self.lm_head(t, seed, stream)
         self.verify(t, seed, stream)
+        if self.options.n_summary:
+            self.summary_fold(t, stream)
         return dict(attn_out=self.attn_out, logits=self.logits, lse=self.lse,
                     tokens=self.tokens, accepted=self.accepted, next_token=self.next_token,
                     ratio=self.ratio)
