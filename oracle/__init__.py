@@ -9,9 +9,14 @@ their inputs from the seeded generators in ``synth``.
 
 Modules:
   philox     -- Philox-4x32-10 and the step's uniform draws
-  attention  -- draft-block attention over the paged target KV cache
+  attention  -- draft-block attention over the paged target KV cache (whole
+                prefix, or recent window + context summary; causal block)
+  summary    -- the fixed-cost drafter's global context summary and its fold
   lm_head    -- LM-head logits, softmax statistics, Gumbel-max draft sampling
-  verify     -- speculative-sampling verification
+  verify     -- speculative-sampling verification (and its temperature-0 and
+                pruned-vocabulary variants)
+  schedule   -- ForeSpark's pre-draft estimation, joint draft / verification
+                schedule and post-draft budget distribution
   step       -- the three parts run end to end with their near-tie audit
 
 Every function is pinned by ``tests/test_oracle_*.py`` against facts the
@@ -19,4 +24,4 @@ pages and the mathematics fix (the lossless theorem by exact enumeration,
 closed-form acceptance rates, decode-attention and SDPA special cases,
 bit-exact agreement of Philox with rocRAND's implementation, chi-square tests of the samplers).
 """
-from . import attention, lm_head, philox, step, verify  # noqa: F401
+from . import attention, lm_head, philox, schedule, step, summary, verify  # noqa: F401
