@@ -132,6 +132,72 @@ def copy_calibration(gib: float):
     log(f"copy calibration: {n * 4} bytes read and written per copy, 3 copies")
 
 
+def bench_schedule(args):
+    """ForeSpark's scheduler between verification and drafting: pre-draft
+    estimation + joint schedule, then post-draft estimation + budget
+    distribution, for 192 requests ("ForeSpark", sec. 4.2-4.4)."""
+    import numpy as np
+    import torch
+    import block_drafting_sd_amd as sd
+    from synth import device as sdev
+    from synth.schedule_inputs import ScheduleInputs
+
+    sd.load()
+    dev = torch.device("cuda:0")
+    si = ScheduleInputs()
+    p = si.predraft()
+    t = {k: (sdev.bf16(v, dev) if v.dtype == np.uint16 else sdev.f32(v, dev)) for k, v in p.items()}
+    caps, dl, vc, vl = si.latency_tables()
+    tab = [sdev.i32(caps, dev), sdev.f32(dl, dev), sdev.i32(vc, dev), sdev.f32(vl, dev)]
+    rows = si.n * si.K
+    pp = si.postdraft(rows)
+    tp = dict(hidden=sdev.bf16(pp["hidden"], dev), w_s=sdev.bf16(pp["w_s"], dev),
+              e_pred=sdev.bf16(pp["e_pred"], dev), w=sdev.f32(pp["w"], dev),
+              temperature=sdev.f32(pp["temperature"], dev), anchor=sdev.i32(pp["anchor"], dev),
+              tokens=sdev.i32(pp["tokens"], dev))
+    ws = torch.empty(sd.load().sd_schedule_workspace_size(si.n, si.r, rows, si.m),
+                     dtype=torch.uint8, device=dev)
+
+    def pre():
+        return sd.sd_schedule_draft(t["ctx_feat"], t["anchor_emb"], t["w_c"], t["w_e"], t["w_o"],
+                                    *tab, si.n, b_u=t["b_u"], b_o=t["b_o"],
+                                    cal_scale=t["cal_scale"], cal_bias=t["cal_bias"], K=si.K,
+                                    workspace=ws)
+
+    def post(o):
+        return sd.sd_schedule_verify(tp["hidden"], tp["w_s"], tp["e_pred"], tp["w"],
+                                     tp["anchor"], tp["tokens"], o["q_off"], o["verify_budget"],
+                                     bias=pp["bias"], temperature=tp["temperature"], K=si.K,
+                                     workspace=ws)
+
+    for _ in range(args.warmup):
+        post(pre())
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        o = pre()
+        ev[i][1].record()
+        post(o)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    pre_us = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
+    post_us = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
+    out = {"metric": "draft/verify scheduler latency per step (192 requests)",
+           "value": round(float((pre_us + post_us).mean()), 2), "unit": "us",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(elapsed * 1e3 / args.steps, 4), "higher_is_better": False,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16/f32",
+           "data": "synthetic (seeded estimator weights and inputs, profiled-like latency tables)",
+           "config": {"workload": "forespark_scheduler_n192_k16", "requests": si.n, "K": si.K,
+                      "d_h": si.d_h, "r": si.r, "selector_dims": si.m, "vocab": si.V},
+           "breakdown_us": {"pre_draft_schedule": round(float(pre_us.mean()), 2),
+                            "post_draft_budget": round(float(post_us.mean()), 2)}}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,6 +215,9 @@ def main():
                          "(window 256 + 16 summary entries), H-Spec (causal block, window "
                          "2048, 32,000-token drafter vocabulary)")
     ap.add_argument("--greedy", action="store_true", help="temperature 0 on both sides")
+    ap.add_argument("--schedule", action="store_true",
+                    help="time the draft / verification scheduler instead of the step "
+                         "(192 requests, K = 16, d_h = 4096, r = 256)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -160,6 +229,10 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.schedule:
+        bench_schedule(args)
+        return
 
     import block_drafting_sd_amd as sd
     from block_drafting_sd_amd.step import DraftVerifyStep, StepOptions, StepShape

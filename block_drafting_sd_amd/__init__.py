@@ -16,7 +16,8 @@ from ._lib import LIB_PATH, SdError, check, load  # noqa: F401
 
 SD_MASK_NONE, SD_MASK_CAUSAL = 0, 1
 
-__all__ = ["sd_draft_attn", "sd_summary_update", "sd_lm_head_probs", "sd_verify", "sd_version",
+__all__ = ["sd_draft_attn", "sd_summary_update", "sd_lm_head_probs", "sd_verify",
+           "sd_schedule_draft", "sd_schedule_verify", "sd_version",
            "SD_MASK_NONE", "SD_MASK_CAUSAL",
            "draft_attn_workspace_size", "lm_head_workspace_size",
            "verify_workspace_size", "SdError", "load"]
@@ -230,3 +231,87 @@ def sd_verify(target_logits, t_off, draft_logits, draft_lse, draft_tokens, q_off
                        _stream_handle(stream))
     check("sd_verify", st)
     return accepted_len, next_token, accept_ratio
+
+
+def _opt_f32(t, name, dev):
+    if t is not None:
+        _req(t, name, _F32, dev)
+    return t
+
+
+def sd_schedule_draft(ctx_feat, anchor_emb, w_c, w_e, w_o, draft_caps, draft_lat, verify_caps,
+                      verify_lat, n_nonspec: int, *, b_u=None, b_o=None, cal_scale=None,
+                      cal_bias=None, K: Optional[int] = None, workspace=None, stream=None):
+    """Pre-draft estimation and the joint draft / verification schedule; see
+    ``sd_schedule_draft`` in include/sd.h.  Returns a dict of device tensors:
+    logits, scores, draft_len, q_off, verify_budget, objective."""
+    lib = load()
+    dev = ctx_feat.device
+    for t, nm in ((ctx_feat, "ctx_feat"), (anchor_emb, "anchor_emb"), (w_c, "w_c"),
+                  (w_e, "w_e"), (w_o, "w_o")):
+        _req(t, nm, _BF16, dev)
+    _req(draft_caps, "draft_caps", _I32, dev)
+    _req(verify_caps, "verify_caps", _I32, dev)
+    _req(draft_lat, "draft_lat", _F32, dev)
+    _req(verify_lat, "verify_lat", _F32, dev)
+    for t, nm in ((b_u, "b_u"), (b_o, "b_o"), (cal_scale, "cal_scale"), (cal_bias, "cal_bias")):
+        _opt_f32(t, nm, dev)
+    n, d_h = ctx_feat.shape
+    r = w_c.shape[0]
+    T = w_o.shape[0]
+    if K is None:
+        K = int((math.isqrt(8 * T + 1) - 1) // 2)
+    if K * (K + 1) // 2 != T:
+        raise ValueError(f"w_o has {T} rows, not K(K+1)/2 for K={K}")
+    f32 = dict(dtype=torch.float32, device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    out = dict(logits=torch.empty(n, T, **f32), scores=torch.empty(n, K, **f32),
+               draft_len=torch.empty(n, **i32), q_off=torch.empty(n + 1, **i32),
+               verify_budget=torch.empty(1, **i32), objective=torch.empty(1, **f32))
+    workspace = _workspace(workspace, lib.sd_schedule_workspace_size(n, r, 0, 1), dev)
+    st = lib.sd_schedule_draft(_ptr(ctx_feat), _ptr(anchor_emb), _ptr(w_c), _ptr(w_e), _ptr(b_u),
+                               _ptr(w_o), _ptr(b_o), _ptr(cal_scale), _ptr(cal_bias), n, d_h, r, K,
+                               _ptr(draft_caps), _ptr(draft_lat), draft_caps.numel(),
+                               _ptr(verify_caps), _ptr(verify_lat), verify_caps.numel(),
+                               int(n_nonspec), _ptr(out["logits"]), _ptr(out["scores"]),
+                               _ptr(out["draft_len"]), _ptr(out["q_off"]),
+                               _ptr(out["verify_budget"]), _ptr(out["objective"]),
+                               _ptr(workspace), workspace.numel(), _stream_handle(stream))
+    check("sd_schedule_draft", st)
+    return out
+
+
+def sd_schedule_verify(hidden, w_s, e_pred, w, anchor_tokens, draft_tokens, q_off,
+                       verify_budget, *, bias: float = 0.0, temperature=None,
+                       K: Optional[int] = None, workspace=None, stream=None):
+    """Post-draft estimation and budget distribution; see
+    ``sd_schedule_verify`` in include/sd.h.  ``hidden`` holds max_rows packed
+    draft rows.  Returns a dict: accept_prob, survival, verify_len, t_off."""
+    lib = load()
+    dev = hidden.device
+    for t, nm in ((hidden, "hidden"), (w_s, "w_s"), (e_pred, "e_pred")):
+        _req(t, nm, _BF16, dev)
+    _req(w, "w", _F32, dev)
+    _opt_f32(temperature, "temperature", dev)
+    for t, nm in ((anchor_tokens, "anchor_tokens"), (draft_tokens, "draft_tokens"),
+                  (q_off, "q_off"), (verify_budget, "verify_budget")):
+        _req(t, nm, _I32, dev)
+    max_rows, H = hidden.shape
+    m = w_s.shape[0]
+    V = e_pred.shape[0]
+    n = q_off.numel() - 1
+    if K is None:
+        K = temperature.numel() if temperature is not None else 32
+    f32 = dict(dtype=torch.float32, device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    out = dict(accept_prob=torch.empty(max_rows, **f32), survival=torch.empty(max_rows, **f32),
+               verify_len=torch.empty(n, **i32), t_off=torch.empty(n + 1, **i32))
+    workspace = _workspace(workspace, lib.sd_schedule_workspace_size(1, 1, max_rows, m), dev)
+    st = lib.sd_schedule_verify(_ptr(hidden), _ptr(w_s), _ptr(e_pred), _ptr(w), float(bias),
+                                _ptr(temperature), _ptr(anchor_tokens), _ptr(draft_tokens),
+                                _ptr(q_off), _ptr(verify_budget), n, max_rows, H, m, V, K,
+                                _ptr(out["accept_prob"]), _ptr(out["survival"]),
+                                _ptr(out["verify_len"]), _ptr(out["t_off"]), _ptr(workspace),
+                                workspace.numel(), _stream_handle(stream))
+    check("sd_schedule_verify", st)
+    return out

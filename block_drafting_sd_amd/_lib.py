@@ -28,6 +28,13 @@ SIGNATURES = {
                              _vp, _vp, _sz, _vp]),
     "sd_summary_update": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                  _i32, _i32, _i32, _f32, _vp, _vp, _vp]),
+    "sd_schedule_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
+    "sd_schedule_draft": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "sd_schedule_verify": (_i32, [_vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp,
+                                  _i32, _i32, _i32, _i32, _i32, _i32,
+                                  _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sd_lm_head_workspace_size": (_sz, [_i32, _i32]),
     "sd_lm_head_probs": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _u64,
                                 _vp, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),

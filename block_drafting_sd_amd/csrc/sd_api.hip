@@ -201,6 +201,127 @@ sd_status sd_summary_update(const void* summary_queries, const void* k_cache, co
   return from_hip(sd::launch_summary(a, head_dim, static_cast<hipStream_t>(stream)));
 }
 
+size_t sd_schedule_workspace_size(int32_t n, int32_t r, int32_t max_rows, int32_t m) {
+  if (n < 1 || r < 1 || max_rows < 0 || m < 1) return 0;
+  return align_up(static_cast<size_t>(n) * r * sizeof(float)) +
+         align_up(static_cast<size_t>(n) * (sd::kSchedMaxK + 1) * sizeof(float)) +
+         align_up(static_cast<size_t>(max_rows) * m * sizeof(float));
+}
+
+sd_status sd_schedule_draft(const void* ctx_feat, const void* anchor_emb, const void* w_c,
+                            const void* w_e, const float* b_u, const void* w_o, const float* b_o,
+                            const float* cal_scale, const float* cal_bias, int32_t n, int32_t d_h,
+                            int32_t r, int32_t K, const int32_t* draft_caps, const float* draft_lat,
+                            int32_t n_draft_buckets, const int32_t* verify_caps,
+                            const float* verify_lat, int32_t n_verify_buckets, int32_t n_nonspec,
+                            float* logits, float* scores, int32_t* draft_len, int32_t* q_off,
+                            int32_t* verify_budget, float* objective, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!ctx_feat || !anchor_emb || !w_c || !w_e || !w_o || !draft_caps || !draft_lat ||
+      !verify_caps || !verify_lat || !logits || !scores || !draft_len || !verify_budget)
+    return SD_ERR_NULL;
+  if (n < 1 || n > sd::kSchedMaxRequests || K < 1 || K > sd::kSchedMaxK ||
+      n * K > sd::kSchedMaxEntries || d_h < 16 || d_h % 16 != 0 || r < 16 || r % 16 != 0 ||
+      d_h > 65536 || r > 65536 || n_draft_buckets < 1 || n_verify_buckets < 1 ||
+      n_draft_buckets > 4096 || n_verify_buckets > 4096 || n_nonspec < 0)
+    return SD_ERR_SHAPE;
+  if (!aligned16(ctx_feat) || !aligned16(anchor_emb) || !aligned16(w_c) || !aligned16(w_e))
+    return SD_ERR_SHAPE;
+  const size_t need = sd_schedule_workspace_size(n, r, 0, 1);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SD_ERR_WORKSPACE;
+  float* u = static_cast<float*>(workspace);
+  sd::SchedGemmArgs g;
+  g.a1 = static_cast<const uint16_t*>(ctx_feat);
+  g.b1 = static_cast<const uint16_t*>(w_c);
+  g.a2 = static_cast<const uint16_t*>(anchor_emb);
+  g.b2 = static_cast<const uint16_t*>(w_e);
+  g.bias = b_u;
+  g.c = u;
+  g.M = n;
+  g.N = r;
+  g.K = d_h;
+  g.silu = 1;
+  sd::SchedArgs a;
+  a.u = u;
+  a.w_o = static_cast<const uint16_t*>(w_o);
+  a.b_o = b_o;
+  a.cal_scale = cal_scale;
+  a.cal_bias = cal_bias;
+  a.d_caps = draft_caps;
+  a.d_lat = draft_lat;
+  a.v_caps = verify_caps;
+  a.v_lat = verify_lat;
+  a.logits = logits;
+  a.rewards = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       align_up(static_cast<size_t>(n) * r * sizeof(float)));
+  a.scores = scores;
+  a.draft_len = draft_len;
+  a.q_off = q_off;
+  a.budget = verify_budget;
+  a.objective = objective;
+  a.n = n;
+  a.r = r;
+  a.K = K;
+  a.n_dbuckets = n_draft_buckets;
+  a.n_vbuckets = n_verify_buckets;
+  a.n_nonspec = n_nonspec;
+  return from_hip(sd::launch_schedule_draft(g, a, static_cast<hipStream_t>(stream)));
+}
+
+sd_status sd_schedule_verify(const void* hidden, const void* w_s, const void* e_pred,
+                             const float* w, float bias, const float* temperature,
+                             const int32_t* anchor_tokens, const int32_t* draft_tokens,
+                             const int32_t* q_off, const int32_t* verify_budget, int32_t n,
+                             int32_t max_rows, int32_t H, int32_t m, int32_t V, int32_t K,
+                             float* accept_prob, float* survival, int32_t* verify_len,
+                             int32_t* t_off, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (!hidden || !w_s || !e_pred || !w || !anchor_tokens || !draft_tokens || !q_off ||
+      !verify_budget || !accept_prob || !survival || !verify_len)
+    return SD_ERR_NULL;
+  if (n < 1 || n > sd::kSchedMaxRequests || max_rows < 1 || max_rows > sd::kSchedMaxEntries ||
+      H < 16 || H % 16 != 0 || H > 65536 || m < 16 || m % 16 != 0 || m > 65536 || V < 1 ||
+      K < 1 || K > sd::kSchedMaxK || !isfinite(bias))
+    return SD_ERR_SHAPE;
+  if (!aligned16(hidden) || !aligned16(w_s)) return SD_ERR_SHAPE;
+  const size_t need = sd_schedule_workspace_size(1, 1, max_rows, m);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SD_ERR_WORKSPACE;
+  float* sh = static_cast<float*>(workspace);
+  sd::SchedGemmArgs g;
+  g.a1 = static_cast<const uint16_t*>(hidden);
+  g.b1 = static_cast<const uint16_t*>(w_s);
+  g.a2 = nullptr;
+  g.b2 = nullptr;
+  g.bias = nullptr;
+  g.c = sh;
+  g.M = max_rows;
+  g.N = m;
+  g.K = H;
+  g.silu = 0;
+  sd::SchedPostArgs a;
+  a.hidden = static_cast<const uint16_t*>(hidden);
+  a.sh = sh;
+  a.e_pred = static_cast<const uint16_t*>(e_pred);
+  a.w = w;
+  a.temperature = temperature;
+  a.anchor = anchor_tokens;
+  a.tokens = draft_tokens;
+  a.q_off = q_off;
+  a.budget = verify_budget;
+  a.prob = accept_prob;
+  a.survival = survival;
+  a.verify_len = verify_len;
+  a.t_off = t_off;
+  a.bias = bias;
+  a.n = n;
+  a.M = max_rows;
+  a.H = H;
+  a.ms = m;
+  a.V = V;
+  a.K = K;
+  return from_hip(sd::launch_schedule_verify(g, a, static_cast<hipStream_t>(stream)));
+}
+
 size_t sd_lm_head_workspace_size(int32_t M, int32_t V) {
   if (M < 1 || V < 1) return 0;
   return lm_layout(M, V).total;

@@ -71,6 +71,63 @@ constexpr int kSummaryMax = 64;   // summary entries per KV head
 
 hipError_t launch_summary(const SummaryArgs& a, int head_dim, hipStream_t s);
 
+// ------------------------------------------------------------- scheduling
+struct SchedGemmArgs {        // c = a1 b1^T (+ a2 b2^T) (+ bias, SiLU)
+  const uint16_t* a1;         // [M][K]
+  const uint16_t* b1;         // [N][K]
+  const uint16_t* a2;         // [M][K] or null
+  const uint16_t* b2;         // [N][K]
+  const float* bias;          // [N] or null
+  float* c;                   // [M][N]
+  int32_t M, N, K, silu;
+};
+
+struct SchedArgs {
+  const float* u;             // [n][r] estimator hidden layer
+  const uint16_t* w_o;        // [T][r]
+  const float* b_o;           // [T] or null
+  const float* cal_scale;     // [T] or null
+  const float* cal_bias;      // [T] or null
+  const int32_t* d_caps;      // [n_dbuckets] drafter token capacities (increasing)
+  const float* d_lat;         // [n_dbuckets]
+  const int32_t* v_caps;      // [n_vbuckets] verifier token capacities (increasing)
+  const float* v_lat;         // [n_vbuckets]
+  float* logits;              // [n][T]
+  float* rewards;             // [n][K + 1] reward curves (workspace)
+  float* scores;              // [n][K]
+  int32_t* draft_len;         // [n]
+  int32_t* q_off;             // [n + 1] or null
+  int32_t* budget;            // [1]
+  float* objective;           // [1] or null
+  int32_t n, r, K, n_dbuckets, n_vbuckets, n_nonspec;
+};
+
+struct SchedPostArgs {
+  const uint16_t* hidden;     // [M][H]
+  const float* sh;            // [M][ms] = hidden W_s^T
+  const uint16_t* e_pred;     // [V][ms]
+  const float* w;             // [H + ms]
+  const float* temperature;   // [K] or null
+  const int32_t* anchor;      // [n]
+  const int32_t* tokens;      // [M]
+  const int32_t* q_off;       // [n + 1]
+  const int32_t* budget;      // [1]
+  float* prob;                // [M]
+  float* survival;            // [M]
+  int32_t* verify_len;        // [n]
+  int32_t* t_off;             // [n + 1] or null
+  float bias;
+  int32_t n, M, H, ms, V, K;
+};
+
+constexpr int kSchedMaxEntries = 4096;   // n K (and draft rows) sorted in one workgroup
+constexpr int kSchedMaxRequests = 1024;
+constexpr int kSchedMaxK = 32;
+
+hipError_t launch_sched_gemm(const SchedGemmArgs& g, hipStream_t s);
+hipError_t launch_schedule_draft(const SchedGemmArgs& g, const SchedArgs& a, hipStream_t s);
+hipError_t launch_schedule_verify(const SchedGemmArgs& g, const SchedPostArgs& a, hipStream_t s);
+
 // ------------------------------------------------------------------ LM head
 struct LmArgs {
   const uint16_t* hidden;   // [M, H]

@@ -6,6 +6,8 @@
  *   sd_draft_attn     draft-block attention over the target's paged KV cache
  *                     (whole prefix, or recent window + context summary)
  *   sd_summary_update fold newly retained target KV rows into the summary
+ *   sd_schedule_draft  pre-draft estimation, joint draft / verify schedule
+ *   sd_schedule_verify post-draft estimation, verification budget split
  *   sd_lm_head_probs  drafter LM head, softmax statistics, draft sampling
  *   sd_verify         lossless speculative-sampling verification
  *
@@ -196,6 +198,109 @@ sd_status sd_summary_update(const void* summary_queries, const void* k_cache,
                             int32_t head_dim, int32_t n_summary,
                             float softmax_scale, float* summary_values,
                             float* summary_lse, void* stream);
+
+/* ------------------------------------------------------------------------
+ * sd_schedule_draft -- pre-draft estimation and the joint draft /
+ * verification schedule.
+ *
+ * Defined by: "ForeSpark", sec. 4.2, eqs. (2)-(3) (the pre-draft survival
+ * estimator reads the context feature c_i and the anchor embedding e_i:
+ * u_i = SiLU(W_c c_i + W_e e_i), z_i = W_o u_i holds K(K+1)/2
+ * conditional-acceptance logits, row d = a length-d draft; survival benefits
+ * S_{i,d,j} = prod_{t<=j} sigmoid(z^(d)_{i,t}); Reward_i(d, b) =
+ * sum_{j<=b} S_{i,d,j}, e.g. benefits 0.9, 0.7, 0.3 give Reward(3, 3) = 1.9,
+ * Fig. 5) and sec. 4.3 (R_i(d) = Reward_i(d, d), R_i(0) = 0; F_i its upper
+ * concave envelope on {0..K}; survival scores g_{i,d} = F_i(d) - F_i(d-1);
+ * all scores pooled and sorted; eq. (4): (D, B) = argmax
+ * (n + sum_{r<=B} g_(r)) / (T_draft(D) + T_verify(N + B)) over B <= sum d_i,
+ * with latencies constant within token-count buckets, searched with one
+ * candidate -- the largest feasible schedule -- per pair of buckets).  The
+ * per-entry calibration of sec. 4.5 (a scale and a bias per logit) and the
+ * biases the page omits are optional.
+ *
+ * Conventions: entry (d, t) of a triangle is at index d(d-1)/2 + t - 1.  The
+ * drafter processes n + sum_i d_i tokens (anchor plus masks), the verifier
+ * N + B; a token count takes the latency of the first bucket whose capacity
+ * holds it; counts above the last bucket are infeasible.  Within a bucket
+ * pair B is the largest feasible count of positive scores.  Equal scores are
+ * ordered by (request, d) and ties of eq. (4) go to the first pair in
+ * (draft bucket, verify bucket) order.  Everything runs on the device (no
+ * host synchronisation): the outputs feed sd_draft_attn (q_off) and
+ * sd_schedule_verify (verify_budget) directly.  Arithmetic is fp32.
+ *
+ * Arguments
+ *   ctx_feat, anchor_emb  bf16 [n, d_h]  c_i and e_i
+ *   w_c, w_e   bf16 [r, d_h];  b_u fp32 [r] or NULL
+ *   w_o        bf16 [K(K+1)/2, r];  b_o fp32 [K(K+1)/2] or NULL
+ *   cal_scale, cal_bias  fp32 [K(K+1)/2] or NULL (z = scale * z + bias)
+ *   n (1..1024), d_h and r (multiples of 16), K (1..32), n * K <= 4096
+ *   draft_caps int32 [n_draft_buckets] increasing token capacities,
+ *   draft_lat  fp32  [n_draft_buckets] latencies (any unit, same as verify)
+ *   verify_caps, verify_lat, n_verify_buckets: the verifier's table
+ *   n_nonspec  N, the verification batch's non-speculative tokens
+ *   logits     fp32 [n, K(K+1)/2] out (calibrated z)
+ *   scores     fp32 [n, K] out (g_{i,d}, non-increasing in d)
+ *   draft_len  int32 [n] out (d_i);  q_off int32 [n+1] out or NULL
+ *   verify_budget int32 [1] out (B);  objective fp32 [1] out or NULL
+ *   workspace  sd_schedule_workspace_size(n, r, max_rows, m) bytes (one
+ *              workspace serves both scheduling calls)
+ * ------------------------------------------------------------------------ */
+size_t sd_schedule_workspace_size(int32_t n, int32_t r, int32_t max_rows,
+                                  int32_t m);
+
+sd_status sd_schedule_draft(const void* ctx_feat, const void* anchor_emb,
+                            const void* w_c, const void* w_e, const float* b_u,
+                            const void* w_o, const float* b_o,
+                            const float* cal_scale, const float* cal_bias,
+                            int32_t n, int32_t d_h, int32_t r, int32_t K,
+                            const int32_t* draft_caps, const float* draft_lat,
+                            int32_t n_draft_buckets, const int32_t* verify_caps,
+                            const float* verify_lat, int32_t n_verify_buckets,
+                            int32_t n_nonspec, float* logits, float* scores,
+                            int32_t* draft_len, int32_t* q_off,
+                            int32_t* verify_budget, float* objective,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* ------------------------------------------------------------------------
+ * sd_schedule_verify -- post-draft estimation and budget distribution.
+ *
+ * Defined by: "ForeSpark", sec. 4.4, eq. (5) (p_{i,j} = sigmoid(w . [h_{i,j};
+ * s_{i,j}]) with selector feature s_{i,j} = (W_s h_{i,j}) * E_pred(x_{i,j-1}),
+ * x_{i,0} the anchor token; S^_{i,j} = prod_{t<=j} p_{i,t}; the B positions
+ * with the highest S^ across the batch are verified, a prefix of every
+ * draft) and sec. 4.5 (a temperature per position calibrates p).  With the
+ * bias c: p = sigmoid((w . [h; s] + c) / theta_j).  Equal S^ are ordered by
+ * (request, position).  B is read on the device (from sd_schedule_draft) and
+ * capped at the drafted rows.  Arithmetic is fp32 (W_s h on MFMA, bf16
+ * products).
+ *
+ * Arguments
+ *   hidden   bf16 [max_rows, H]  h_{i,j}, rows packed by q_off (the LM head's
+ *            input rows); rows past q_off[n] are read but unused
+ *   w_s      bf16 [m, H];  e_pred bf16 [V, m];  w fp32 [H + m];  bias c
+ *   temperature fp32 [K] or NULL (theta_j of position j)
+ *   anchor_tokens int32 [n];  draft_tokens int32 [max_rows] (packed)
+ *   q_off    int32 [n+1] device (e.g. from sd_schedule_draft)
+ *   verify_budget int32 [1] device
+ *   n (1..1024), max_rows (1..4096) host bound on q_off[n], H and m
+ *   multiples of 16, V >= 1, K (1..32)
+ *   accept_prob, survival fp32 [max_rows] out (p and S^ of every drafted row;
+ *            rows from q_off[n] on are not written)
+ *   verify_len int32 [n] out (b_i);  t_off int32 [n+1] out or NULL
+ *            (t_off[i+1] - t_off[i] = b_i + 1 target rows, as sd_verify takes)
+ * ------------------------------------------------------------------------ */
+sd_status sd_schedule_verify(const void* hidden, const void* w_s,
+                             const void* e_pred, const float* w, float bias,
+                             const float* temperature,
+                             const int32_t* anchor_tokens,
+                             const int32_t* draft_tokens, const int32_t* q_off,
+                             const int32_t* verify_budget, int32_t n,
+                             int32_t max_rows, int32_t H, int32_t m, int32_t V,
+                             int32_t K, float* accept_prob, float* survival,
+                             int32_t* verify_len, int32_t* t_off,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* ------------------------------------------------------------------------
  * sd_lm_head_probs -- drafter LM head, softmax statistics, draft sampling.

@@ -137,25 +137,34 @@ def sorted_scores(g):
     return np.array([-k[0] for k in keys]), np.array([k[1] for k in keys], np.int64)
 
 
+def pair_candidates(g, n_nonspec: int, d_caps, d_lat, v_caps, v_lat):
+    """The candidate of every (draft bucket, verify bucket) pair, in that
+    order: a list of (objective, k, B), objective -inf if infeasible."""
+    n, K = g.shape
+    vals, _ = sorted_scores(g)
+    prefix = np.concatenate([[0.0], np.cumsum(vals)])
+    n_pos = int((vals > 0).sum())
+    out = []
+    for dc, dl in zip(d_caps, d_lat):
+        k = min(int(dc) - n, n * K)
+        for vc, vl in zip(v_caps, v_lat):
+            B = min(int(vc) - n_nonspec, k, n_pos)
+            if k < 0 or B < 0:
+                out.append((-np.inf, 0, 0))
+            else:
+                out.append(((n + prefix[B]) / (float(dl) + float(vl)), k, B))
+    return out
+
+
 def joint_schedule(g, n_nonspec: int, d_caps, d_lat, v_caps, v_lat):
     """Eq. (4) by the bucket-pair search.  Returns dict(draft_len [n],
     budget B, objective, k = sum d_i)."""
     n, K = g.shape
     vals, owner = sorted_scores(g)
-    prefix = np.concatenate([[0.0], np.cumsum(vals)])
-    n_pos = int((vals > 0).sum())
     best = (-np.inf, 0, 0)
-    for a, (dc, dl) in enumerate(zip(d_caps, d_lat)):
-        k = min(int(dc) - n, n * K)
-        if k < 0:
-            continue
-        for v, (vc, vl) in enumerate(zip(v_caps, v_lat)):
-            B = min(int(vc) - n_nonspec, k, n_pos)
-            if B < 0:
-                continue
-            obj = (n + prefix[B]) / (float(dl) + float(vl))
-            if obj > best[0]:
-                best = (obj, k, B)
+    for cand in pair_candidates(g, n_nonspec, d_caps, d_lat, v_caps, v_lat):
+        if cand[0] > best[0]:
+            best = cand
     obj, k, B = best
     d = np.zeros(n, np.int32)
     for r in range(k):

@@ -156,3 +156,48 @@ def test_python_binding_rejects_cpu_dtype_mismatch():
     with pytest.raises(TypeError):
         sd.sd_lm_head_probs(x, x, torch.zeros(2, dtype=torch.int32),
                             torch.zeros(1, dtype=torch.int32), 0)
+
+
+def _sch(lib, **kw):
+    a = dict(c=FAKE, e=FAKE, wc=FAKE, we=FAKE, bu=None, wo=FAKE, bo=None, cs=None, cb=None,
+             n=4, dh=64, r=32, K=6, dcap=FAKE, dlat=FAKE, ndb=3, vcap=FAKE, vlat=FAKE, nvb=2,
+             N=4, logits=FAKE, scores=FAKE, dlen=FAKE, qoff=None, budget=FAKE, obj=None, ws=FAKE,
+             ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.sd_schedule_draft(a["c"], a["e"], a["wc"], a["we"], a["bu"], a["wo"], a["bo"],
+                                 a["cs"], a["cb"], a["n"], a["dh"], a["r"], a["K"], a["dcap"],
+                                 a["dlat"], a["ndb"], a["vcap"], a["vlat"], a["nvb"], a["N"],
+                                 a["logits"], a["scores"], a["dlen"], a["qoff"], a["budget"],
+                                 a["obj"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(c=None), 1), (dict(wo=None), 1), (dict(dcap=None), 1), (dict(budget=None), 1),
+    (dict(n=0), 2), (dict(n=1025), 2), (dict(K=0), 2), (dict(K=33), 2),
+    (dict(n=200, K=32), 2),               # n K > 4096 entries
+    (dict(dh=40), 2), (dict(r=8), 2), (dict(ndb=0), 2), (dict(N=-1), 2), (dict(c=ODD), 2),
+    (dict(ws=None), 3), (dict(ws_bytes=8), 3),
+])
+def test_schedule_draft_validation(lib, kw, status):
+    assert _sch(lib, **kw) == status
+
+
+def _schv(lib, **kw):
+    a = dict(h=FAKE, ws_=FAKE, ep=FAKE, w=FAKE, bias=1.0, temp=None, anchor=FAKE, tok=FAKE,
+             qoff=FAKE, budget=FAKE, n=4, rows=24, H=64, m=16, V=100, K=6, p=FAKE, s=FAKE,
+             vlen=FAKE, toff=None, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.sd_schedule_verify(a["h"], a["ws_"], a["ep"], a["w"], a["bias"], a["temp"],
+                                  a["anchor"], a["tok"], a["qoff"], a["budget"], a["n"],
+                                  a["rows"], a["H"], a["m"], a["V"], a["K"], a["p"], a["s"],
+                                  a["vlen"], a["toff"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(h=None), 1), (dict(qoff=None), 1), (dict(budget=None), 1), (dict(vlen=None), 1),
+    (dict(n=0), 2), (dict(rows=0), 2), (dict(rows=4097), 2), (dict(H=40), 2), (dict(m=8), 2),
+    (dict(V=0), 2), (dict(K=33), 2), (dict(bias=float("nan")), 2), (dict(h=ODD), 2),
+    (dict(ws=None), 3), (dict(ws_bytes=8), 3),
+])
+def test_schedule_verify_validation(lib, kw, status):
+    assert _schv(lib, **kw) == status
