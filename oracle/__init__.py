@@ -13,6 +13,7 @@ Modules:
                 prefix, or recent window + context summary; causal block)
   summary    -- the fixed-cost drafter's global context summary and its fold
   lm_head    -- LM-head logits, softmax statistics, Gumbel-max draft sampling
+  markov     -- the sequential (Markov) correction of the draft distributions
   verify     -- speculative-sampling verification (and its temperature-0 and
                 pruned-vocabulary variants)
   schedule   -- ForeSpark's pre-draft estimation, joint draft / verification
@@ -24,4 +25,4 @@ pages and the mathematics fix (the lossless theorem by exact enumeration,
 closed-form acceptance rates, decode-attention and SDPA special cases,
 bit-exact agreement of Philox with rocRAND's implementation, chi-square tests of the samplers).
 """
-from . import attention, lm_head, philox, schedule, step, summary, verify  # noqa: F401
+from . import attention, lm_head, markov, philox, schedule, step, summary, verify  # noqa: F401
