@@ -42,6 +42,9 @@ PATHS = {
     # "H-Spec": causal block over a 2048-token window, drafter vocabulary
     # pruned to 32,000 target tokens (sec. 3.3.2, App. B.2)
     "hspec": dict(causal_block=True, window=2048, draft_vocab=32000),
+    # "LongSpark" with the sequential correction of rank 256 (sec. 2.3) on top
+    # of the fixed-cost context
+    "longspark": dict(window=256, n_summary=16, markov_rank=256),
 }
 
 
@@ -75,11 +78,16 @@ def cpu_baseline(inp, n_req: int, target, opts, extra):
     t1 = time.perf_counter()
     lm = ostep.run_lm_head(inp.hidden, inp.w_vocab, b.q_off, inp.req_id, inp.philox_seed,
                            rows=rows, greedy=opts.greedy, vocab_map=extra.get("vmap"))
-    t2 = time.perf_counter()
     full_z = np.zeros((inp.total_q, lm["logits"].shape[1]), np.float64)
     full_z[rows] = lm["logits"]
     tok = np.zeros(inp.total_q, np.int32)
     tok[rows] = lm["tokens"]
+    if opts.markov_rank:
+        from oracle import markov as omk
+        mk = omk.markov_sample(full_z, b.q_off, extra["anchor"], extra["w_c"], extra["e_c"],
+                               inp.req_id, inp.philox_seed, requests=reqs)
+        full_z[rows], tok[rows] = mk["logits"][rows], mk["tokens"][rows]
+    t2 = time.perf_counter()
     tgt = inp.target_logits if target is None else target
     res = overify.verify(tgt, b.t_off, full_z, tok, b.q_off, inp.req_id, inp.philox_seed,
                          requests=reqs, greedy=opts.greedy, draft_vocab_inv=extra.get("vinv"))
@@ -94,7 +102,9 @@ def cpu_baseline(inp, n_req: int, target, opts, extra):
             "kind": "oracle",
             "sample": (f"{n_req} of {c.batch} requests: attention over all "
                        f"{c.num_heads_kv} KV heads at N={int(b.ctx_len[0])}, LM head on "
-                       f"{len(rows)} rows x {lm['logits'].shape[1]}, verification"
+                       f"{len(rows)} rows x {lm['logits'].shape[1]}"
+                       + (f", rank-{opts.markov_rank} sequential correction"
+                          if opts.markov_rank else "") + ", verification"
                        + (", summary fold" if opts.n_summary else "") +
                        f"; attn {t1 - t0:.2f}s lm {t2 - t1:.2f}s verify {t3 - t2:.2f}s"
                        + (f" fold {t4 - t3:.2f}s" if opts.n_summary else ""))}
@@ -213,7 +223,8 @@ def main():
     ap.add_argument("--path", choices=sorted(PATHS), default="full",
                     help="attention context: full prefix (default), LongSpark fixed-cost "
                          "(window 256 + 16 summary entries), H-Spec (causal block, window "
-                         "2048, 32,000-token drafter vocabulary)")
+                         "2048, 32,000-token drafter vocabulary), LongSpark fixed-cost with "
+                         "the rank-256 sequential correction")
     ap.add_argument("--greedy", action="store_true", help="temperature 0 on both sides")
     ap.add_argument("--schedule", action="store_true",
                     help="time the draft / verification scheduler instead of the step "
@@ -270,6 +281,12 @@ def main():
         extra["vinv"][extra["vmap"]] = np.arange(opts.draft_vocab, dtype=np.int32)
         t["vocab_map"] = sdev.i32(extra["vmap"], dev)
         t["vocab_inv"] = sdev.i32(extra["vinv"], dev)
+    if opts.markov_rank:
+        extra["w_c"], extra["e_c"] = inp.markov_tables(opts.markov_rank)
+        extra["anchor"] = inp.anchor_tokens()
+        t["markov_w_c"] = sdev.bf16(extra["w_c"], dev)
+        t["markov_e_c"] = sdev.bf16(extra["e_c"], dev)
+        t["anchor"] = sdev.i32(extra["anchor"], dev)
     if cfg.target[0] == "normal":
         t.update(sdev.verify_tensors(inp, dev))
     else:
@@ -291,7 +308,7 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -301,19 +318,23 @@ def main():
         e[1].record()
         step.lm_head(t, seed + 1000 + i)
         e[2].record()
-        step.verify(t, seed + 1000 + i)
+        if opts.markov_rank:
+            step.markov(t, seed + 1000 + i)
         e[3].record()
+        step.verify(t, seed + 1000 + i)
+        e[4].record()
         if opts.n_summary:
             step.summary_fold(t)
-        e[4].record()
+        e[5].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     log(f"[bench] timed {args.steps} steps in {elapsed:.3f}s")
 
     attn_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     lm_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
-    ver_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
-    fold_ms = np.array([e[3].elapsed_time(e[4]) for e in ev])
+    mk_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    ver_ms = np.array([e[3].elapsed_time(e[4]) for e in ev])
+    fold_ms = np.array([e[4].elapsed_time(e[5]) for e in ev])
     tokens_per_step = int(b.draft_k.sum())
     ms_per_step = elapsed * 1e3 / args.steps
     value = tokens_per_step * args.steps / elapsed
@@ -355,7 +376,7 @@ def main():
                    "split_tokens": args.split_tokens or "auto", "path": args.path,
                    "greedy": bool(args.greedy), "window": opts.window,
                    "summary_entries": opts.n_summary, "causal_block": opts.causal_block,
-                   "draft_vocab": v_draft},
+                   "draft_vocab": v_draft, "markov_rank": opts.markov_rank},
         "roofline": {"kernel": "sd_draft_attn call: attn_worklist + attn_splitk + attn_combine",
                      "bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
@@ -365,6 +386,7 @@ def main():
                      "avg_ms": round(float(attn_ms.mean()), 4)},
         "breakdown_ms": {"attention": round(float(attn_ms.mean()), 4),
                          "lm_head": round(float(lm_ms.mean()), 4),
+                         "markov": round(float(mk_ms.mean()), 4),
                          "verify": round(float(ver_ms.mean()), 4),
                          "summary_fold": round(float(fold_ms.mean()), 4)},
         "breakdown_p10_p90_ms": {k: [round(float(np.percentile(v, 10)), 4),
@@ -379,7 +401,7 @@ def main():
         # 3 attention modules of "H-Spec" and the 5 draft layers of "LongSpark"
         "projection_tokens_per_s": {
             f"{L}_layers": round(tokens_per_step / ((L * float(attn_ms.mean()) + float(lm_ms.mean())
-                                                      + float(ver_ms.mean())
+                                                      + float(mk_ms.mean()) + float(ver_ms.mean())
                                                       + float(fold_ms.mean())) * 1e-3), 1)
             for L in (3, 5)},
     }

@@ -16,7 +16,8 @@ from ._lib import LIB_PATH, SdError, check, load  # noqa: F401
 
 SD_MASK_NONE, SD_MASK_CAUSAL = 0, 1
 
-__all__ = ["sd_draft_attn", "sd_summary_update", "sd_lm_head_probs", "sd_verify",
+__all__ = ["sd_draft_attn", "sd_summary_update", "sd_lm_head_probs", "sd_markov_sample",
+           "sd_verify",
            "sd_schedule_draft", "sd_schedule_verify", "sd_version",
            "SD_MASK_NONE", "SD_MASK_CAUSAL",
            "draft_attn_workspace_size", "lm_head_workspace_size",
@@ -62,6 +63,10 @@ def draft_attn_workspace_size(batch, num_heads_q, num_heads_kv, head_dim, max_to
 
 def lm_head_workspace_size(M, V) -> int:
     return int(load().sd_lm_head_workspace_size(M, V))
+
+
+def markov_workspace_size(batch, V, max_draft_k) -> int:
+    return int(load().sd_markov_workspace_size(batch, V, max_draft_k))
 
 
 def verify_workspace_size(batch, total_q, total_target_rows, V) -> int:
@@ -188,6 +193,36 @@ def sd_lm_head_probs(hidden, w_vocab, q_off, req_id, seed: int, *, vocab_map=Non
                               _ptr(draft_tokens), _ptr(workspace), workspace.numel(),
                               _stream_handle(stream))
     check("sd_lm_head_probs", st)
+    return logits, lse, draft_tokens
+
+
+def sd_markov_sample(logits, anchor_tokens, w_c, e_c, q_off, req_id, seed: int, *,
+                     max_draft_k: int, lse=None, draft_tokens=None, workspace=None, stream=None):
+    """Sequential correction of the draft logits (in place) and sampling;
+    see ``sd_markov_sample`` in include/sd.h.  Returns (logits, lse, tokens)."""
+    lib = load()
+    dev = logits.device
+    _req(logits, "logits", _F32, dev)
+    _req(anchor_tokens, "anchor_tokens", _I32, dev)
+    _req(w_c, "w_c", _BF16, dev)
+    _req(e_c, "e_c", _BF16, dev)
+    _req(q_off, "q_off", _I32, dev)
+    _req(req_id, "req_id", _U32, dev)
+    M, V = logits.shape
+    r = w_c.shape[1]
+    if tuple(w_c.shape) != (V, r) or tuple(e_c.shape) != (V, r):
+        raise ValueError("w_c and e_c must be [V, r]")
+    batch = q_off.numel() - 1
+    if lse is None:
+        lse = torch.empty(M, dtype=torch.float32, device=dev)
+    if draft_tokens is None:
+        draft_tokens = torch.empty(M, dtype=torch.int32, device=dev)
+    workspace = _workspace(workspace, markov_workspace_size(batch, V, max_draft_k), dev)
+    st = lib.sd_markov_sample(_ptr(logits), _ptr(lse), _ptr(draft_tokens), _ptr(anchor_tokens),
+                              _ptr(w_c), _ptr(e_c), _ptr(q_off), batch, M, V, r, int(max_draft_k),
+                              _ptr(req_id), int(seed) & ((1 << 64) - 1), _ptr(workspace),
+                              workspace.numel(), _stream_handle(stream))
+    check("sd_markov_sample", st)
     return logits, lse, draft_tokens
 
 

@@ -366,6 +366,55 @@ sd_status sd_lm_head_probs(const void* hidden, const void* w_vocab, int32_t M, i
   return from_hip(sd::launch_lm_head(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t sd_markov_workspace_size(int32_t batch, int32_t V, int32_t max_draft_k) {
+  if (batch < 1 || V < 1 || max_draft_k < 1) return 0;
+  const size_t cells = static_cast<size_t>(max_draft_k) * batch;
+  return align_up(cells * sd::markov_parts(V) * sizeof(float2)) +
+         align_up(cells * sizeof(unsigned long long));
+}
+
+sd_status sd_markov_sample(float* logits, float* lse, int32_t* draft_tokens,
+                           const int32_t* anchor_tokens, const void* w_c, const void* e_c,
+                           const int32_t* q_off, int32_t batch, int32_t M, int32_t V, int32_t r,
+                           int32_t max_draft_k, const uint32_t* req_id, uint64_t seed,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!logits || !lse || !draft_tokens || !anchor_tokens || !w_c || !e_c || !q_off || !req_id)
+    return SD_ERR_NULL;
+  if (batch < 1 || M < 0 || V < 1 || r < 16 || r % 16 != 0 || r > 65536 || max_draft_k < 0 ||
+      max_draft_k > 4096)
+    return SD_ERR_SHAPE;
+  if (!aligned16(w_c) || !aligned16(e_c)) return SD_ERR_SHAPE;
+  if (static_cast<int64_t>(max_draft_k) * batch * sd::markov_parts(V) > (int64_t(1) << 31) - 1)
+    return SD_ERR_SHAPE;
+  if (M == 0 || max_draft_k == 0) return SD_OK;
+  const size_t need = sd_markov_workspace_size(batch, V, max_draft_k);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SD_ERR_WORKSPACE;
+  sd::MarkovArgs a;
+  a.logits = logits;
+  a.lse = lse;
+  a.tokens = draft_tokens;
+  a.anchor = anchor_tokens;
+  a.w_c = static_cast<const uint16_t*>(w_c);
+  a.e_c = static_cast<const uint16_t*>(e_c);
+  a.q_off = q_off;
+  a.req_id = req_id;
+  const size_t cells = static_cast<size_t>(max_draft_k) * batch;
+  a.part = static_cast<float2*>(workspace);
+  a.cell = reinterpret_cast<unsigned long long*>(
+      static_cast<char*>(workspace) + align_up(cells * sd::markov_parts(V) * sizeof(float2)));
+  a.batch = batch;
+  a.M = M;
+  a.V = V;
+  a.r = r;
+  a.max_k = max_draft_k;
+  a.n_chunks = sd::markov_chunks(V);
+  a.n_parts = sd::markov_parts(V);
+  a.vec4 = (V % 4 == 0 && aligned16(logits)) ? 1 : 0;
+  a.key0 = static_cast<uint32_t>(seed);
+  a.key1 = static_cast<uint32_t>(seed >> 32);
+  return from_hip(sd::launch_markov(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t sd_verify_workspace_size(int32_t batch, int32_t total_q, int32_t total_target_rows, int32_t V) {
   if (batch < 1 || total_q < 0 || total_target_rows < 1 || V < 1) return 0;
   return verify_layout(batch, total_q, total_target_rows, V).total;

@@ -152,6 +152,27 @@ constexpr int kLmHMultiple = 64;   // H must be a multiple of this
 
 hipError_t launch_lm_head(const LmArgs& a, hipStream_t s);
 
+// ------------------------------------------------------- Markov correction
+struct MarkovArgs {
+  float* logits;              // [M][V] base logits in, corrected out
+  float* lse;                 // [M]
+  int32_t* tokens;            // [M]
+  const int32_t* anchor;      // [batch] committed tokens y_0
+  const uint16_t* w_c;        // [V][r]
+  const uint16_t* e_c;        // [V][r]
+  const int32_t* q_off;       // [batch + 1]
+  const uint32_t* req_id;     // [batch]
+  float2* part;               // [max_k][batch][n_parts] (max, sum exp) (workspace)
+  unsigned long long* cell;   // [max_k][batch] packed draw (workspace)
+  int32_t batch, M, V, r, max_k, n_chunks, n_parts;
+  int32_t vec4;               // logits rows 16-byte aligned (V % 4 == 0, aligned base)
+  uint32_t key0, key1;
+};
+
+int32_t markov_chunks(int32_t V);   // 128-row vocab chunks
+int32_t markov_parts(int32_t V);    // partial statistics per (position, request)
+hipError_t launch_markov(const MarkovArgs& a, hipStream_t s);
+
 // ------------------------------------------------------------------- verify
 struct VerifyArgs {
   const float* target;      // [R, V]

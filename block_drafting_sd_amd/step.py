@@ -3,13 +3,16 @@
 Runs the C-ABI calls back to back on one stream: draft-block attention, LM
 head + draft sampling, verification ("LongSpark", sec. 2.1 and App. A.1,
 Fig. 6) and, on the fixed-cost context path, the fold of the retained rows
-into the context summary ("LongSpark", sec. 2.2 and App. A.2).  The drafter
+into the context summary ("LongSpark", sec. 2.2 and App. A.2).  With a
+correction rank the draws of the LM head are replaced by the sequential
+(Markov) correction and sampling ("LongSpark", sec. 2.3, eqs. (7)-(8)), whose
+corrected distributions verification then uses.  The drafter
 layers between attention and the LM head need trained weights and are outside
 the step, so the LM head consumes given draft states.
 
 ``StepOptions`` selects the variants the calls take as parameters: causal
 block mask, recent window, summary entries, pruned drafter vocabulary,
-temperature 0.
+temperature 0, rank of the sequential correction.
 """
 from __future__ import annotations
 
@@ -19,8 +22,9 @@ from typing import Dict, Optional
 import torch
 
 from . import (SD_MASK_CAUSAL, SD_MASK_NONE, draft_attn_workspace_size,
-               lm_head_workspace_size, sd_draft_attn, sd_lm_head_probs, sd_summary_update,
-               sd_verify, verify_workspace_size)
+               lm_head_workspace_size, markov_workspace_size, sd_draft_attn,
+               sd_lm_head_probs, sd_markov_sample, sd_summary_update, sd_verify,
+               verify_workspace_size)
 
 
 @dataclass
@@ -45,6 +49,12 @@ class StepOptions:
     n_summary: int = 0           # context-summary entries per KV head (0: none)
     draft_vocab: int = 0         # 0: full vocabulary; else the pruned drafter's size
     greedy: bool = False         # temperature 0 on both sides
+    markov_rank: int = 0         # 0: factorised drafts; r: sequential correction of rank r
+
+    def __post_init__(self):
+        if self.markov_rank and (self.greedy or self.draft_vocab):
+            raise ValueError("the sequential correction samples over the full drafter "
+                             "vocabulary at temperature 1")
 
 
 class DraftVerifyStep:
@@ -52,7 +62,8 @@ class DraftVerifyStep:
     verification tensors; with summary entries also ``summary_keys``
     [Hkv, S, D] and ``ctx_len_prev`` (prefix lengths before the rows the fold
     appends); with a pruned vocabulary ``vocab_map`` [V_d] and ``vocab_inv``
-    [V]."""
+    [V]; with a correction rank ``anchor`` [B] (the committed tokens) and the
+    bf16 tables ``markov_w_c``, ``markov_e_c`` [V, r]."""
 
     def __init__(self, shape: StepShape, device, options: Optional[StepOptions] = None):
         s = shape
@@ -79,6 +90,8 @@ class DraftVerifyStep:
                                               dtype=torch.float32, device=dev)
             self.summary_lse = torch.full((s.batch, s.num_heads_kv, o.n_summary), float("-inf"),
                                           dtype=torch.float32, device=dev)
+        if o.markov_rank:
+            self.ws_markov = torch.empty(max(256, markov_workspace_size(s.batch, vd, s.max_draft_k)), **u8)
         self.ws_verify = torch.empty(max(256, verify_workspace_size(
             s.batch, s.total_q, s.total_target_rows, s.vocab)), **u8)
 
@@ -107,6 +120,15 @@ class DraftVerifyStep:
                                 greedy=o.greedy, logits=self.logits, lse=self.lse,
                                 draft_tokens=self.tokens, workspace=self.ws_lm, stream=stream)
 
+    def markov(self, t: Dict[str, torch.Tensor], seed: int, stream=None):
+        """Correct the LM head's logits in place and redraw the tokens in
+        order (the LM head's own draws are overwritten)."""
+        return sd_markov_sample(self.logits, t["anchor"], t["markov_w_c"], t["markov_e_c"],
+                                t["q_off"], t["req_id"], seed,
+                                max_draft_k=self.shape.max_draft_k, lse=self.lse,
+                                draft_tokens=self.tokens, workspace=self.ws_markov,
+                                stream=stream)
+
     def verify(self, t: Dict[str, torch.Tensor], seed: int, stream=None):
         o = self.options
         return sd_verify(t["target_logits"], t["t_off"], self.logits, self.lse, self.tokens,
@@ -126,6 +148,8 @@ class DraftVerifyStep:
     def run(self, t: Dict[str, torch.Tensor], seed: int, stream=None):
         self.attention(t, stream)
         self.lm_head(t, seed, stream)
+        if self.options.markov_rank:
+            self.markov(t, seed, stream)
         self.verify(t, seed, stream)
         if self.options.n_summary:
             self.summary_fold(t, stream)

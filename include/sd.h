@@ -9,6 +9,7 @@
  *   sd_schedule_draft  pre-draft estimation, joint draft / verify schedule
  *   sd_schedule_verify post-draft estimation, verification budget split
  *   sd_lm_head_probs  drafter LM head, softmax statistics, draft sampling
+ *   sd_markov_sample   sequential (Markov) correction and sampling
  *   sd_verify         lossless speculative-sampling verification
  *
  * Conventions shared by every call
@@ -351,6 +352,49 @@ sd_status sd_lm_head_probs(const void* hidden, const void* w_vocab, int32_t M,
                            int32_t w_rows, int32_t greedy, float* logits,
                            float* lse, int32_t* draft_tokens, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * sd_markov_sample -- sequential (Markov) correction and sampling of the
+ * draft distributions.
+ *
+ * Defined by: "LongSpark", sec. 2.3, eqs. (7)-(8) (the base logits l_j^(0) of
+ * all K_b positions, computed in parallel, are refined as
+ * l_j = l_j^(0) + W_c e_c(y_{j-1}) with y_0 the committed token and a
+ * rank-r correction embedding e_c and output mapping W_c; q_j = softmax(l_j)
+ * is sampled position by position and the same q_j are used for
+ * verification; only the correction and the sampling are sequential).
+ *
+ * For every request b and j = 1..K_b (row m = q_off[b] + j - 1):
+ *   logits[m, v] += sum_k W_c[v, k] e_c[y_{j-1}, k]   (bf16 products, fp32)
+ *   lse[m] = log sum_v exp(logits[m, v])
+ *   draft_tokens[m] = y_j = argmax_v (logits[m, v] - log(-log u_v)), the
+ *   stream-0 uniforms of (request b, position j), as sd_lm_head_probs draws
+ * so W_c = 0 gives exactly the draws of sd_lm_head_probs.  The positions run
+ * in order on the stream (one launch each, plus one before and one after);
+ * nothing returns to the host.
+ *
+ * Arguments
+ *   logits   fp32 [M, V] in: base logits (e.g. from sd_lm_head_probs);
+ *            out: the corrected logits l_j
+ *   lse fp32 [M] out;  draft_tokens int32 [M] out
+ *   anchor_tokens int32 [batch]  y_0 of every request
+ *   w_c, e_c bf16 [V, r]  (r a multiple of 16, 16-byte aligned)
+ *   q_off    int32 [batch+1]; positions beyond max_draft_k (host bound,
+ *            0..4096) are left untouched
+ *   req_id, seed: as for sd_lm_head_probs
+ *   workspace sd_markov_workspace_size(batch, V, max_draft_k) bytes
+ * Errors: NULL -> SD_ERR_NULL; sizes out of range or unaligned tables ->
+ * SD_ERR_SHAPE; M == 0 or max_draft_k == 0 -> SD_OK with nothing launched;
+ * short or unaligned workspace -> SD_ERR_WORKSPACE.
+ * ------------------------------------------------------------------------ */
+size_t sd_markov_workspace_size(int32_t batch, int32_t V, int32_t max_draft_k);
+
+sd_status sd_markov_sample(float* logits, float* lse, int32_t* draft_tokens,
+                           const int32_t* anchor_tokens, const void* w_c,
+                           const void* e_c, const int32_t* q_off, int32_t batch,
+                           int32_t M, int32_t V, int32_t r, int32_t max_draft_k,
+                           const uint32_t* req_id, uint64_t seed,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * sd_verify -- lossless speculative-sampling verification.

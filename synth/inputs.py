@@ -36,6 +36,7 @@ TAG_CTX, TAG_KB, TAG_VB, TAG_PERM, TAG_K, TAG_V = 1, 2, 3, 4, 5, 6
 TAG_Q, TAG_KBLK, TAG_VBLK, TAG_HID, TAG_W, TAG_TGT = 7, 8, 9, 10, 11, 12
 TAG_SIGMA, TAG_REQ, TAG_SEED, TAG_NOISE, TAG_TOK = 13, 14, 15, 16, 17
 TAG_SUMQ, TAG_SUMV, TAG_VMAP = 18, 19, 20
+TAG_MKW, TAG_MKE, TAG_ANCHOR = 21, 22, 23
 
 PAGES_PER_CHUNK = 256
 W_ROWS_PER_CHUNK = 4096
@@ -410,3 +411,19 @@ class StepInputs:
         c = self.cfg
         ids = _rng(c.seed, TAG_VMAP, v_draft).choice(c.vocab, size=v_draft, replace=False)
         return np.sort(ids).astype(np.int32)
+
+    # ------------------------------------------------- sequential correction
+    def markov_tables(self, rank: int = 256):
+        """Seeded stand-ins for the correction's output mapping W_c and
+        embedding table e_c, bf16 bits ``[V, rank]`` each, entries
+        N(0, s^2) with s^2 = 0.5 / sqrt(rank): the correction of one logit
+        has standard deviation 0.5 whatever the rank."""
+        c = self.cfg
+        s = float(np.sqrt(0.5 / np.sqrt(rank)))
+        return (_normal_bf16(_rng(c.seed, TAG_MKW, rank), (c.vocab, rank), s),
+                _normal_bf16(_rng(c.seed, TAG_MKE, rank), (c.vocab, rank), s))
+
+    def anchor_tokens(self) -> np.ndarray:
+        """Seeded committed tokens y_0, one per request, in [0, V)."""
+        c = self.cfg
+        return _rng(c.seed, TAG_ANCHOR).integers(0, c.vocab, c.batch).astype(np.int32)

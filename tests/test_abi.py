@@ -201,3 +201,31 @@ def _schv(lib, **kw):
 ])
 def test_schedule_verify_validation(lib, kw, status):
     assert _schv(lib, **kw) == status
+
+
+def _mk(lib, **kw):
+    a = dict(z=FAKE, lse=FAKE, tok=FAKE, anchor=FAKE, wc=FAKE, ec=FAKE, qoff=FAKE, batch=2,
+             M=8, V=1000, r=32, k=4, req=FAKE, seed=5, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.sd_markov_sample(a["z"], a["lse"], a["tok"], a["anchor"], a["wc"], a["ec"],
+                                a["qoff"], a["batch"], a["M"], a["V"], a["r"], a["k"], a["req"],
+                                a["seed"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(z=None), 1), (dict(anchor=None), 1), (dict(wc=None), 1), (dict(req=None), 1),
+    (dict(batch=0), 2), (dict(M=-1), 2), (dict(V=0), 2), (dict(r=0), 2), (dict(r=24), 2),
+    (dict(k=-1), 2), (dict(k=5000), 2), (dict(wc=ODD), 2), (dict(ec=ODD), 2),
+    (dict(ws=None), 3), (dict(ws_bytes=16), 3), (dict(ws=ODD), 3),
+    (dict(M=0), 0), (dict(k=0), 0), (dict(k=0, ws=None), 0),          # nothing to launch
+])
+def test_markov_validation(lib, kw, status):
+    assert _mk(lib, **kw) == status
+
+
+def test_markov_workspace_size(lib):
+    # (max, sum exp) per workgroup and a 64-bit draw cell per (position, request)
+    assert lib.sd_markov_workspace_size(16, 151936, 16) >= 16 * 16 * (512 * 8 + 8)
+    assert lib.sd_markov_workspace_size(3, 1000, 5) >= 3 * 5 * (8 * 8 + 8)
+    assert lib.sd_markov_workspace_size(0, 10, 1) == 0
+    assert lib.sd_markov_workspace_size(1, 10, 0) == 0

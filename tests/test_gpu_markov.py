@@ -1,0 +1,111 @@
+"""GPU parity of the sequential (Markov) correction (sd_markov_sample).
+
+Corrected logits and lse within 1e-5 of the oracle's fp64 values (a rank-r
+bf16 product with fp32 accumulation added to fp32 logits), draws exact except
+audited near-ties (Gumbel top-2 key gap < 1e-5); after a near-tie draw the
+rest of that request follows another chain and is not compared.  With
+W_c = 0 the draws must equal sd_lm_head_probs' own, exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_drafting_sd_amd as sd
+from oracle import markov as omk, step as ostep
+from oracle.step import NEAR_TIE
+from synth import StepInputs, device as sdev
+from synth.configs import C1_32K, C2_128K
+
+from gpu_common import DEV, log, requires_gpu
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def _bf16(x):
+    return (torch.tensor(x, dtype=torch.float32).to(torch.bfloat16)
+            .view(torch.int16).numpy().view(np.uint16))
+
+
+def _tables(V, r, seed, scale=0.5):
+    rng = np.random.default_rng(seed)
+    return _bf16(rng.normal(0, scale, (V, r))), _bf16(rng.normal(0, scale, (V, r)))
+
+
+def _run(base, q_off, anchor, w_c, e_c, req_id, seed, max_k):
+    z = sdev.f32(base, DEV)
+    _, lse, tok = sd.sd_markov_sample(z, sdev.i32(anchor, DEV), sdev.bf16(w_c, DEV),
+                                      sdev.bf16(e_c, DEV), sdev.i32(q_off, DEV),
+                                      sdev.i32(req_id.view(np.int32), DEV), seed,
+                                      max_draft_k=max_k)
+    torch.cuda.synchronize()
+    return z.cpu().numpy(), lse.cpu().numpy(), tok.cpu().numpy()
+
+
+def _compare(got, ref, q_off, requests, tag):
+    z, lse, tok = got
+    worst_z = worst_l = 0.0
+    compared = mism = 0
+    for b in requests:
+        for m in range(int(q_off[b]), int(q_off[b + 1])):
+            worst_z = max(worst_z, float(np.abs(z[m] - ref["logits"][m]).max()))
+            worst_l = max(worst_l, abs(float(lse[m]) - ref["lse"][m]))
+            compared += 1
+            if tok[m] != ref["tokens"][m]:
+                assert ref["gap"][m] < NEAR_TIE, (tag, b, m, tok[m], ref["tokens"][m])
+                mism += 1
+                break      # the chains differ from here on
+    log(f"{tag}: rows {compared}, logits max-abs {worst_z:.2e}, lse max-abs {worst_l:.2e}, "
+        f"near-tie draws {mism}")
+    assert worst_z <= 1e-5 and worst_l <= 1e-5
+
+
+@pytest.mark.parametrize("V,r", [(1000, 32), (4096, 256)])
+def test_markov_small(V, r):
+    rng = np.random.default_rng(V + r)
+    d = np.array([3, 16, 1, 0, 9])
+    q_off = np.concatenate([[0], np.cumsum(d)]).astype(np.int32)
+    base = rng.normal(0, 2.0, (int(q_off[-1]), V)).astype(np.float32)
+    anchor = rng.integers(0, V, len(d)).astype(np.int32)
+    req_id = rng.integers(0, 2**32, len(d), dtype=np.uint64).astype(np.uint32)
+    w_c, e_c = _tables(V, r, V * r, scale=0.3)
+    got = _run(base, q_off, anchor, w_c, e_c, req_id, 77, 16)
+    ref = omk.markov_sample(base, q_off, anchor, w_c, e_c, req_id, 77)
+    _compare(got, ref, q_off, range(len(d)), f"markov V={V} r={r}")
+
+
+def test_zero_correction_reproduces_the_lm_head_draws():
+    cfg = C1_32K.with_(batch=4, ctx=16, draft_k=(16, 5, 1, 9), hidden=256, vocab=5000, seed=3)
+    inp = StepInputs(cfg)
+    t = sdev.lm_head_tensors(inp, DEV)
+    z, lse, tok = sd.sd_lm_head_probs(t["hidden"], t["w_vocab"], t["q_off"], t["req_id"],
+                                      inp.philox_seed)
+    zero = torch.zeros(cfg.vocab, 32, dtype=torch.bfloat16, device=DEV)
+    anchor = torch.zeros(cfg.batch, dtype=torch.int32, device=DEV)
+    z2 = z.clone()
+    _, lse2, tok2 = sd.sd_markov_sample(z2, anchor, zero, zero, t["q_off"], t["req_id"],
+                                        inp.philox_seed, max_draft_k=16)
+    torch.cuda.synchronize()
+    assert torch.equal(tok, tok2)
+    assert torch.equal(z, z2)
+    assert (lse - lse2).abs().max().item() <= 1e-6
+
+
+def test_markov_full_size_128k_shapes():
+    # 16 requests x K = 16 over the 151,936-token vocabulary, rank 256, the
+    # base logits from the LM head; two whole requests against the oracle
+    cfg = C2_128K.with_(ctx=16)
+    inp = StepInputs(cfg)
+    b = inp.budgets
+    t = sdev.lm_head_tensors(inp, DEV)
+    z, _, _ = sd.sd_lm_head_probs(t["hidden"], t["w_vocab"], t["q_off"], t["req_id"],
+                                  inp.philox_seed)
+    torch.cuda.synchronize()
+    base = z.cpu().numpy()
+    rng = np.random.default_rng(11)
+    anchor = rng.integers(0, cfg.vocab, cfg.batch).astype(np.int32)
+    w_c, e_c = _tables(cfg.vocab, 256, 12, scale=0.15)
+    got = _run(base, b.q_off, anchor, w_c, e_c, inp.req_id, inp.philox_seed, 16)
+    reqs = [0, cfg.batch - 1]
+    ref = omk.markov_sample(base, b.q_off, anchor, w_c, e_c, inp.req_id, inp.philox_seed,
+                            requests=reqs)
+    _compare(got, ref, b.q_off, reqs, "markov 16 x 16 x 151936, r = 256")
