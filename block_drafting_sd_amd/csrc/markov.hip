@@ -13,9 +13,11 @@
 //                 the stream-0 uniforms of position j.  A lane owns 4
 //                 consecutive vocab entries of one request: one Philox call.
 //                 Each workgroup stores its (max, sum exp) and merges its
-//                 candidate into the request's draw cell with one 64-bit
-//                 atomic max on (ordered key, ~index), so the next position
-//                 reads y_j from the cell without a merge launch.
+//                 candidate into one of the request's 16 draw cells with a
+//                 64-bit atomic max on (ordered key, ~index); the next
+//                 position reads y_j as the largest of the 16 cells, without
+//                 a merge launch.  (All workgroups on one cell would
+//                 serialise: each cell group is a separate 512-byte block.)
 //   markov_final  lse of every (request, position) from the stored partials
 //                 and the drawn tokens from the cells.
 // The positions follow each other on the stream; nothing returns to the host.
@@ -48,6 +50,23 @@ __device__ __forceinline__ int cand_index(unsigned long long w) {
   return static_cast<int>(~static_cast<uint32_t>(w));
 }
 
+// Draw cell `sub` of (position j, request b); cells of one (j, sub) group
+// are contiguous, groups are cell_stride words apart.
+__device__ __forceinline__ size_t cell_at(const MarkovArgs& a, int j, int sub, int b) {
+  return (static_cast<size_t>(j - 1) * kMarkovCells + sub) * a.cell_stride + b;
+}
+
+// y_j of request b: the best of its cells.
+__device__ __forceinline__ int drawn_token(const MarkovArgs& a, int j, int b) {
+  unsigned long long w = 0;
+#pragma unroll
+  for (int c = 0; c < kMarkovCells; ++c) {
+    const unsigned long long x = a.cell[cell_at(a, j, c, b)];
+    w = x > w ? x : w;
+  }
+  return clampi(cand_index(w), 0, a.V - 1);
+}
+
 // Folds value x of vocab entry v into (mx, se) and the Gumbel-max candidate.
 __device__ __forceinline__ void fold_entry(float x, float g, int v, float& mx, float& se, Cand& best) {
   if (x > mx) {
@@ -74,8 +93,8 @@ __device__ __forceinline__ void active_row(const MarkovArgs& a, int b, int j, bo
 }
 
 __global__ __launch_bounds__(256) void markov_init(MarkovArgs a) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < a.max_k * a.batch) a.cell[i] = 0ull;
+  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < static_cast<size_t>(a.max_k) * kMarkovCells * a.cell_stride) a.cell[i] = 0ull;
 }
 
 // Workgroup (p, tile) walks the chunks p, p + gridDim.x, ... for requests
@@ -94,8 +113,7 @@ __global__ __launch_bounds__(256) void markov_step(MarkovArgs a, int j) {
   if (b < a.batch) {
     active_row(a, b, j, active, m);
     rid = a.req_id[b];
-    y = j == 1 ? a.anchor[b] : cand_index(a.cell[static_cast<size_t>(j - 2) * a.batch + b]);
-    y = clampi(y, 0, a.V - 1);
+    y = j == 1 ? clampi(a.anchor[b], 0, a.V - 1) : drawn_token(a, j - 1, b);
   }
   float* row = a.logits + static_cast<size_t>(m) * a.V;
   const uint16_t* er = a.e_c + static_cast<size_t>(y) * a.r + 8 * q;
@@ -194,7 +212,7 @@ __global__ __launch_bounds__(256) void markov_step(MarkovArgs a, int j) {
     }
     const size_t jb = static_cast<size_t>(j - 1) * a.batch + b;
     a.part[jb * a.n_parts + blockIdx.x] = make_float2(M, S);
-    atomicMax(a.cell + jb, pack_cand(bb.key, bb.idx));
+    atomicMax(a.cell + cell_at(a, j, blockIdx.x % kMarkovCells, b), pack_cand(bb.key, bb.idx));
   }
 }
 
@@ -223,14 +241,15 @@ __global__ __launch_bounds__(256) void markov_final(MarkovArgs a) {
 #pragma unroll
     for (int w = 1; w < 4; ++w) merge_stats(M, S, sh[w], sh[4 + w]);
     a.lse[m] = M + logf(S);
-    a.tokens[m] = clampi(cand_index(a.cell[jb]), 0, a.V - 1);
+    a.tokens[m] = drawn_token(a, j, b);
   }
 }
 
 }  // namespace
 
 hipError_t launch_markov(const MarkovArgs& a, hipStream_t s) {
-  hipError_t e = launch_kernel(markov_init, dim3((a.max_k * a.batch + 255) / 256), dim3(256), s, a);
+  const size_t cells = static_cast<size_t>(a.max_k) * kMarkovCells * a.cell_stride;
+  hipError_t e = launch_kernel(markov_init, dim3(static_cast<unsigned>((cells + 255) / 256)), dim3(256), s, a);
   const dim3 grid(a.n_parts, (a.batch + kRTile - 1) / kRTile);
   for (int j = 1; j <= a.max_k && e == hipSuccess; ++j) {
     void* args[] = {const_cast<MarkovArgs*>(&a), &j};

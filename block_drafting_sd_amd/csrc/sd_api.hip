@@ -369,8 +369,9 @@ sd_status sd_lm_head_probs(const void* hidden, const void* w_vocab, int32_t M, i
 size_t sd_markov_workspace_size(int32_t batch, int32_t V, int32_t max_draft_k) {
   if (batch < 1 || V < 1 || max_draft_k < 1) return 0;
   const size_t cells = static_cast<size_t>(max_draft_k) * batch;
+  const size_t draw = static_cast<size_t>(max_draft_k) * sd::kMarkovCells * sd::markov_cell_stride(batch);
   return align_up(cells * sd::markov_parts(V) * sizeof(float2)) +
-         align_up(cells * sizeof(unsigned long long));
+         align_up(draw * sizeof(unsigned long long));
 }
 
 sd_status sd_markov_sample(float* logits, float* lse, int32_t* draft_tokens,
@@ -409,6 +410,7 @@ sd_status sd_markov_sample(float* logits, float* lse, int32_t* draft_tokens,
   a.max_k = max_draft_k;
   a.n_chunks = sd::markov_chunks(V);
   a.n_parts = sd::markov_parts(V);
+  a.cell_stride = sd::markov_cell_stride(batch);
   a.vec4 = (V % 4 == 0 && aligned16(logits)) ? 1 : 0;
   a.key0 = static_cast<uint32_t>(seed);
   a.key1 = static_cast<uint32_t>(seed >> 32);

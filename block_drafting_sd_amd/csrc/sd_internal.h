@@ -163,12 +163,14 @@ struct MarkovArgs {
   const int32_t* q_off;       // [batch + 1]
   const uint32_t* req_id;     // [batch]
   float2* part;               // [max_k][batch][n_parts] (max, sum exp) (workspace)
-  unsigned long long* cell;   // [max_k][batch] packed draw (workspace)
-  int32_t batch, M, V, r, max_k, n_chunks, n_parts;
+  unsigned long long* cell;   // [max_k][kMarkovCells][cell_stride] packed draws (workspace)
+  int32_t batch, M, V, r, max_k, n_chunks, n_parts, cell_stride;
   int32_t vec4;               // logits rows 16-byte aligned (V % 4 == 0, aligned base)
   uint32_t key0, key1;
 };
 
+constexpr int kMarkovCells = 16;     // draw cells per (position, request)
+inline int32_t markov_cell_stride(int32_t batch) { return (batch + 63) / 64 * 64; }  // 512-byte groups
 int32_t markov_chunks(int32_t V);   // 128-row vocab chunks
 int32_t markov_parts(int32_t V);    // partial statistics per (position, request)
 hipError_t launch_markov(const MarkovArgs& a, hipStream_t s);
