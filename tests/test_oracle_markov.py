@@ -6,6 +6,13 @@ sec. 2.3, eqs. (7)-(8)).
   the previous draw, position by position (the dependence on y_{j-1});
 * a correction that adds a huge bonus to one token forces every draw after
   the first (a closed form: y_j = argmax of that bonus), whatever the base.
+
+"DeLS-Spec" fusion (alpha, unigram-prior bias):
+* the smoothed prior is a distribution; uniform counts give 1/V and lambda = 0
+  the empirical frequencies (closed forms);
+* long logits equal to the log prior, minus the prior (beta = 1, alpha = 0),
+  leave a flat row: lse = log V exactly (a sign error would double the prior);
+* alpha = 2 equals doubling W_M (exact in bf16).
 """
 import numpy as np
 import torch
@@ -72,3 +79,36 @@ def test_dominant_correction_forces_the_chain():
         for m in range(q_off[b], q_off[b + 1]):
             assert got["tokens"][m] == (prev + 7) % V
             prev = int(got["tokens"][m])
+
+
+def test_unigram_prior_closed_forms():
+    counts = np.array([0, 3, 10, 0, 7, 1000], np.int64)
+    lp = omk.unigram_log_prior(counts)
+    assert abs(np.exp(lp).sum() - 1.0) < 1e-15
+    np.testing.assert_allclose(np.exp(lp), (counts + 1.0) / (counts.sum() + 6.0), rtol=1e-15)
+    np.testing.assert_allclose(omk.unigram_log_prior(np.full(9, 5)), np.full(9, -np.log(9.0)), rtol=0,
+                               atol=1e-15)
+    nz = counts > 0
+    np.testing.assert_allclose(np.exp(omk.unigram_log_prior(counts, lam=0.0))[nz],
+                               counts[nz] / counts.sum(), rtol=1e-15)
+
+
+def test_prior_subtraction_flattens_the_prior():
+    V = 37
+    rng = np.random.default_rng(4)
+    counts = rng.integers(0, 50, V)
+    b0 = omk.unigram_log_prior(counts).astype(np.float32)
+    base, q_off, anchor, w_c, e_c, req_id = _problem(3, V=V)
+    base = np.broadcast_to(b0, base.shape).copy()
+    got = omk.markov_sample(base, q_off, anchor, w_c, e_c, req_id, 8, alpha=0.0, vocab_bias=-b0)
+    np.testing.assert_array_equal(got["logits"], 0.0)
+    np.testing.assert_allclose(got["lse"], np.log(V), rtol=0, atol=1e-15)
+
+
+def test_alpha_scales_the_correction():
+    base, q_off, anchor, w_c, e_c, req_id = _problem(5)
+    w2 = _bf16(2.0 * bf16_bits_to_f64(w_c))
+    a = omk.markov_sample(base, q_off, anchor, w_c, e_c, req_id, 17, alpha=2.0)
+    b = omk.markov_sample(base, q_off, anchor, w2, e_c, req_id, 17)
+    np.testing.assert_array_equal(a["tokens"], b["tokens"])
+    np.testing.assert_allclose(a["logits"], b["logits"], rtol=0, atol=1e-13)
