@@ -45,6 +45,9 @@ PATHS = {
     # "LongSpark" with the sequential correction of rank 256 (sec. 2.3) on top
     # of the fixed-cost context
     "longspark": dict(window=256, n_summary=16, markov_rank=256),
+    # "DeLS-Spec": the full-prefix block drafter with the Markov local head
+    # fused as l_L + 0.3 l_S - 0.3 log p~_0 (rank 256: a reading)
+    "dels": dict(markov_rank=256, markov_alpha=0.3, prior_beta=0.3),
 }
 
 
@@ -84,8 +87,11 @@ def cpu_baseline(inp, n_req: int, target, opts, extra):
     tok[rows] = lm["tokens"]
     if opts.markov_rank:
         from oracle import markov as omk
+        bias = (-opts.prior_beta * omk.unigram_log_prior(extra["counts"])
+                if opts.prior_beta else None)
         mk = omk.markov_sample(full_z, b.q_off, extra["anchor"], extra["w_c"], extra["e_c"],
-                               inp.req_id, inp.philox_seed, requests=reqs)
+                               inp.req_id, inp.philox_seed, requests=reqs,
+                               alpha=opts.markov_alpha, vocab_bias=bias)
         full_z[rows], tok[rows] = mk["logits"][rows], mk["tokens"][rows]
     t2 = time.perf_counter()
     tgt = inp.target_logits if target is None else target
@@ -224,7 +230,8 @@ def main():
                     help="attention context: full prefix (default), LongSpark fixed-cost "
                          "(window 256 + 16 summary entries), H-Spec (causal block, window "
                          "2048, 32,000-token drafter vocabulary), LongSpark fixed-cost with "
-                         "the rank-256 sequential correction")
+                         "the rank-256 sequential correction, DeLS-Spec fusion (full prefix, "
+                         "Markov local head of rank 256, alpha = beta = 0.3)")
     ap.add_argument("--greedy", action="store_true", help="temperature 0 on both sides")
     ap.add_argument("--schedule", action="store_true",
                     help="time the draft / verification scheduler instead of the step "
@@ -287,6 +294,11 @@ def main():
         t["markov_w_c"] = sdev.bf16(extra["w_c"], dev)
         t["markov_e_c"] = sdev.bf16(extra["e_c"], dev)
         t["anchor"] = sdev.i32(extra["anchor"], dev)
+    if opts.prior_beta:
+        # fixed vocabulary bias from corpus counts (setup, untimed)
+        extra["counts"] = inp.unigram_counts()
+        t["vocab_bias"] = sd.sd_log_prior_bias(torch.from_numpy(extra["counts"]).to(dev),
+                                               lam=1.0, scale=-opts.prior_beta)
     if cfg.target[0] == "normal":
         t.update(sdev.verify_tensors(inp, dev))
     else:
@@ -376,7 +388,8 @@ def main():
                    "split_tokens": args.split_tokens or "auto", "path": args.path,
                    "greedy": bool(args.greedy), "window": opts.window,
                    "summary_entries": opts.n_summary, "causal_block": opts.causal_block,
-                   "draft_vocab": v_draft, "markov_rank": opts.markov_rank},
+                   "draft_vocab": v_draft, "markov_rank": opts.markov_rank,
+                   "markov_alpha": opts.markov_alpha, "prior_beta": opts.prior_beta},
         "roofline": {"kernel": "sd_draft_attn call: attn_worklist + attn_splitk + attn_combine",
                      "bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),

@@ -197,9 +197,11 @@ def sd_lm_head_probs(hidden, w_vocab, q_off, req_id, seed: int, *, vocab_map=Non
 
 
 def sd_markov_sample(logits, anchor_tokens, w_c, e_c, q_off, req_id, seed: int, *,
-                     max_draft_k: int, lse=None, draft_tokens=None, workspace=None, stream=None):
+                     max_draft_k: int, alpha: float = 1.0, vocab_bias=None, lse=None,
+                     draft_tokens=None, workspace=None, stream=None):
     """Sequential correction of the draft logits (in place) and sampling;
-    see ``sd_markov_sample`` in include/sd.h.  Returns (logits, lse, tokens)."""
+    see ``sd_markov_sample`` in include/sd.h (``alpha`` and ``vocab_bias``
+    give the logit fusion).  Returns (logits, lse, tokens)."""
     lib = load()
     dev = logits.device
     _req(logits, "logits", _F32, dev)
@@ -212,6 +214,10 @@ def sd_markov_sample(logits, anchor_tokens, w_c, e_c, q_off, req_id, seed: int, 
     r = w_c.shape[1]
     if tuple(w_c.shape) != (V, r) or tuple(e_c.shape) != (V, r):
         raise ValueError("w_c and e_c must be [V, r]")
+    if vocab_bias is not None:
+        _req(vocab_bias, "vocab_bias", _F32, dev)
+        if vocab_bias.numel() != V:
+            raise ValueError("vocab_bias must have V entries")
     batch = q_off.numel() - 1
     if lse is None:
         lse = torch.empty(M, dtype=torch.float32, device=dev)
@@ -219,11 +225,28 @@ def sd_markov_sample(logits, anchor_tokens, w_c, e_c, q_off, req_id, seed: int, 
         draft_tokens = torch.empty(M, dtype=torch.int32, device=dev)
     workspace = _workspace(workspace, markov_workspace_size(batch, V, max_draft_k), dev)
     st = lib.sd_markov_sample(_ptr(logits), _ptr(lse), _ptr(draft_tokens), _ptr(anchor_tokens),
-                              _ptr(w_c), _ptr(e_c), _ptr(q_off), batch, M, V, r, int(max_draft_k),
+                              _ptr(w_c), _ptr(e_c), float(alpha),
+                              None if vocab_bias is None else _ptr(vocab_bias), _ptr(q_off),
+                              batch, M, V, r, int(max_draft_k),
                               _ptr(req_id), int(seed) & ((1 << 64) - 1), _ptr(workspace),
                               workspace.numel(), _stream_handle(stream))
     check("sd_markov_sample", st)
     return logits, lse, draft_tokens
+
+
+def sd_log_prior_bias(counts, *, lam: float = 1.0, scale: float = -0.3, out=None, stream=None):
+    """``scale * log p~_0`` from int64 corpus counts [V] (additive smoothing
+    ``lam``); see ``sd_log_prior_bias`` in include/sd.h.  Returns fp32 [V]."""
+    lib = load()
+    dev = counts.device
+    _req(counts, "counts", (torch.int64,), dev)
+    V = counts.numel()
+    if out is None:
+        out = torch.empty(V, dtype=torch.float32, device=dev)
+    _req(out, "out", _F32, dev)
+    check("sd_log_prior_bias", lib.sd_log_prior_bias(_ptr(counts), V, float(lam), float(scale),
+                                                     _ptr(out), _stream_handle(stream)))
+    return out
 
 
 def sd_verify(target_logits, t_off, draft_logits, draft_lse, draft_tokens, q_off, req_id,

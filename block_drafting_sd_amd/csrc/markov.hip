@@ -20,6 +20,9 @@
 //                 serialise: each cell group is a separate 512-byte block.)
 //   markov_final  lse of every (request, position) from the stored partials
 //                 and the drawn tokens from the cells.
+// The same launch computes the "DeLS-Spec" fusion with its Markov local head:
+// the correction is scaled by alpha and a fixed per-vocab bias (minus beta
+// times the log unigram prior, from log_prior_bias) is added to every row.
 // The positions follow each other on the stream; nothing returns to the host.
 #include "sd_common.h"
 #include "sd_internal.h"
@@ -128,8 +131,9 @@ __global__ __launch_bounds__(256) void markov_step(MarkovArgs a, int j) {
   Cand best{-FLT_MAX, 0x7fffffff};
   for (int chunk = blockIdx.x; chunk < a.n_chunks; chunk += gridDim.x) {
     const int vw = chunk * kVChunk + 32 * wave;       // first vocab row of this wave
-    // base logits first, so that their latency overlaps the W_c loads
-    float4 l[2];
+    // base logits (and the vocab bias) first, so that their latency
+    // overlaps the W_c loads
+    float4 l[2], vb[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int v = vw + 16 * t + 4 * q;
@@ -140,6 +144,17 @@ __global__ __launch_bounds__(256) void markov_step(MarkovArgs a, int j) {
         l[t].y = active && v + 1 < a.V ? row[v + 1] : 0.f;
         l[t].z = active && v + 2 < a.V ? row[v + 2] : 0.f;
         l[t].w = active && v + 3 < a.V ? row[v + 3] : 0.f;
+      }
+      vb[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (a.vbias && active) {
+        if (a.vec4 && v + 3 < a.V) {
+          vb[t] = *reinterpret_cast<const float4*>(a.vbias + v);
+        } else {
+          vb[t].x = v < a.V ? a.vbias[v] : 0.f;
+          vb[t].y = v + 1 < a.V ? a.vbias[v + 1] : 0.f;
+          vb[t].z = v + 2 < a.V ? a.vbias[v + 2] : 0.f;
+          vb[t].w = v + 3 < a.V ? a.vbias[v + 3] : 0.f;
+        }
       }
     }
     // A operands: W_c rows vw + 16 t + col, every k-step of a k-chunk in flight
@@ -171,7 +186,8 @@ __global__ __launch_bounds__(256) void markov_step(MarkovArgs a, int j) {
       for (int t = 0; t < 2; ++t) {
         const f32x4 c = t == 0 ? acc0 : acc1;
         const int v = vw + 16 * t + 4 * q;              // multiple of 4
-        const float x[4] = {l[t].x + c[0], l[t].y + c[1], l[t].z + c[2], l[t].w + c[3]};
+        const float x[4] = {l[t].x + a.alpha * c[0] + vb[t].x, l[t].y + a.alpha * c[1] + vb[t].y,
+                            l[t].z + a.alpha * c[2] + vb[t].z, l[t].w + a.alpha * c[3] + vb[t].w};
         if (a.vec4 && v + 3 < a.V) {
           *reinterpret_cast<float4*>(row + v) = make_float4(x[0], x[1], x[2], x[3]);
         } else {
@@ -245,7 +261,34 @@ __global__ __launch_bounds__(256) void markov_final(MarkovArgs a) {
   }
 }
 
+// scale * log((c_v + lambda) / (sum_u c_u + lambda V)), one workgroup: the
+// smoothed unigram log-prior, scaled (-beta for the fusion bias).
+__global__ __launch_bounds__(1024) void log_prior_bias(const int64_t* counts, int V, double lam, float scale,
+                                                       float* out) {
+  __shared__ double sh[16];
+  double s = 0.0;
+  for (int v = threadIdx.x; v < V; v += 1024) s += static_cast<double>(max(counts[v], int64_t(0)));
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o, 64);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = s;
+  __syncthreads();
+  double tot = 0.0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) tot += sh[w];
+  const double den = tot + lam * V;
+  for (int v = threadIdx.x; v < V; v += 1024) {
+    const double c = static_cast<double>(max(counts[v], int64_t(0)));
+    out[v] = static_cast<float>(scale * log((c + lam) / den));
+  }
+}
+
 }  // namespace
+
+hipError_t launch_log_prior_bias(const int64_t* counts, int V, double lam, float scale, float* out,
+                                 hipStream_t s) {
+  void* args[] = {const_cast<int64_t**>(&counts), &V, &lam, &scale, &out};
+  return hipLaunchKernel(reinterpret_cast<const void*>(log_prior_bias), dim3(1), dim3(1024), args, 0, s);
+}
 
 hipError_t launch_markov(const MarkovArgs& a, hipStream_t s) {
   const size_t cells = static_cast<size_t>(a.max_k) * kMarkovCells * a.cell_stride;

@@ -376,7 +376,7 @@ size_t sd_markov_workspace_size(int32_t batch, int32_t V, int32_t max_draft_k) {
 
 sd_status sd_markov_sample(float* logits, float* lse, int32_t* draft_tokens,
                            const int32_t* anchor_tokens, const void* w_c, const void* e_c,
-                           const int32_t* q_off, int32_t batch, int32_t M, int32_t V, int32_t r,
+                           float alpha, const float* vocab_bias, const int32_t* q_off, int32_t batch, int32_t M, int32_t V, int32_t r,
                            int32_t max_draft_k, const uint32_t* req_id, uint64_t seed,
                            void* workspace, size_t workspace_bytes, void* stream) {
   if (!logits || !lse || !draft_tokens || !anchor_tokens || !w_c || !e_c || !q_off || !req_id)
@@ -384,7 +384,7 @@ sd_status sd_markov_sample(float* logits, float* lse, int32_t* draft_tokens,
   if (batch < 1 || M < 0 || V < 1 || r < 16 || r % 16 != 0 || r > 65536 || max_draft_k < 0 ||
       max_draft_k > 4096)
     return SD_ERR_SHAPE;
-  if (!aligned16(w_c) || !aligned16(e_c)) return SD_ERR_SHAPE;
+  if (!aligned16(w_c) || !aligned16(e_c) || !isfinite(alpha)) return SD_ERR_SHAPE;
   if (static_cast<int64_t>(max_draft_k) * batch * sd::markov_parts(V) > (int64_t(1) << 31) - 1)
     return SD_ERR_SHAPE;
   if (M == 0 || max_draft_k == 0) return SD_OK;
@@ -397,6 +397,8 @@ sd_status sd_markov_sample(float* logits, float* lse, int32_t* draft_tokens,
   a.anchor = anchor_tokens;
   a.w_c = static_cast<const uint16_t*>(w_c);
   a.e_c = static_cast<const uint16_t*>(e_c);
+  a.vbias = vocab_bias;
+  a.alpha = alpha;
   a.q_off = q_off;
   a.req_id = req_id;
   const size_t cells = static_cast<size_t>(max_draft_k) * batch;
@@ -411,10 +413,17 @@ sd_status sd_markov_sample(float* logits, float* lse, int32_t* draft_tokens,
   a.n_chunks = sd::markov_chunks(V);
   a.n_parts = sd::markov_parts(V);
   a.cell_stride = sd::markov_cell_stride(batch);
-  a.vec4 = (V % 4 == 0 && aligned16(logits)) ? 1 : 0;
+  a.vec4 = (V % 4 == 0 && aligned16(logits) && (!vocab_bias || aligned16(vocab_bias))) ? 1 : 0;
   a.key0 = static_cast<uint32_t>(seed);
   a.key1 = static_cast<uint32_t>(seed >> 32);
   return from_hip(sd::launch_markov(a, static_cast<hipStream_t>(stream)));
+}
+
+sd_status sd_log_prior_bias(const int64_t* counts, int32_t V, double lambda, float scale, float* out,
+                            void* stream) {
+  if (!counts || !out) return SD_ERR_NULL;
+  if (V < 1 || !(lambda > 0.0) || !isfinite(lambda) || !isfinite(scale)) return SD_ERR_SHAPE;
+  return from_hip(sd::launch_log_prior_bias(counts, V, lambda, scale, out, static_cast<hipStream_t>(stream)));
 }
 
 size_t sd_verify_workspace_size(int32_t batch, int32_t total_q, int32_t total_target_rows, int32_t V) {

@@ -160,6 +160,8 @@ struct MarkovArgs {
   const int32_t* anchor;      // [batch] committed tokens y_0
   const uint16_t* w_c;        // [V][r]
   const uint16_t* e_c;        // [V][r]
+  const float* vbias;         // [V] added to every row, or null
+  float alpha;                // scale of the correction
   const int32_t* q_off;       // [batch + 1]
   const uint32_t* req_id;     // [batch]
   float2* part;               // [max_k][batch][n_parts] (max, sum exp) (workspace)
@@ -174,6 +176,8 @@ inline int32_t markov_cell_stride(int32_t batch) { return (batch + 63) / 64 * 64
 int32_t markov_chunks(int32_t V);   // 128-row vocab chunks
 int32_t markov_parts(int32_t V);    // partial statistics per (position, request)
 hipError_t launch_markov(const MarkovArgs& a, hipStream_t s);
+hipError_t launch_log_prior_bias(const int64_t* counts, int V, double lam, float scale, float* out,
+                                 hipStream_t s);
 
 // ------------------------------------------------------------------- verify
 struct VerifyArgs {

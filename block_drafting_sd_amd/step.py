@@ -50,6 +50,8 @@ class StepOptions:
     draft_vocab: int = 0         # 0: full vocabulary; else the pruned drafter's size
     greedy: bool = False         # temperature 0 on both sides
     markov_rank: int = 0         # 0: factorised drafts; r: sequential correction of rank r
+    markov_alpha: float = 1.0    # scale of the correction (logit fusion: 0.3)
+    prior_beta: float = 0.0      # fusion: subtract beta x log unigram prior (t["vocab_bias"])
 
     def __post_init__(self):
         if self.markov_rank and (self.greedy or self.draft_vocab):
@@ -63,7 +65,8 @@ class DraftVerifyStep:
     [Hkv, S, D] and ``ctx_len_prev`` (prefix lengths before the rows the fold
     appends); with a pruned vocabulary ``vocab_map`` [V_d] and ``vocab_inv``
     [V]; with a correction rank ``anchor`` [B] (the committed tokens) and the
-    bf16 tables ``markov_w_c``, ``markov_e_c`` [V, r]."""
+    bf16 tables ``markov_w_c``, ``markov_e_c`` [V, r]; with a prior weight
+    ``vocab_bias`` [V] (-beta log p~_0, from ``sd_log_prior_bias``)."""
 
     def __init__(self, shape: StepShape, device, options: Optional[StepOptions] = None):
         s = shape
@@ -123,9 +126,11 @@ class DraftVerifyStep:
     def markov(self, t: Dict[str, torch.Tensor], seed: int, stream=None):
         """Correct the LM head's logits in place and redraw the tokens in
         order (the LM head's own draws are overwritten)."""
+        o = self.options
         return sd_markov_sample(self.logits, t["anchor"], t["markov_w_c"], t["markov_e_c"],
                                 t["q_off"], t["req_id"], seed,
-                                max_draft_k=self.shape.max_draft_k, lse=self.lse,
+                                max_draft_k=self.shape.max_draft_k, alpha=o.markov_alpha,
+                                vocab_bias=t["vocab_bias"] if o.prior_beta else None, lse=self.lse,
                                 draft_tokens=self.tokens, workspace=self.ws_markov,
                                 stream=stream)
 

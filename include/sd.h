@@ -9,7 +9,8 @@
  *   sd_schedule_draft  pre-draft estimation, joint draft / verify schedule
  *   sd_schedule_verify post-draft estimation, verification budget split
  *   sd_lm_head_probs  drafter LM head, softmax statistics, draft sampling
- *   sd_markov_sample   sequential (Markov) correction and sampling
+ *   sd_markov_sample   sequential (Markov) correction and sampling, logit fusion
+ *   sd_log_prior_bias  smoothed unigram log-prior (fusion bias)
  *   sd_verify         lossless speculative-sampling verification
  *
  * Conventions shared by every call
@@ -362,15 +363,21 @@ sd_status sd_lm_head_probs(const void* hidden, const void* w_vocab, int32_t M,
  * l_j = l_j^(0) + W_c e_c(y_{j-1}) with y_0 the committed token and a
  * rank-r correction embedding e_c and output mapping W_c; q_j = softmax(l_j)
  * is sampled position by position and the same q_j are used for
- * verification; only the correction and the sampling are sequential).
+ * verification; only the correction and the sampling are sequential), and
+ * "DeLS-Spec" (logit fusion at inference with the Markov local head: the
+ * long logits plus alpha times W_M e_M(x_{i-1}) minus beta times the log
+ * unigram prior; alpha = beta = 0.3 by default).
  *
  * For every request b and j = 1..K_b (row m = q_off[b] + j - 1):
- *   logits[m, v] += sum_k W_c[v, k] e_c[y_{j-1}, k]   (bf16 products, fp32)
+ *   logits[m, v] += alpha * sum_k W_c[v, k] e_c[y_{j-1}, k] + vocab_bias[v]
+ *                   (bf16 products, fp32 accumulation and sums)
  *   lse[m] = log sum_v exp(logits[m, v])
  *   draft_tokens[m] = y_j = argmax_v (logits[m, v] - log(-log u_v)), the
  *   stream-0 uniforms of (request b, position j), as sd_lm_head_probs draws
- * so W_c = 0 gives exactly the draws of sd_lm_head_probs.  The positions run
- * in order on the stream (one launch each, plus one before and one after);
+ * so W_c = 0 (or alpha = 0) without a bias gives exactly the draws of
+ * sd_lm_head_probs.  LongSpark: alpha = 1, vocab_bias = NULL.  DeLS-Spec:
+ * vocab_bias = -beta log p~_0 from sd_log_prior_bias.  The positions run in
+ * order on the stream (one launch each, plus one before and one after);
  * nothing returns to the host.
  *
  * Arguments
@@ -379,22 +386,43 @@ sd_status sd_lm_head_probs(const void* hidden, const void* w_vocab, int32_t M,
  *   lse fp32 [M] out;  draft_tokens int32 [M] out
  *   anchor_tokens int32 [batch]  y_0 of every request
  *   w_c, e_c bf16 [V, r]  (r a multiple of 16, 16-byte aligned)
+ *   alpha    finite scale of the correction
+ *   vocab_bias fp32 [V] or NULL
  *   q_off    int32 [batch+1]; positions beyond max_draft_k (host bound,
  *            0..4096) are left untouched
  *   req_id, seed: as for sd_lm_head_probs
  *   workspace sd_markov_workspace_size(batch, V, max_draft_k) bytes
- * Errors: NULL -> SD_ERR_NULL; sizes out of range or unaligned tables ->
- * SD_ERR_SHAPE; M == 0 or max_draft_k == 0 -> SD_OK with nothing launched;
- * short or unaligned workspace -> SD_ERR_WORKSPACE.
+ * Errors: NULL -> SD_ERR_NULL; sizes out of range, unaligned tables or a
+ * non-finite alpha -> SD_ERR_SHAPE; M == 0 or max_draft_k == 0 -> SD_OK with
+ * nothing launched; short or unaligned workspace -> SD_ERR_WORKSPACE.
  * ------------------------------------------------------------------------ */
 size_t sd_markov_workspace_size(int32_t batch, int32_t V, int32_t max_draft_k);
 
 sd_status sd_markov_sample(float* logits, float* lse, int32_t* draft_tokens,
                            const int32_t* anchor_tokens, const void* w_c,
-                           const void* e_c, const int32_t* q_off, int32_t batch,
+                           const void* e_c, float alpha, const float* vocab_bias,
+                           const int32_t* q_off, int32_t batch,
                            int32_t M, int32_t V, int32_t r, int32_t max_draft_k,
                            const uint32_t* req_id, uint64_t seed,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * sd_log_prior_bias -- scaled, smoothed unigram log-prior for the fusion bias.
+ *
+ * Defined by: "DeLS-Spec", appendix on the unigram prior (corpus counts c(v)
+ * with additive smoothing, lambda = 1 by default; its log is a fixed
+ * vocabulary-level bias).
+ *   out[v] = scale * log((c(v) + lambda) / (sum_u c(u) + lambda V))
+ * computed in fp64, stored as fp32 (scale = -beta gives the fusion bias).
+ * One-time setup, one workgroup.
+ *
+ * Arguments
+ *   counts int64 [V] device (negative counts are read as 0); out fp32 [V]
+ *   lambda > 0 and finite; scale finite
+ * Errors: NULL -> SD_ERR_NULL; V < 1 or a bad lambda / scale -> SD_ERR_SHAPE.
+ * ------------------------------------------------------------------------ */
+sd_status sd_log_prior_bias(const int64_t* counts, int32_t V, double lambda, float scale,
+                            float* out, void* stream);
 
 /* ------------------------------------------------------------------------
  * sd_verify -- lossless speculative-sampling verification.

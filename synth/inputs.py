@@ -36,7 +36,7 @@ TAG_CTX, TAG_KB, TAG_VB, TAG_PERM, TAG_K, TAG_V = 1, 2, 3, 4, 5, 6
 TAG_Q, TAG_KBLK, TAG_VBLK, TAG_HID, TAG_W, TAG_TGT = 7, 8, 9, 10, 11, 12
 TAG_SIGMA, TAG_REQ, TAG_SEED, TAG_NOISE, TAG_TOK = 13, 14, 15, 16, 17
 TAG_SUMQ, TAG_SUMV, TAG_VMAP = 18, 19, 20
-TAG_MKW, TAG_MKE, TAG_ANCHOR = 21, 22, 23
+TAG_MKW, TAG_MKE, TAG_ANCHOR, TAG_COUNTS = 21, 22, 23, 24
 
 PAGES_PER_CHUNK = 256
 W_ROWS_PER_CHUNK = 4096
@@ -427,3 +427,13 @@ class StepInputs:
         """Seeded committed tokens y_0, one per request, in [0, V)."""
         c = self.cfg
         return _rng(c.seed, TAG_ANCHOR).integers(0, c.vocab, c.batch).astype(np.int32)
+
+    def unigram_counts(self) -> np.ndarray:
+        """Seeded stand-in for corpus token counts, int64 ``[V]``: a Zipf-like
+        profile (1e9 / rank^1.1) over a random permutation of the vocabulary,
+        with a tenth of the entries never seen (count 0)."""
+        c = self.cfg
+        rng = _rng(c.seed, TAG_COUNTS)
+        counts = (1e9 / np.arange(1, c.vocab + 1) ** 1.1).astype(np.int64)
+        counts[rng.random(c.vocab) < 0.1] = 0
+        return rng.permutation(counts)

@@ -4,14 +4,17 @@ Corrected logits and lse within 1e-5 of the oracle's fp64 values (a rank-r
 bf16 product with fp32 accumulation added to fp32 logits), draws exact except
 audited near-ties (Gumbel top-2 key gap < 1e-5); after a near-tie draw the
 rest of that request follows another chain and is not compared.  With
-W_c = 0 the draws must equal sd_lm_head_probs' own, exactly.
+W_c = 0 the draws must equal sd_lm_head_probs' own, exactly.  The
+"DeLS-Spec" fusion (alpha, unigram-prior bias) is compared the same way,
+with the device's bias as the oracle's input; the bias itself within 2e-6
+of the fp64 prior (fp32 rounding of values up to ~6).
 """
 import numpy as np
 import pytest
 import torch
 
 import block_drafting_sd_amd as sd
-from oracle import markov as omk, step as ostep
+from oracle import markov as omk
 from oracle.step import NEAR_TIE
 from synth import StepInputs, device as sdev
 from synth.configs import C1_32K, C2_128K
@@ -109,3 +112,42 @@ def test_markov_full_size_128k_shapes():
     ref = omk.markov_sample(base, b.q_off, anchor, w_c, e_c, inp.req_id, inp.philox_seed,
                             requests=reqs)
     _compare(got, ref, b.q_off, reqs, "markov 16 x 16 x 151936, r = 256")
+
+
+def test_log_prior_bias_matches_the_smoothed_prior():
+    # 151,936 Zipf-like counts with zeros; fp64 in the kernel, fp32 out
+    rng = np.random.default_rng(21)
+    V = 151936
+    counts = (1e7 / np.arange(1, V + 1) ** 1.1).astype(np.int64)
+    counts[rng.random(V) < 0.1] = 0
+    counts = rng.permutation(counts)
+    got = sd.sd_log_prior_bias(torch.from_numpy(counts).to(DEV), lam=1.0, scale=-0.3)
+    torch.cuda.synchronize()
+    ref = -0.3 * omk.unigram_log_prior(counts, 1.0)
+    err = np.abs(got.cpu().numpy() - ref).max()
+    log(f"log prior bias V={V}: max-abs {err:.2e} (values up to {np.abs(ref).max():.2f})")
+    assert err <= 2e-6
+
+
+@pytest.mark.parametrize("V,r", [(1001, 64), (4096, 256)])
+def test_fusion_small(V, r):
+    # "DeLS-Spec" fusion: alpha = 0.3, bias = -0.3 log p~_0 from the device
+    rng = np.random.default_rng(V)
+    d = np.array([16, 2, 7])
+    q_off = np.concatenate([[0], np.cumsum(d)]).astype(np.int32)
+    base = rng.normal(0, 2.0, (int(q_off[-1]), V)).astype(np.float32)
+    anchor = rng.integers(0, V, len(d)).astype(np.int32)
+    req_id = rng.integers(0, 2**32, len(d), dtype=np.uint64).astype(np.uint32)
+    w_c, e_c = _tables(V, r, V + r, scale=0.4)
+    counts = rng.integers(0, 1000, V).astype(np.int64)
+    bias = sd.sd_log_prior_bias(torch.from_numpy(counts).to(DEV), lam=1.0, scale=-0.3)
+    z = sdev.f32(base, DEV)
+    _, lse, tok = sd.sd_markov_sample(z, sdev.i32(anchor, DEV), sdev.bf16(w_c, DEV),
+                                      sdev.bf16(e_c, DEV), sdev.i32(q_off, DEV),
+                                      sdev.i32(req_id.view(np.int32), DEV), 31, max_draft_k=16,
+                                      alpha=0.3, vocab_bias=bias)
+    torch.cuda.synchronize()
+    got = (z.cpu().numpy(), lse.cpu().numpy(), tok.cpu().numpy())
+    ref = omk.markov_sample(base, q_off, anchor, w_c, e_c, req_id, 31, alpha=0.3,
+                            vocab_bias=bias.cpu().numpy())        # staged: the device's bias
+    _compare(got, ref, q_off, range(len(d)), f"fusion V={V} r={r}")
