@@ -151,3 +151,40 @@ def test_fusion_small(V, r):
     ref = omk.markov_sample(base, q_off, anchor, w_c, e_c, req_id, 31, alpha=0.3,
                             vocab_bias=bias.cpu().numpy())        # staged: the device's bias
     _compare(got, ref, q_off, range(len(d)), f"fusion V={V} r={r}")
+
+
+@pytest.mark.parametrize("batch,V,r,max_k", [
+    (33, 2000, 320, 16),     # three request tiles; r > 256: the k-chunk loop
+    (4, 7, 16, 16),          # tiny vocab (one partial chunk, scalar row ends); r = 16
+    (5, 3001, 48, 6),        # positions beyond max_draft_k stay untouched
+])
+def test_markov_edges(batch, V, r, max_k):
+    rng = np.random.default_rng(batch * 1000 + V + r)
+    d = rng.integers(0, 17, batch)
+    d[0] = 16
+    q_off = np.concatenate([[0], np.cumsum(d)]).astype(np.int32)
+    M = int(q_off[-1])
+    base = rng.normal(0, 2.0, (M, V)).astype(np.float32)
+    anchor = rng.integers(0, V, batch).astype(np.int32)
+    req_id = rng.integers(0, 2**32, batch, dtype=np.uint64).astype(np.uint32)
+    w_c, e_c = _tables(V, r, V * 7 + r, scale=0.3)
+    z = sdev.f32(base, DEV)
+    lse0 = torch.full((M,), -7.0, device=DEV)
+    tok0 = torch.full((M,), -3, dtype=torch.int32, device=DEV)
+    sd.sd_markov_sample(z, sdev.i32(anchor, DEV), sdev.bf16(w_c, DEV), sdev.bf16(e_c, DEV),
+                        sdev.i32(q_off, DEV), sdev.i32(req_id.view(np.int32), DEV), 5,
+                        max_draft_k=max_k, lse=lse0, draft_tokens=tok0)
+    torch.cuda.synchronize()
+    zg, lg, tg = z.cpu().numpy(), lse0.cpu().numpy(), tok0.cpu().numpy()
+    # rows past max_draft_k: untouched
+    pos = np.arange(M) - q_off[np.repeat(np.arange(batch), d)] + 1
+    beyond = pos > max_k
+    np.testing.assert_array_equal(zg[beyond], base[beyond])
+    assert np.all(lg[beyond] == -7.0) and np.all(tg[beyond] == -3)
+    # the oracle over the first max_k positions of every request
+    dk = np.minimum(d, max_k)
+    q_cut = np.concatenate([[0], np.cumsum(dk)]).astype(np.int32)
+    keep = ~beyond
+    ref = omk.markov_sample(base[keep], q_cut, anchor, w_c, e_c, req_id, 5)
+    _compare((zg[keep], lg[keep], tg[keep]), ref, q_cut, range(batch),
+             f"markov edges batch={batch} V={V} r={r} max_k={max_k}")
