@@ -148,6 +148,37 @@ def copy_calibration(gib: float):
     log(f"copy calibration: {n * 4} bytes read and written per copy, 3 copies")
 
 
+def measured_peaks(dev, read_gib: float = 4.0, mfma_iters: int = 20000, reps: int = 5):
+    """The GPU's own ceilings: a plain streaming read of ``read_gib`` GiB and
+    back-to-back independent bf16 MFMAs on every CU (library probes, HIP
+    events on the current stream; the best of ``reps`` launches)."""
+    import torch
+    import block_drafting_sd_amd as sd
+    buf = torch.empty(int(read_gib * (1 << 30)), dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    fsink = torch.zeros(4, dtype=torch.float32, device=dev)
+    sd.sd_probe_read(buf, sink)
+    sd.sd_probe_mfma(100, fsink)
+    torch.cuda.synchronize()
+    best_read = best_mfma = float("inf")
+    flops = 0
+    for _ in range(reps):
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record()
+        sd.sd_probe_read(buf, sink)
+        e1.record()
+        flops = sd.sd_probe_mfma(mfma_iters, fsink)
+        e2.record()
+        torch.cuda.synchronize()
+        best_read = min(best_read, e0.elapsed_time(e1))
+        best_mfma = min(best_mfma, e1.elapsed_time(e2))
+    del buf
+    return {"hbm_read_gbs": round(read_gib * (1 << 30) / (best_read * 1e-3) / 1e9, 1),
+            "mfma_bf16_tflops": round(flops / (best_mfma * 1e-3) / 1e12, 1),
+            "read_bytes": int(read_gib * (1 << 30)), "mfma_flops": flops,
+            "method": "sd_probe_read / sd_probe_mfma, best of %d launches" % reps}
+
+
 def bench_schedule(args):
     """ForeSpark's scheduler between verification and drafting: pre-draft
     estimation + joint schedule, then post-draft estimation + budget
@@ -233,6 +264,8 @@ def main():
                          "the rank-256 sequential correction, DeLS-Spec fusion (full prefix, "
                          "Markov local head of rank 256, alpha = beta = 0.3)")
     ap.add_argument("--greedy", action="store_true", help="temperature 0 on both sides")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured HBM-read and MFMA ceilings (library probes, untimed)")
     ap.add_argument("--schedule", action="store_true",
                     help="time the draft / verification scheduler instead of the step "
                          "(192 requests, K = 16, d_h = 4096, r = 256)")
@@ -342,6 +375,7 @@ def main():
     elapsed = time.perf_counter() - t0
     log(f"[bench] timed {args.steps} steps in {elapsed:.3f}s")
 
+    peaks = None if args.no_peaks else measured_peaks(dev)
     attn_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     lm_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
     mk_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
@@ -396,7 +430,9 @@ def main():
                      "traffic": measured_traffic() if args.path == "full" and args.config == 2
                      else None,
                      "algorithmic_bytes": attn_bytes,
-                     "avg_ms": round(float(attn_ms.mean()), 4)},
+                     "avg_ms": round(float(attn_ms.mean()), 4),
+                     "measured_peak": peaks and peaks["hbm_read_gbs"],
+                     "frac_of_measured": peaks and round(attn_gbs / peaks["hbm_read_gbs"], 4)},
         "breakdown_ms": {"attention": round(float(attn_ms.mean()), 4),
                          "lm_head": round(float(lm_ms.mean()), 4),
                          "markov": round(float(mk_ms.mean()), 4),
@@ -408,7 +444,9 @@ def main():
                                               ("verify", ver_ms))},
         "lm_head": {"tflops": round(lm_tflops, 1),
                     "frac_mfma_bf16": round(lm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "frac_of_measured_mfma": peaks and round(lm_tflops / peaks["mfma_bf16_tflops"], 4),
                     "w_hbm_gbs": round(v_draft * c.hidden * 2 / (float(lm_ms.mean()) * 1e-3) / 1e9, 1)},
+        "measured_peaks": peaks,
         "emitted_tokens_per_step_last": emitted,
         # one drafter attention layer per step is timed; projections for the
         # 3 attention modules of "H-Spec" and the 5 draft layers of "LongSpark"

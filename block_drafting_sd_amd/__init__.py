@@ -55,6 +55,29 @@ def sd_version() -> str:
     return load().sd_version().decode()
 
 
+def sd_probe_read(src, sink=None, stream=None):
+    """Stream every byte of the device tensor ``src`` with plain loads
+    (HBM read ceiling); see include/sd.h.  Returns the sink tensor."""
+    lib = load()
+    if not isinstance(src, torch.Tensor) or not src.is_contiguous():
+        raise TypeError("src must be a contiguous torch.Tensor")
+    if sink is None:
+        sink = torch.zeros(4, dtype=torch.int32, device=src.device)
+    check("sd_probe_read", lib.sd_probe_read(_ptr(src), src.numel() * src.element_size(),
+                                             _ptr(sink), _stream_handle(stream)))
+    return sink
+
+
+def sd_probe_mfma(iters: int, sink=None, device=None, stream=None):
+    """Back-to-back independent bf16 MFMAs on every CU (MFMA ceiling).
+    Returns the flop count of the launch."""
+    lib = load()
+    if sink is None:
+        sink = torch.zeros(4, dtype=torch.float32, device=device or "cuda")
+    check("sd_probe_mfma", lib.sd_probe_mfma(int(iters), _ptr(sink), _stream_handle(stream)))
+    return int(lib.sd_probe_mfma_flops(int(iters)))
+
+
 def draft_attn_workspace_size(batch, num_heads_q, num_heads_kv, head_dim, max_total_ctx,
                               split_tokens=0) -> int:
     return int(load().sd_draft_attn_workspace_size(batch, num_heads_q, num_heads_kv, head_dim,

@@ -21,6 +21,9 @@ _vp, _i32, _i64, _sz, _f32, _u64 = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t,
 SIGNATURES = {
     "sd_status_str": (C.c_char_p, [_i32]),
     "sd_version": (C.c_char_p, []),
+    "sd_probe_read": (_i32, [_vp, _sz, _vp, _vp]),
+    "sd_probe_mfma_flops": (_i64, [_i32]),
+    "sd_probe_mfma": (_i32, [_i32, _vp, _vp]),
     "sd_draft_attn_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i64, _i32]),
     "sd_draft_attn": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                              _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,

@@ -1,0 +1,73 @@
+// Measured ceilings for the roofline figures: what this GPU actually streams
+// from HBM with a plain read kernel, and what its matrix cores sustain on
+// independent bf16 MFMAs.  Neither is part of the method; the bench reports
+// its kernels against both these and the vendor figures.
+//
+//   probe_read   1,024 workgroups (four per CU) read the buffer in
+//                contiguous 16 KiB blocks with 16-byte loads, four in flight
+//                per thread; the words are folded into one value that is
+//                stored only if it equals a fixed key, so the loads cannot be
+//                dropped and (in practice) nothing is written.
+//   probe_mfma   every wave runs `iters` rounds of 8 independent
+//                v_mfma_f32_32x32x16_bf16 on register operands (no memory in
+//                the loop); the accumulators are folded and stored the same
+//                conditional way.
+#include "sd_common.h"
+#include "sd_internal.h"
+
+namespace sd {
+namespace {
+
+__global__ __launch_bounds__(256) void probe_read(const u32x4* src, size_t n16, uint32_t key, uint32_t* sink) {
+  // each workgroup step reads one contiguous 16 KiB block: four 4 KiB rows of
+  // 256 x 16 bytes, all four loads of a thread in flight together
+  const size_t stride = static_cast<size_t>(gridDim.x) * 1024;
+  uint32_t acc = 0;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * 1024 + threadIdx.x; i < n16; i += stride) {
+    const u32x4 a = src[i];
+    const u32x4 b = i + 256 < n16 ? src[i + 256] : a;
+    const u32x4 c = i + 512 < n16 ? src[i + 512] : a;
+    const u32x4 d = i + 768 < n16 ? src[i + 768] : a;
+    acc ^= a[0] ^ a[1] ^ a[2] ^ a[3] ^ b[0] ^ b[1] ^ b[2] ^ b[3];
+    acc ^= c[0] ^ c[1] ^ c[2] ^ c[3] ^ d[0] ^ d[1] ^ d[2] ^ d[3];
+  }
+  if (acc == key) sink[0] = acc;
+}
+
+__global__ __launch_bounds__(256) void probe_mfma(int iters, uint32_t seed, float* sink) {
+  const uint32_t s = seed ^ (threadIdx.x * 0x9E3779B9u);
+  const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{s & 0x3f803f80u, s, 0x3c003c00u, s >> 3});
+  const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{0x3c003c00u, s >> 5, s & 0x3f003f00u, 0x3c003c00u});
+  f32x16 acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = f32x16{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] = mfma_32x32x16(a, b, acc[t]);
+  }
+  float x = 0.f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) x += acc[t][e];
+  if (x == -1.2345e30f) sink[0] = x;
+}
+
+}  // namespace
+
+hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s) {
+  const u32x4* p = static_cast<const u32x4*>(src);
+  size_t n16 = bytes / 16;
+  uint32_t key = 0x5D00BEEFu;
+  void* args[] = {&p, &n16, &key, &sink};
+  return hipLaunchKernel(reinterpret_cast<const void*>(probe_read), dim3(1024), dim3(256), args, 0, s);
+}
+
+hipError_t launch_probe_mfma(int iters, float* sink, hipStream_t s) {
+  uint32_t seed = 0x12345u;
+  void* args[] = {&iters, &seed, &sink};
+  // two workgroups of 4 waves per CU: 2 waves per SIMD
+  return hipLaunchKernel(reinterpret_cast<const void*>(probe_mfma), dim3(256 * 2), dim3(256), args, 0, s);
+}
+
+}  // namespace sd

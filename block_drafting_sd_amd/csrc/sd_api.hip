@@ -90,6 +90,24 @@ const char* sd_status_str(sd_status s) {
 
 const char* sd_version(void) { return "0.1.0"; }
 
+sd_status sd_probe_read(const void* src, size_t bytes, void* sink, void* stream) {
+  if (!src || !sink) return SD_ERR_NULL;
+  if (bytes < 16 || !aligned16(src)) return SD_ERR_SHAPE;
+  return from_hip(sd::launch_probe_read(src, bytes, static_cast<uint32_t*>(sink),
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int64_t sd_probe_mfma_flops(int32_t iters) {
+  // 512 workgroups x 4 waves x iters x 8 MFMAs x (2 x 32 x 32 x 16) flops
+  return iters < 1 ? 0 : static_cast<int64_t>(512) * 4 * iters * 8 * 2 * 32 * 32 * 16;
+}
+
+sd_status sd_probe_mfma(int32_t iters, void* sink, void* stream) {
+  if (!sink) return SD_ERR_NULL;
+  if (iters < 1 || iters > (1 << 24)) return SD_ERR_SHAPE;
+  return from_hip(sd::launch_probe_mfma(iters, static_cast<float*>(sink), static_cast<hipStream_t>(stream)));
+}
+
 size_t sd_draft_attn_workspace_size(int32_t batch, int32_t num_heads_q, int32_t num_heads_kv,
                                     int32_t head_dim, int64_t max_total_ctx, int32_t split_tokens) {
   (void)num_heads_q;

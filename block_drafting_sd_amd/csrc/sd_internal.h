@@ -176,6 +176,8 @@ inline int32_t markov_cell_stride(int32_t batch) { return (batch + 63) / 64 * 64
 int32_t markov_chunks(int32_t V);   // 128-row vocab chunks
 int32_t markov_parts(int32_t V);    // partial statistics per (position, request)
 hipError_t launch_markov(const MarkovArgs& a, hipStream_t s);
+hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
+hipError_t launch_probe_mfma(int iters, float* sink, hipStream_t s);
 hipError_t launch_log_prior_bias(const int64_t* counts, int V, double lam, float scale, float* out,
                                  hipStream_t s);
 

@@ -74,6 +74,23 @@ const char* sd_status_str(sd_status s);
 const char* sd_version(void);
 
 /* ------------------------------------------------------------------------
+ * Measured ceilings (not part of the method; for the roofline figures).
+ *
+ * sd_probe_read  streams `bytes` (>= 16) of device memory at `src` (16-byte
+ *   aligned) with plain 16-byte loads, 1,024 workgroups each reading
+ *   contiguous 16 KiB blocks, and writes nothing (`sink`: a device word that is only written if the XOR of all
+ *   words equals a fixed key).  HBM read rate = bytes / kernel time.
+ * sd_probe_mfma  512 workgroups of 4 waves each run `iters` (1..2^24)
+ *   rounds of 8 independent bf16 MFMA 32x32x16 on register operands;
+ *   sd_probe_mfma_flops(iters) is the flop count of one launch (0 if
+ *   iters < 1).  `sink`: a device float written only for one impossible sum.
+ * Errors: NULL -> SD_ERR_NULL; bad sizes or alignment -> SD_ERR_SHAPE.
+ * ------------------------------------------------------------------------ */
+sd_status sd_probe_read(const void* src, size_t bytes, void* sink, void* stream);
+int64_t sd_probe_mfma_flops(int32_t iters);
+sd_status sd_probe_mfma(int32_t iters, void* sink, void* stream);
+
+/* ------------------------------------------------------------------------
  * sd_draft_attn -- draft-block attention over the target's paged KV cache.
  *
  * Defined by: "ForeSpark: Joint draft and verification budget scheduling for

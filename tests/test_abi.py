@@ -240,3 +240,14 @@ def test_markov_workspace_size(lib):
 ])
 def test_log_prior_bias_validation(lib, args, status):
     assert lib.sd_log_prior_bias(*args, None) == status
+
+
+def test_probe_validation(lib):
+    assert lib.sd_probe_read(None, 64, FAKE, None) == 1
+    assert lib.sd_probe_read(FAKE, 64, None, None) == 1
+    assert lib.sd_probe_read(FAKE, 8, FAKE, None) == 2
+    assert lib.sd_probe_read(ODD, 64, FAKE, None) == 2
+    assert lib.sd_probe_mfma(0, FAKE, None) == 2
+    assert lib.sd_probe_mfma(10, None, None) == 1
+    assert lib.sd_probe_mfma_flops(1) == 512 * 4 * 8 * 2 * 32 * 32 * 16
+    assert lib.sd_probe_mfma_flops(0) == 0
