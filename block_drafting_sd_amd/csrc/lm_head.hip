@@ -3,17 +3,20 @@
 // and App. A.1, Fig. 6: the frozen target vocabulary head produces every
 // slot's base logits in parallel and each slot is sampled independently).
 //
-// lm_gemm: one workgroup (4 waves, 2 x 2) computes a 128-vocab x 256-row
-// tile of logits^T = W * hidden^T with MFMA 32x32x16 bf16 (fp32
+// lm_gemm<WV>: one workgroup (2 x WV waves) computes a 64 WV-vocab x 256-row
+// tile (128 x 256 with 4 waves for one row tile; 256 x 256 with 8 waves when
+// there are several) of logits^T = W * hidden^T with MFMA 32x32x16 bf16 (fp32
 // accumulation); each wave owns a 64 x 128 sub-tile (8 accumulator tiles).
-// Both operands are H-contiguous.  They stream through a ring of kNS LDS
-// stages of 32 hidden dims (8 KiB of W, 16 KiB of hidden per stage), filled by
+// Both operands are H-contiguous.  They stream through a ring of LDS stages
+// of 32 hidden dims (W rows, then 16 KiB of hidden rows, per stage), filled by
 // direct-to-LDS loads: each 1 KiB wave load covers 16 rows x 64 bytes, so
 // global reads stay coalesced, and rows are stored with a 16-byte-chunk XOR
 // swizzle so the MFMA operand reads (32 rows, one chunk) are conflict-free.
-// The ring is small enough (72 KiB) for two workgroups to share a CU: each
+// With 4 waves the ring (3 x 24 KiB) lets two workgroups share a CU: each
 // SIMD then runs two waves whose barriers are independent, so one
-// workgroup's MFMAs cover the other's waits for loads and its epilogue.  At up
+// workgroup's MFMAs cover the other's waits for loads and its epilogue; with
+// 8 waves one workgroup (4 x 32 KiB) fills the CU with the same two waves per
+// SIMD and re-reads the hidden rows half as often.  At up
 // to 256 draft rows the whole W (1.2 GB) is read from HBM exactly once.
 // Tiles are ordered so that all row tiles of one vocab tile, and a compact
 // block of vocab tiles, run together on one XCD (blockIdx % 8 picks the XCD),
@@ -33,16 +36,33 @@
 namespace sd {
 namespace {
 
-constexpr int kThreads = 256;                       // every kernel: 4 waves
-constexpr int kNS = 3;                              // LDS stages
-constexpr int kWBytes = kLmBV * kLmBK * 2;          // W rows of one stage: 8 KiB
-constexpr int kHBytes = kLmBM * kLmBK * 2;          // hidden rows of one stage: 16 KiB
-constexpr int kStageBytes = kWBytes + kHBytes;      // 24 KiB; 3 stages let 2 workgroups share a CU
-constexpr int kWLoads = kWBytes / 1024 / 4;         // direct-to-LDS loads per wave per stage
-constexpr int kHLoads = kHBytes / 1024 / 4;
-constexpr int kLoadsPerWave = kWLoads + kHLoads;
-static_assert(kLmBV == 128 && kLmBM == 256 && kLmBK == 32, "stage layout assumes 128 x 256 tiles of 32 dims");
-static_assert(kWLoads == 2 && kHLoads == 4, "per wave: 2 W loads, 4 hidden loads");
+constexpr int kThreads = 256;                       // lm_row_reduce: 4 waves
+
+// Workgroup shape by the number of waves along the vocabulary (WV): 2 x WV
+// waves, each owning 64 vocab x 128 rows; a tile is 64 WV vocab x 256 rows.
+//   WV = 2: 128 x 256 tiles, 4 waves, 24 KiB stages, 3 stages: two
+//           workgroups per CU.
+//   WV = 4: 256 x 256 tiles, 8 waves, 32 KiB stages, 4 stages: one
+//           workgroup per CU with the same waves per SIMD, a third less
+//           operand traffic per output (hidden is re-read per vocab tile)
+//           and one more stage of lookahead.
+template <int WV>
+struct LmTile {
+  static constexpr int Waves = 2 * WV;
+  static constexpr int Threads = 64 * Waves;
+  static constexpr int BV = 64 * WV;                      // vocab rows per tile
+  static constexpr int NS = WV == 2 ? 3 : 4;              // LDS stages
+  static constexpr int WBytes = BV * kLmBK * 2;           // W rows of one stage
+  static constexpr int HBytes = kLmBM * kLmBK * 2;        // hidden rows of one stage: 16 KiB
+  static constexpr int StageBytes = WBytes + HBytes;
+  static constexpr int WLoads = WBytes / 1024 / Waves;    // direct-to-LDS loads per wave per stage
+  static constexpr int HLoads = HBytes / 1024 / Waves;
+  static constexpr int Loads = WLoads + HLoads;
+};
+static_assert(kLmBM == 256 && kLmBK == 32, "stage layout assumes 256-row tiles of 32 dims");
+static_assert(LmTile<2>::BV == kLmBV, "the workspace is sized for the 128-vocab tiles");
+static_assert(LmTile<2>::WLoads == 2 && LmTile<2>::HLoads == 4 && LmTile<4>::WLoads == 2 &&
+              LmTile<4>::HLoads == 2, "loads per wave per stage");
 
 // 16-byte chunk c (of 4) of row r of a staged tile sits at byte
 // 64 r + 16 (c ^ swz(r)): eight consecutive rows of one chunk then fall in
@@ -67,21 +87,25 @@ __device__ __forceinline__ void row_owner(const LmArgs& a, int m, uint32_t& rid,
   pos = static_cast<uint32_t>(m - a.q_off[lo] + 1);
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int WV>
+__global__ __launch_bounds__(LmTile<WV>::Threads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void lm_gemm(LmArgs a) {
+  using T = LmTile<WV>;
+  constexpr int kNS = T::NS, kStageBytes = T::StageBytes, kWBytes = T::WBytes;
+  constexpr int kWLoads = T::WLoads, kHLoads = T::HLoads, kLoadsPerWave = T::Loads;
   __shared__ __attribute__((aligned(1024))) char smem[kNS * kStageBytes];
   const int P = blockIdx.x;
   const int xcd = P & 7, slot = P >> 3;
   const int vt = (slot / a.n_mt) * 8 + xcd;
   const int mt = slot % a.n_mt;
   if (vt >= a.n_vt) return;
-  const int v0 = vt * kLmBV, m0 = mt * kLmBM;
+  const int v0 = vt * T::BV, m0 = mt * kLmBM;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wv = wave & 1, wm = wave >> 1, h = lane >> 5;
+  const int wv = wave % WV, wm = wave / WV, h = lane >> 5;
 
   // ------------------------------------------------ direct-to-LDS loads
   // Wave w fetches W rows 32 w .. 32 w + 31 (loads q = 2 w, 2 w + 1) and
-  // hidden rows 64 w .. 64 w + 63 (loads q = 4 w .. 4 w + 3); load q covers
+  // its share of the hidden rows (loads q = HLoads w ..); load q covers
   // rows 16 q .. 16 q + 15 of its tile and lane l fetches chunk
   // (l & 3) ^ swz(row) of row 16 q + l / 4.  Rows past V (or M) read the last
   // row instead and are never stored.
@@ -157,10 +181,10 @@ void lm_gemm(LmArgs a) {
   //                 row    m0 + 128 wm + 32 tm + lane%32
   // Each lane holds 32 vocab entries of one row per row tile: it stores them
   // and folds them into the row's (max, sum of exp, best Gumbel-max
-  // candidate) over this vocab tile; the two vocab waves (wv) merge through
+  // candidate) over this vocab tile; the WV vocab waves (wv) merge through
   // LDS (the ring is free once every wave is past the loop).
   __syncthreads();
-  float4* red = reinterpret_cast<float4*>(smem);   // [wm][tm][32], written by wv = 1
+  float4* red = reinterpret_cast<float4*>(smem);   // [wv][wm][tm][32]
   const bool vec_ok = (a.V & 3) == 0;
   static_for<0, 4>([&](auto TM) {
     const int m = m0 + 128 * wm + 32 * TM + rr;
@@ -220,16 +244,20 @@ void lm_gemm(LmArgs a) {
       const int oi = xor_shuffle(best.idx, 32);
       if (better(ok, oi, best.key, best.idx)) best = Cand{ok, oi};
     }
-    float4* slot4 = red + (wm * 4 + TM) * 32 + rr;
-    if (wv == 1 && h == 0) *slot4 = make_float4(mx, se, best.key, __int_as_float(best.idx));
+    if (wv != 0 && h == 0)
+      red[((wv * 2 + wm) * 4 + TM) * 32 + rr] = make_float4(mx, se, best.key, __int_as_float(best.idx));
     __syncthreads();
     if (wv == 0 && h == 0 && mok) {
-      const float4 o = *slot4;
-      const int oi = __float_as_int(o.w);
-      const float nmx = fmaxf(mx, o.x);
-      se = se * __builtin_amdgcn_exp2f((mx - nmx) * kLog2e) + o.y * __builtin_amdgcn_exp2f((o.x - nmx) * kLog2e);
-      if (better(o.z, oi, best.key, best.idx)) best = Cand{o.z, oi};
-      a.part[static_cast<size_t>(m) * a.n_vt + vt] = make_float4(nmx, se, best.key, __int_as_float(best.idx));
+#pragma unroll
+      for (int o2 = 1; o2 < WV; ++o2) {
+        const float4 o = red[((o2 * 2 + wm) * 4 + TM) * 32 + rr];
+        const int oi = __float_as_int(o.w);
+        const float nmx = fmaxf(mx, o.x);
+        se = se * __builtin_amdgcn_exp2f((mx - nmx) * kLog2e) + o.y * __builtin_amdgcn_exp2f((o.x - nmx) * kLog2e);
+        mx = nmx;
+        if (better(o.z, oi, best.key, best.idx)) best = Cand{o.z, oi};
+      }
+      a.part[static_cast<size_t>(m) * a.n_vt + vt] = make_float4(mx, se, best.key, __int_as_float(best.idx));
     }
   });
 }
@@ -262,10 +290,20 @@ __global__ __launch_bounds__(kThreads) void lm_row_reduce(LmArgs a) {
 
 }  // namespace
 
+template <int WV>
+hipError_t launch_gemm(LmArgs& b, hipStream_t s) {
+  b.n_vt = (b.V + LmTile<WV>::BV - 1) / LmTile<WV>::BV;
+  const int slots = (b.n_vt + 7) / 8 * b.n_mt;
+  return launch_kernel(lm_gemm<WV>, dim3(slots * 8), dim3(LmTile<WV>::Threads), s, b);
+}
+
 hipError_t launch_lm_head(const LmArgs& a, hipStream_t s) {
-  const int slots = (a.n_vt + 7) / 8 * a.n_mt;
-  hipError_t e = launch_kernel(lm_gemm, dim3(slots * 8), dim3(kThreads), s, a);
-  if (e == hipSuccess) e = launch_kernel(lm_row_reduce, dim3(a.M), dim3(kThreads), s, a);
+  // several row tiles (M > 256): 256-vocab tiles (measured ~4% faster at
+  // M = 1024); one row tile: 128-vocab tiles, whose 1,187 tiles at V =
+  // 151,936 spread over twice as many resident workgroups
+  LmArgs b = a;
+  hipError_t e = a.n_mt > 1 ? launch_gemm<4>(b, s) : launch_gemm<2>(b, s);
+  if (e == hipSuccess) e = launch_kernel(lm_row_reduce, dim3(b.M), dim3(kThreads), s, b);
   return e;
 }
 
