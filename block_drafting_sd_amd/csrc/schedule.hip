@@ -14,14 +14,14 @@
 //                    R(d) = Reward(d, d), one thread per (request, d).
 //   sched_joint      one workgroup: the upper concave envelope F of every
 //                    reward curve (monotone chain, O(K) per request) and the
-//                    survival scores g_d = F(d) - F(d-1); a bitonic sort of all
-//                    scores in LDS; the bucket-pair search of eq. (4) against
+//                    survival scores g_d = F(d) - F(d-1); a stable merge of
+//                    the requests' (already sorted) score runs in LDS; the bucket-pair search of eq. (4) against
 //                    the latency tables; the draft schedule d_i (the owners of
 //                    the top k scores), q_off and the budget B.
 //   sched_post_logit one wavefront per draft row: p = sigmoid((w . [h; s] + c) /
 //                    theta_j), s = (W_s h) * E_pred(previous token) (eq. (5)).
 //   sched_budget     one workgroup: S^_j = prod_{t<=j} p_t per request, a
-//                    bitonic sort of all rows, the top B rows -> verify prefix
+//                    stable merge of the requests' rows, the top B rows -> verify prefix
 //                    b_i and t_off (sec. 4.4).
 //
 // Equal scores are ordered by (request, position), which keeps every
@@ -142,40 +142,46 @@ __device__ __forceinline__ bool before(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-// Bitonic sort of P (a power of two) (value, index) pairs in LDS.  Thread t
-// takes pairs t, t + NT, ...; for strides up to 64 the pairs of 64
-// consecutive t -- one wavefront -- stay inside one 128-element block, which
-// no other wavefront touches, so those stages need no workgroup barrier (a
-// wavefront's LDS accesses are processed in order); a barrier precedes every
-// stage with a larger stride and the first small-stride stage after it.
-template <int NT>
-__device__ void bitonic_sort(float* v, int* ix, int P) {
-  static_assert(NT % 64 == 0, "whole wavefronts");
-  bool wide_before = true;
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const bool wide = stride > 64;
-      if (wide || wide_before) __syncthreads();
-      else asm volatile("" ::: "memory");
-      wide_before = wide;
-      for (int t = threadIdx.x; t < P / 2; t += NT) {
-        const int lo = 2 * t - (t & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;   // this block sorts in "before" order
-        const bool swap = up ? before(v[hi], ix[hi], v[lo], ix[lo])
-                             : before(v[lo], ix[lo], v[hi], ix[hi]);
-        if (swap) {
-          const float tv = v[lo];
-          v[lo] = v[hi];
-          v[hi] = tv;
-          const int ti = ix[lo];
-          ix[lo] = ix[hi];
-          ix[hi] = ti;
-        }
+// Stable merge of sorted runs in LDS.  Request i's entries occupy positions
+// bounds(i) .. bounds(i + 1) - 1 and are already in "before" order (values
+// non-increasing along a request, original indices increasing); own[p] is
+// the request of position p.  Round r merges neighbouring groups of 2^r
+// requests: an element's new position is its rank in its own group plus the
+// number of elements of the partner group that go before it, found by binary
+// search -- a partner element comes first if its value is larger (partner on
+// the right: its original indices are all larger) or not smaller (partner on
+// the left).  ceil(log2 n) rounds, one barrier each; (v, ix) hold the result.
+template <int NT, typename Bounds>
+__device__ void merge_runs(float*& v, int*& ix, float*& v2, int*& ix2, int total, int n,
+                           const int* own, Bounds bounds) {
+  for (int w = 1; w < n; w <<= 1) {
+    for (int p = threadIdx.x; p < total; p += NT) {
+      const int i = own[p];
+      const int g0 = (i / (2 * w)) * (2 * w);
+      const int lo = bounds(g0), mid = bounds(min(g0 + w, n)), hi = bounds(min(g0 + 2 * w, n));
+      const float x = v[p];
+      const bool left = p < mid;
+      int a = left ? mid : lo, c = left ? hi : mid;   // binary search in the partner run
+      while (a < c) {                                 // first partner entry that goes after x
+        const int m = (a + c) >> 1;
+        const bool first = left ? v[m] > x : v[m] >= x;
+        if (first) a = m + 1;
+        else c = m;
+      }
+      const int np = lo + (left ? p - lo + (a - mid) : p - mid + (a - lo));
+      if (np >= 0 && np < total) {
+        v2[np] = x;
+        ix2[np] = ix[p];
       }
     }
+    __syncthreads();
+    float* tv = v;
+    v = v2;
+    v2 = tv;
+    int* ti = ix;
+    ix = ix2;
+    ix2 = ti;
   }
-  __syncthreads();
 }
 
 // Inclusive prefix sum of x[0..P) in place (P <= 4 * NT), Hillis-Steele over
@@ -206,8 +212,9 @@ constexpr int kSchedThreads = 1024;
 
 // ------------------------------------------------------------ joint schedule
 __global__ __launch_bounds__(kSchedThreads) void sched_joint(SchedArgs a) {
-  __shared__ float s_v[kSchedMaxEntries];
-  __shared__ int s_i[kSchedMaxEntries];
+  __shared__ float s_va[kSchedMaxEntries], s_vb[kSchedMaxEntries];
+  __shared__ int s_ia[kSchedMaxEntries], s_ib[kSchedMaxEntries];
+  __shared__ int s_own[kSchedMaxEntries];
   __shared__ float s_tmp[kSchedThreads];
   __shared__ int s_d[kSchedMaxRequests];
   __shared__ float s_best[kSchedThreads];
@@ -217,8 +224,10 @@ __global__ __launch_bounds__(kSchedThreads) void sched_joint(SchedArgs a) {
   const int tid = threadIdx.x;
   const int n = a.n, K = a.K;
   const int E = n * K;
-  int P = 1;
-  while (P < E) P <<= 1;
+  float* s_v = s_va;
+  int* s_i = s_ia;
+  float* s_v2 = s_vb;
+  int* s_i2 = s_ib;
 
   // reward curves (from sched_rewards) into LDS; then the upper concave
   // envelope and the scores, one thread per request
@@ -253,13 +262,12 @@ __global__ __launch_bounds__(kSchedThreads) void sched_joint(SchedArgs a) {
       a.scores[static_cast<size_t>(i) * K + d - 1] = g;
       s_v[i * K + d - 1] = g;
       s_i[i * K + d - 1] = i * K + d - 1;
+      s_own[i * K + d - 1] = i;
     }
   }
-  for (int e = E + tid; e < P; e += kSchedThreads) {
-    s_v[e] = -FLT_MAX;
-    s_i[e] = 0x7fffffff;
-  }
-  bitonic_sort<kSchedThreads>(s_v, s_i, P);
+  __syncthreads();
+  // every request's scores are non-increasing: merge the n sorted runs
+  merge_runs<kSchedThreads>(s_v, s_i, s_v2, s_i2, E, n, s_own, [K](int i) { return i * K; });
 
   // count of positive scores, then prefix sums of the sorted scores
   int pos = 0;
@@ -273,8 +281,6 @@ __global__ __launch_bounds__(kSchedThreads) void sched_joint(SchedArgs a) {
   const int n_pos = static_cast<int>(s_tmp[0]);
   __syncthreads();
   // prefix[B] = sum of the top B scores: s_v becomes the inclusive prefix sum
-  for (int e = E + tid; e < P; e += kSchedThreads) s_v[e] = 0.f;
-  __syncthreads();
   prefix_sum<kSchedThreads>(s_v, E, s_tmp);
 
   // eq. (4): one candidate per (draft bucket, verify bucket) pair
@@ -374,8 +380,8 @@ __global__ __launch_bounds__(64) void sched_post_logit(SchedPostArgs a) {
 }
 
 __global__ __launch_bounds__(kSchedThreads) void sched_budget(SchedPostArgs a) {
-  __shared__ float s_v[kSchedMaxEntries];
-  __shared__ int s_i[kSchedMaxEntries];
+  __shared__ float s_va[kSchedMaxEntries], s_vb[kSchedMaxEntries];
+  __shared__ int s_ia[kSchedMaxEntries], s_ib[kSchedMaxEntries];
   __shared__ int s_own[kSchedMaxEntries];
   __shared__ int s_q[kSchedMaxRequests + 1];
   __shared__ int s_b[kSchedMaxRequests];
@@ -384,8 +390,10 @@ __global__ __launch_bounds__(kSchedThreads) void sched_budget(SchedPostArgs a) {
   for (int i = tid; i <= n; i += kSchedThreads) s_q[i] = a.q_off[i];
   __syncthreads();
   const int total = clampi(s_q[n], 0, a.M);
-  int P = 1;
-  while (P < total) P <<= 1;
+  float* s_v = s_va;
+  int* s_i = s_ia;
+  float* s_v2 = s_vb;
+  int* s_i2 = s_ib;
   for (int m = tid; m < total; m += kSchedThreads) {
     s_v[m] = a.prob[m];
     s_own[m] = 0;
@@ -403,16 +411,15 @@ __global__ __launch_bounds__(kSchedThreads) void sched_budget(SchedPostArgs a) {
     }
   }
   __syncthreads();
-  for (int m = tid; m < P; m += kSchedThreads) {
-    if (m < total) {
-      a.survival[m] = s_v[m];
-      s_i[m] = m;
-    } else {
-      s_v[m] = -FLT_MAX;
-      s_i[m] = 0x7fffffff;
-    }
+  for (int m = tid; m < total; m += kSchedThreads) {
+    a.survival[m] = s_v[m];
+    s_i[m] = m;
   }
-  bitonic_sort<kSchedThreads>(s_v, s_i, P);
+  __syncthreads();
+  // survival is non-increasing along each draft: merge the n sorted runs
+  // (request i's rows are positions s_q[i] .. s_q[i + 1] - 1, clamped)
+  merge_runs<kSchedThreads>(s_v, s_i, s_v2, s_i2, total, n, s_own,
+                            [&](int i) { return clampi(s_q[i], 0, total); });
   const int B = clampi(a.budget[0], 0, total);
   for (int i = tid; i < n; i += kSchedThreads) s_b[i] = 0;
   __syncthreads();
