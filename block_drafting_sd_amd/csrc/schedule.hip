@@ -2,8 +2,9 @@
 // sec. 4.2-4.4), entirely on the device so that the host never waits:
 //
 //   sched_gemm       C = A1 B1^T (+ A2 B2^T), bf16 in, fp32 out, MFMA 32x32x16
-//                    (four wavefronts split K per 32 x 32 tile); epilogue:
-//                    + bias, SiLU.
+//                    (four wavefronts split K per 32 x 32 tile, and K split
+//                    across workgroups for the few-row pre-draft product,
+//                    finished by sched_gemm_reduce); epilogue: + bias, SiLU.
 //                    Serves the pre-draft estimator's hidden layer
 //                    u = SiLU(W_c c + W_e e + b) (eq. (2)) and the post-draft
 //                    selector projection W_s h (eq. (5)).
@@ -39,11 +40,14 @@ __device__ __forceinline__ float sigmoidf(float x) { return 1.f / (1.f + expf(-x
 // ------------------------------------------------------------------ GEMM
 // One workgroup (4 wavefronts) computes a 32 x 32 tile of C[M][N] =
 // A1 B1^T (+ A2 B2^T) with A [M][K], B [N][K] row-major bf16, K a multiple of
-// 16; the wavefronts take interleaved 16-dim steps of K and their partial
-// tiles are summed through LDS.  Lane l feeds row l % 32 of the A (and B)
-// tile with dims 8 (l / 32) .. +8 of a step; element i of a partial tile is
+// 16, over its share (blockIdx.z of ksplit) of the 16-dim steps of both
+// products; the wavefronts take interleaved steps and their partial tiles
+// are summed through LDS.  Lane l feeds row l % 32 of the A (and B) tile with
+// dims 8 (l / 32) .. +8 of a step; element i of a partial tile is
 // C[row 8 (i/4) + 4 (l/32) + i%4][col l % 32].  Rows past M (N) load the last
-// row and are not stored.
+// row and are not stored.  With one split the epilogue adds the bias and
+// applies SiLU; with several, raw sums go to part[z] and sched_gemm_reduce
+// finishes (few rows: the K splits are what fill the GPU).
 constexpr int kGemmWaves = 4;
 
 __global__ __launch_bounds__(64 * kGemmWaves) void sched_gemm(SchedGemmArgs a) {
@@ -55,25 +59,27 @@ __global__ __launch_bounds__(64 * kGemmWaves) void sched_gemm(SchedGemmArgs a) {
   const size_t rb = static_cast<size_t>(min(n0 + rr, a.N - 1)) * a.K + 8 * h;
   f32x16 acc = {};
   const int steps = a.K / 16;
-  for (int pass = 0; pass < (a.a2 ? 2 : 1); ++pass) {
-    const uint16_t* A = pass ? a.a2 : a.a1;
-    const uint16_t* B = pass ? a.b2 : a.b1;
-    int s0 = wave;
-    for (; s0 + 3 * kGemmWaves < steps; s0 += 4 * kGemmWaves) {
-      bf16x8 x[4], y[4];
+  const int total = steps * (a.a2 ? 2 : 1);
+  const int per = (total + a.ksplit - 1) / a.ksplit;
+  const int sb = static_cast<int>(blockIdx.z) * per, se = min(total, sb + per);
+  auto opnd = [&](int g, bf16x8& x, bf16x8& y) {
+    const bool second = g >= steps;
+    const size_t k = static_cast<size_t>(second ? g - steps : g) * 16;
+    x = load_bf16x8((second ? a.a2 : a.a1) + ra + k);
+    y = load_bf16x8((second ? a.b2 : a.b1) + rb + k);
+  };
+  int s = sb + wave;
+  for (; s + 3 * kGemmWaves < se; s += 4 * kGemmWaves) {
+    bf16x8 x[4], y[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const size_t k = static_cast<size_t>(s0 + u * kGemmWaves) * 16;
-        x[u] = load_bf16x8(A + ra + k);
-        y[u] = load_bf16x8(B + rb + k);
-      }
+    for (int u = 0; u < 4; ++u) opnd(s + u * kGemmWaves, x[u], y[u]);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc = mfma_32x32x16(x[u], y[u], acc);
-    }
-    for (; s0 < steps; s0 += kGemmWaves) {
-      const size_t k = static_cast<size_t>(s0) * 16;
-      acc = mfma_32x32x16(load_bf16x8(A + ra + k), load_bf16x8(B + rb + k), acc);
-    }
+    for (int u = 0; u < 4; ++u) acc = mfma_32x32x16(x[u], y[u], acc);
+  }
+  for (; s < se; s += kGemmWaves) {
+    bf16x8 x, y;
+    opnd(s, x, y);
+    acc = mfma_32x32x16(x, y, acc);
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) red[wave][(8 * (i >> 2) + 4 * h + (i & 3)) * 33 + rr] = acc[i];
@@ -84,11 +90,27 @@ __global__ __launch_bounds__(64 * kGemmWaves) void sched_gemm(SchedGemmArgs a) {
       float v = 0.f;
 #pragma unroll
       for (int w = 0; w < kGemmWaves; ++w) v += red[w][(e / 32) * 33 + e % 32];
-      if (a.bias) v += a.bias[col];
-      if (a.silu) v = v * sigmoidf(v);
-      a.c[static_cast<size_t>(row) * a.N + col] = v;
+      if (a.ksplit > 1) {
+        a.part[(static_cast<size_t>(blockIdx.z) * a.M + row) * a.N + col] = v;
+      } else {
+        if (a.bias) v += a.bias[col];
+        if (a.silu) v = v * sigmoidf(v);
+        a.c[static_cast<size_t>(row) * a.N + col] = v;
+      }
     }
   }
+}
+
+// c = act(sum_z part[z] + bias), one thread per element.
+__global__ __launch_bounds__(256) void sched_gemm_reduce(SchedGemmArgs a) {
+  const size_t e = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  const size_t mn = static_cast<size_t>(a.M) * a.N;
+  if (e >= mn) return;
+  float v = 0.f;
+  for (int z = 0; z < a.ksplit; ++z) v += a.part[z * mn + e];
+  if (a.bias) v += a.bias[e % a.N];
+  if (a.silu) v = v * sigmoidf(v);
+  a.c[e] = v;
 }
 
 // z[i][e] = scale[e] * (u[i] . W_o[e] + b_o[e]) + bias[e]; one wavefront per
@@ -442,7 +464,13 @@ __global__ __launch_bounds__(kSchedThreads) void sched_budget(SchedPostArgs a) {
 }  // namespace
 
 hipError_t launch_sched_gemm(const SchedGemmArgs& g, hipStream_t s) {
-  return launch_kernel(sched_gemm, dim3((g.M + 31) / 32, (g.N + 31) / 32), dim3(64 * kGemmWaves), s, g);
+  hipError_t e = launch_kernel(sched_gemm, dim3((g.M + 31) / 32, (g.N + 31) / 32, g.ksplit),
+                               dim3(64 * kGemmWaves), s, g);
+  if (e == hipSuccess && g.ksplit > 1) {
+    const size_t mn = static_cast<size_t>(g.M) * g.N;
+    e = launch_kernel(sched_gemm_reduce, dim3(static_cast<unsigned>((mn + 255) / 256)), dim3(256), s, g);
+  }
+  return e;
 }
 
 hipError_t launch_schedule_draft(const SchedGemmArgs& g, const SchedArgs& a, hipStream_t s) {

@@ -223,7 +223,8 @@ size_t sd_schedule_workspace_size(int32_t n, int32_t r, int32_t max_rows, int32_
   if (n < 1 || r < 1 || max_rows < 0 || m < 1) return 0;
   return align_up(static_cast<size_t>(n) * r * sizeof(float)) +
          align_up(static_cast<size_t>(n) * (sd::kSchedMaxK + 1) * sizeof(float)) +
-         align_up(static_cast<size_t>(max_rows) * m * sizeof(float));
+         align_up(static_cast<size_t>(max_rows) * m * sizeof(float)) +
+         align_up(static_cast<size_t>(sd::kSchedSplitK) * n * r * sizeof(float));
 }
 
 sd_status sd_schedule_draft(const void* ctx_feat, const void* anchor_emb, const void* w_c,
@@ -255,6 +256,11 @@ sd_status sd_schedule_draft(const void* ctx_feat, const void* anchor_emb, const 
   g.b2 = static_cast<const uint16_t*>(w_e);
   g.bias = b_u;
   g.c = u;
+  // after u and the rewards (the post-draft slot is empty: max_rows = 0)
+  g.part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                    align_up(static_cast<size_t>(n) * r * sizeof(float)) +
+                                    align_up(static_cast<size_t>(n) * (sd::kSchedMaxK + 1) * sizeof(float)));
+  g.ksplit = sd::kSchedSplitK;
   g.M = n;
   g.N = r;
   g.K = d_h;
@@ -312,6 +318,8 @@ sd_status sd_schedule_verify(const void* hidden, const void* w_s, const void* e_
   g.b2 = nullptr;
   g.bias = nullptr;
   g.c = sh;
+  g.part = nullptr;   // many rows fill the GPU without splitting K (a 4-way split measured slower)
+  g.ksplit = 1;
   g.M = max_rows;
   g.N = m;
   g.K = H;

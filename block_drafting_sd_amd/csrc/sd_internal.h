@@ -79,8 +79,10 @@ struct SchedGemmArgs {        // c = a1 b1^T (+ a2 b2^T) (+ bias, SiLU)
   const uint16_t* b2;         // [N][K]
   const float* bias;          // [N] or null
   float* c;                   // [M][N]
-  int32_t M, N, K, silu;
+  float* part;                // [ksplit][M][N] partial sums (ksplit > 1)
+  int32_t M, N, K, silu, ksplit;
 };
+constexpr int kSchedSplitK = 8;   // K splits of the pre-draft estimator GEMM (few rows)
 
 struct SchedArgs {
   const float* u;             // [n][r] estimator hidden layer
