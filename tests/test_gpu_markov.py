@@ -19,7 +19,7 @@ from oracle.step import NEAR_TIE
 from synth import StepInputs, device as sdev
 from synth.configs import C1_32K, C2_128K
 
-from gpu_common import DEV, log, requires_gpu
+from gpu_common import DEV, bits, log, requires_gpu
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -188,3 +188,91 @@ def test_markov_edges(batch, V, r, max_k):
     ref = omk.markov_sample(base[keep], q_cut, anchor, w_c, e_c, req_id, 5)
     _compare((zg[keep], lg[keep], tg[keep]), ref, q_cut, range(batch),
              f"markov edges batch={batch} V={V} r={r} max_k={max_k}")
+
+
+# ------------------------------------------------ the step with the correction
+
+def _chain_cfg():
+    return C1_32K.with_(name="markov_chain", batch=4, ctx=("list", (300, 37, 0, 600)),
+                        draft_k=("list", (16, 5, 3, 9)), verify="full", num_heads_q=8,
+                        num_heads_kv=2, head_dim=64, hidden=256, vocab=4100, seed=777)
+
+
+@pytest.mark.parametrize("path", ["longspark", "dels"])
+def test_step_with_correction_chain(path):
+    """Attention -> LM head -> sequential correction -> verification through
+    DraftVerifyStep, each stage compared with the oracle on the previous
+    stage's device outputs."""
+    from block_drafting_sd_amd.step import DraftVerifyStep, StepOptions, StepShape
+    from oracle import attention as oa, compare, lm_head as olm, verify as overify
+
+    cfg = _chain_cfg()
+    inp = StepInputs(cfg)
+    b = inp.budgets
+    r = 64
+    if path == "longspark":
+        opts = StepOptions(window=256, n_summary=16, markov_rank=r)
+    else:
+        opts = StepOptions(markov_rank=r, markov_alpha=0.3, prior_beta=0.3)
+    t = {}
+    t.update(sdev.attention_tensors(inp, DEV))
+    t.update(sdev.lm_head_tensors(inp, DEV))
+    t.update(sdev.verify_tensors(inp, DEV))
+    w_c, e_c = inp.markov_tables(r)
+    anchor = inp.anchor_tokens()
+    t.update(markov_w_c=sdev.bf16(w_c, DEV), markov_e_c=sdev.bf16(e_c, DEV),
+             anchor=sdev.i32(anchor, DEV))
+    bias = None
+    if opts.prior_beta:
+        counts = inp.unigram_counts()
+        t["vocab_bias"] = sd.sd_log_prior_bias(torch.from_numpy(counts).to(DEV), lam=1.0,
+                                               scale=-opts.prior_beta)
+        bias = -opts.prior_beta * omk.unigram_log_prior(counts)
+    if opts.n_summary:
+        u = inp.summary_queries(opts.n_summary)
+        t["summary_keys"] = sdev.bf16(u, DEV)
+        t["ctx_len_prev"] = sdev.i32(np.maximum(b.ctx_len - 4, 0), DEV)
+    shape = StepShape(batch=cfg.batch, total_q=inp.total_q, total_target_rows=inp.total_target_rows,
+                      num_heads_q=cfg.num_heads_q, num_heads_kv=cfg.num_heads_kv,
+                      head_dim=cfg.head_dim, hidden=cfg.hidden, vocab=cfg.vocab,
+                      max_total_ctx=inp.max_total_ctx, max_draft_k=int(b.draft_k.max()))
+    step = DraftVerifyStep(shape, DEV, opts)
+    if opts.n_summary:
+        step.summary_init(t)
+        torch.cuda.synchronize()
+        zs = step.summary_values.cpu().numpy()      # the state the attention reads
+    seed = inp.philox_seed
+    step.attention(t)
+    step.lm_head(t, seed)
+    torch.cuda.synchronize()
+    base = step.logits.cpu().numpy()                # before the correction
+    step.markov(t, seed)
+    step.verify(t, seed)
+    torch.cuda.synchronize()
+    reqs = range(cfg.batch)
+
+    # 1. attention (with the device's summary state, staged)
+    kw = dict(window=256, summary_keys=u, summary_values=zs) if opts.n_summary else {}
+    ref = oa.draft_attn(inp.q, inp.k_blk, inp.v_blk, inp.k_cache, inp.v_cache, inp.page_table,
+                        b.ctx_len, b.q_off, cfg.num_heads_kv, inp.softmax_scale, **kw)
+    rep = compare.attention_report(bits(step.attn_out), ref)
+    log(f"{path} chain: attention {rep}")
+    assert rep["ok"] and rep["rel_l2"] < 1e-2
+    # 2. LM head base logits
+    z_ref = olm.lm_head_logits(inp.hidden, inp.w_vocab)
+    dz = np.abs(base - z_ref).max()
+    # 3. correction and draws from the device's base logits
+    got = (step.logits.cpu().numpy(), step.lse.cpu().numpy(), step.tokens.cpu().numpy())
+    ref_m = omk.markov_sample(base, b.q_off, anchor, w_c, e_c, inp.req_id, seed,
+                              alpha=opts.markov_alpha,
+                              vocab_bias=None if bias is None else t["vocab_bias"].cpu().numpy())
+    log(f"{path} chain: base logits max-abs {dz:.2e}")
+    assert dz <= 1e-5
+    _compare(got, ref_m, b.q_off, reqs, f"{path} chain: correction")
+    # 4. verification of the device's corrected drafts
+    ref_v = overify.verify(inp.target_logits, b.t_off, got[0].astype(np.float64), got[2], b.q_off,
+                           inp.req_id, seed, requests=list(reqs))
+    rep = compare.verify_report(step.accepted.cpu().numpy(), step.next_token.cpu().numpy(), ref_v,
+                                reqs)
+    log(f"{path} chain: verify {rep}")
+    assert rep["ok"]
