@@ -11,11 +11,16 @@
 // eq. (11), c'' = log(e^c + e^c'), Z'' = e^(c - c'') Z + e^(c' - c'') Z'.
 // An empty set of new rows leaves the state as it is.
 //
-// summary_fold: one workgroup per (request, KV head).  The new rows are read
-// in place through the page table in tiles of 64; scores, the running max
-// and sum and the weighted values are fp32.  A step folds at most K + 1 rows
-// (one tile); initialising from a whole prefix is the same loop over all of
-// its tiles.
+// summary_fold: one workgroup (4 waves) per (request, KV head).  The new rows
+// are read in place through the page table in tiles of 64: the tile's page
+// ids first, then every key chunk and every 8-token value chunk as
+// independent 16-byte loads.  Lane l of every wave owns row l of the tile;
+// wave w owns the summary queries w, w + 4, ...: its scores are dot products
+// of the lane's key row (read once per 8 dims) with each query (a broadcast
+// read), the online softmax of a query is a wave reduction, and the weighted
+// values are summed per (query, dim) entry with independent accumulators.
+// Everything is fp32.  A step folds at most K + 1 rows (one tile);
+// initialising from a whole prefix is the same loop over all of its tiles.
 #include "sd_common.h"
 #include "sd_internal.h"
 
@@ -25,19 +30,23 @@ namespace sd {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRows = 64;   // rows per tile
+constexpr int kWaves = kThreads / 64;
+constexpr int kRows = 64;                         // rows per tile = lanes
+constexpr int kQPerWave = kSummaryMax / kWaves;   // summary queries per wave (max)
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void summary_fold(SummaryArgs a) {
-  __shared__ float s_u[D * kSummaryMax];          // summary queries, [d][i] (fp32)
-  __shared__ uint16_t s_k[D * kRows];             // key tile, [d][row] (bf16 bits)
-  __shared__ uint16_t s_v[kRows * D];             // value tile
-  __shared__ float s_p[kSummaryMax * kRows];      // scores, then weights
-  __shared__ float s_m[kSummaryMax], s_l[kSummaryMax], s_alpha[kSummaryMax];
+  constexpr int KP = D + 8;                       // key row pitch (bf16): spreads banks
+  __shared__ __attribute__((aligned(16))) float s_u[kSummaryMax * D];   // queries [q][d]
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[kRows * KP];     // keys [row][d]
+  __shared__ uint16_t s_v[kRows * D];                                   // values [row][d]
+  __shared__ float s_p[kSummaryMax * kRows];                            // weights [q][row]
+  __shared__ float s_alpha[kSummaryMax];
+  __shared__ int s_pg[kRows];
 
   const int b = blockIdx.x / a.hkv;
   const int g = blockIdx.x % a.hkv;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.n_summary;
   const int n_max = a.max_pages * 16;
   const int n = clampi(a.ctx_len[b], 0, n_max);
@@ -60,13 +69,16 @@ __global__ __launch_bounds__(kThreads) void summary_fold(SummaryArgs a) {
   }
 
   const uint16_t* uq = a.u + static_cast<size_t>(g) * S * D;
-  for (int i = tid; i < S * D; i += kThreads)
-    s_u[(i % D) * S + i / D] = __uint_as_float(static_cast<uint32_t>(uq[i]) << 16);
-  for (int i = tid; i < S; i += kThreads) {
-    s_m[i] = -INFINITY;
-    s_l[i] = 0.f;
+  for (int i = tid; i < S * D; i += kThreads) s_u[i] = __uint_as_float(static_cast<uint32_t>(uq[i]) << 16);
+  // running max and sum of the wave's queries (wave-uniform)
+  float m_run[kQPerWave], l_run[kQPerWave];
+#pragma unroll
+  for (int j = 0; j < kQPerWave; ++j) {
+    m_run[j] = -INFINITY;
+    l_run[j] = 0.f;
   }
-  // weighted values of the new rows: thread t owns entries t, t + 256, ...
+  // weighted values: thread t owns entries t, t + 256, ... of [q][d]
+  static_assert(kThreads % D == 0, "a thread's entries share one dim");
   constexpr int kOwn = kSummaryMax * D / kThreads;
   float acc[kOwn];
 #pragma unroll
@@ -76,72 +88,125 @@ __global__ __launch_bounds__(kThreads) void summary_fold(SummaryArgs a) {
   for (int t0 = r0; t0 < r1; t0 += kRows) {
     const int rows = min(kRows, r1 - t0);
     __syncthreads();   // the previous tile's readers are done
-    // keys: one 16-byte chunk (8 dims) per (row, chunk), stored transposed;
-    // values: per (row, dim)
-    for (int i = tid; i < kRows * (D / 8); i += kThreads) {
-      const int rr = i % kRows, c = i / kRows;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (rr < rows) {
-        const int tok = t0 + rr;
-        const int pg = clampi(pt[tok >> 4], 0, a.num_pages - 1);
-        const uint16_t* src =
-            a.k_cache + ((static_cast<size_t>(pg) * a.hkv + g) * (D / 8) + c) * 128 + (tok & 15) * 8;
-        v = *reinterpret_cast<const u32x4*>(src);
-      }
+    if (tid < kRows) s_pg[tid] = tid < rows ? clampi(pt[(t0 + tid) >> 4], 0, a.num_pages - 1) : 0;
+    __syncthreads();
+    // keys: one 16-byte chunk (8 dims) per (row, chunk)
+    constexpr int kKeyLoads = kRows * (D / 8) / kThreads;
+    u32x4 kv[kKeyLoads];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        s_k[(8 * c + e) * kRows + rr] = static_cast<uint16_t>(v[e / 2] >> (16 * (e & 1)));
+    for (int j = 0; j < kKeyLoads; ++j) {
+      const int i = tid + kThreads * j;
+      const int rr = i % kRows, c = i / kRows;
+      kv[j] = u32x4{0u, 0u, 0u, 0u};
+      if (rr < rows)
+        kv[j] = *reinterpret_cast<const u32x4*>(
+            a.k_cache + ((static_cast<size_t>(s_pg[rr]) * a.hkv + g) * (D / 8) + c) * 128 + ((t0 + rr) & 15) * 8);
     }
-    for (int i = tid; i < kRows * D; i += kThreads) {
-      const int rr = i / D, d = i % D;
-      uint16_t v = 0;
-      if (rr < rows) {
-        const int tok = t0 + rr;
-        const int pg = clampi(pt[tok >> 4], 0, a.num_pages - 1);
-        v = a.v_cache[((static_cast<size_t>(pg) * a.hkv + g) * D + d) * 16 + (tok & 15)];
+    // values: one 16-byte chunk = 8 consecutive tokens (8-aligned, so inside
+    // one page) of one dim; chunk ch covers tokens 8 ch .. 8 ch + 7
+    const int ch0 = t0 >> 3;
+    const int nch = ((t0 + rows - 1) >> 3) - ch0 + 1;           // <= kRows / 8 + 1
+    constexpr int kValLoads = (kRows / 8 + 1) * D / kThreads + 1;
+    u32x4 vv[kValLoads];
+#pragma unroll
+    for (int j = 0; j < kValLoads; ++j) {
+      const int i = tid + kThreads * j;
+      const int cj = i / D, d = i % D;
+      vv[j] = u32x4{0u, 0u, 0u, 0u};
+      if (cj < nch) {
+        const int first = max((ch0 + cj) * 8, t0);                // a row of this tile in the chunk's page
+        vv[j] = *reinterpret_cast<const u32x4*>(
+            a.v_cache + ((static_cast<size_t>(s_pg[first - t0]) * a.hkv + g) * D + d) * 16 + ((ch0 + cj) * 8 & 15));
       }
-      s_v[rr * D + d] = v;
+    }
+#pragma unroll
+    for (int j = 0; j < kKeyLoads; ++j) {
+      const int i = tid + kThreads * j;
+      const int rr = i % kRows, c = i / kRows;
+      *reinterpret_cast<u32x4*>(s_k + rr * KP + 8 * c) = kv[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kValLoads; ++j) {
+      const int i = tid + kThreads * j;
+      const int cj = i / D, d = i % D;
+      if (cj < nch) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int rr = (ch0 + cj) * 8 + e - t0;
+          if (rr >= 0 && rr < rows) s_v[rr * D + d] = static_cast<uint16_t>(vv[j][e / 2] >> (16 * (e & 1)));
+        }
+      }
+    }
+    for (int i = tid; i < (kRows - rows) * D; i += kThreads) s_v[rows * D + i] = 0;
+    __syncthreads();
+
+    // scores of the wave's queries against row `lane`
+    float sc[kQPerWave];
+#pragma unroll
+    for (int j = 0; j < kQPerWave; ++j) sc[j] = 0.f;
+#pragma unroll 2
+    for (int c = 0; c < D / 8; ++c) {
+      const u32x4 kc = *reinterpret_cast<const u32x4*>(s_k + lane * KP + 8 * c);
+      float kf[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kf[e] = __uint_as_float((e & 1) ? (kc[e / 2] & 0xffff0000u) : (kc[e / 2] << 16));
+#pragma unroll
+      for (int j = 0; j < kQPerWave; ++j) {
+        const int q = wave + kWaves * j;
+        if (q < S) {                                     // wave-uniform
+          const float4 u0 = *reinterpret_cast<const float4*>(s_u + q * D + 8 * c);
+          const float4 u1 = *reinterpret_cast<const float4*>(s_u + q * D + 8 * c + 4);
+          sc[j] += u0.x * kf[0] + u0.y * kf[1] + u0.z * kf[2] + u0.w * kf[3] + u1.x * kf[4] + u1.y * kf[5] +
+                   u1.z * kf[6] + u1.w * kf[7];
+        }
+      }
+    }
+    // online softmax of each query over the tile (a wave reduction)
+#pragma unroll
+    for (int j = 0; j < kQPerWave; ++j) {
+      const int q = wave + kWaves * j;
+      if (q < S) {                                       // wave-uniform
+        const float s = lane < rows ? sc[j] * a.scale : -INFINITY;
+        float mx = s;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        const float mnew = fmaxf(m_run[j], mx);
+        const float w = lane < rows ? expf(s - mnew) : 0.f;
+        float sum = w;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) sum += __shfl_xor(sum, o, 64);
+        const float alpha = expf(m_run[j] - mnew);       // 0 on the first tile (m_run = -inf)
+        l_run[j] = l_run[j] * alpha + sum;
+        m_run[j] = mnew;
+        s_p[q * kRows + lane] = w;
+        if (lane == 0) s_alpha[q] = alpha;
+      }
     }
     __syncthreads();
-    // scores s_ik = scale * u_i . k_k
-    for (int i = tid; i < S * kRows; i += kThreads) {
-      const int q = i / kRows, k = i % kRows;
-      float s = -INFINITY;
-      if (k < rows) {
-        float dot = 0.f;
-        for (int d = 0; d < D; ++d)
-          dot += s_u[d * S + q] * __uint_as_float(static_cast<uint32_t>(s_k[d * kRows + k]) << 16);
-        s = dot * a.scale;
-      }
-      s_p[i] = s;
-    }
-    __syncthreads();
-    // online softmax per query: new max, rescale factor, weights, sum
-    for (int q = tid; q < S; q += kThreads) {
-      float mx = s_m[q];
-      for (int k = 0; k < rows; ++k) mx = fmaxf(mx, s_p[q * kRows + k]);
-      const float alpha = expf(s_m[q] - mx);   // 0 on the first tile (s_m = -inf)
-      float l = s_l[q] * alpha;
-      for (int k = 0; k < kRows; ++k) {
-        const float w = k < rows ? expf(s_p[q * kRows + k] - mx) : 0.f;
-        s_p[q * kRows + k] = w;
-        l += w;
-      }
-      s_m[q] = mx;
-      s_l[q] = l;
-      s_alpha[q] = alpha;
-    }
-    __syncthreads();
+    // entry e of this thread is (query (tid + 256 e) / D, dim tid % D): one
+    // value read per row serves all of them
 #pragma unroll
     for (int e = 0; e < kOwn; ++e) {
       const int idx = tid + kThreads * e;
-      if (idx < S * D) {
-        const int q = idx / D, d = idx % D;
-        float v = acc[e] * s_alpha[q];
-        for (int k = 0; k < rows; ++k)
-          v += s_p[q * kRows + k] * __uint_as_float(static_cast<uint32_t>(s_v[k * D + d]) << 16);
-        acc[e] = v;
+      if (idx < S * D) acc[e] *= s_alpha[idx / D];
+    }
+    for (int k = 0; k < rows; ++k) {
+      const float vk = __uint_as_float(static_cast<uint32_t>(s_v[k * D + tid % D]) << 16);
+#pragma unroll
+      for (int e = 0; e < kOwn; ++e) {
+        const int idx = tid + kThreads * e;
+        if (idx < S * D) acc[e] += s_p[(idx / D) * kRows + k] * vk;
       }
+    }
+  }
+  // publish each query's running max and sum (s_alpha and s_p are free)
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kQPerWave; ++j) {
+    const int q = wave + kWaves * j;
+    if (q < S && lane == 0) {
+      s_alpha[q] = m_run[j];
+      s_p[q] = l_run[j];
     }
   }
   __syncthreads();
@@ -152,8 +217,8 @@ __global__ __launch_bounds__(kThreads) void summary_fold(SummaryArgs a) {
     const int idx = tid + kThreads * e;
     if (idx < S * D) {
       const int q = idx / D;
-      const float c_new = s_m[q] + logf(s_l[q]);
-      const float z_new = acc[e] / s_l[q];
+      const float c_new = s_alpha[q] + logf(s_p[q]);
+      const float z_new = acc[e] / s_p[q];
       const float c_old = a.accepted ? cs[q] : -INFINITY;
       if (c_old == -INFINITY) {
         zs[idx] = z_new;
@@ -166,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void summary_fold(SummaryArgs a) {
   }
   __syncthreads();   // every thread has read cs[] before it is overwritten
   for (int q = tid; q < S; q += kThreads) {
-    const float c_new = s_m[q] + logf(s_l[q]);
+    const float c_new = s_alpha[q] + logf(s_p[q]);
     const float c_old = a.accepted ? cs[q] : -INFINITY;
     if (c_old == -INFINITY) {
       cs[q] = c_new;
