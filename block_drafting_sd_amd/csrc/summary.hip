@@ -32,16 +32,18 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kRows = 64;                         // rows per tile = lanes
-constexpr int kQPerWave = kSummaryMax / kWaves;   // summary queries per wave (max)
 
-template <int D>
+// D: head dim; SMAX: the most summary entries this instance handles (16, or
+// kSummaryMax), which sizes the per-wave query registers and accumulators.
+template <int D, int SMAX>
 __global__ __launch_bounds__(kThreads) void summary_fold(SummaryArgs a) {
+  constexpr int kQPerWave = SMAX / kWaves;        // summary queries per wave (max)
   constexpr int KP = D + 8;                       // key row pitch (bf16): spreads banks
-  __shared__ __attribute__((aligned(16))) float s_u[kSummaryMax * D];   // queries [q][d]
+  __shared__ __attribute__((aligned(16))) float s_u[SMAX * D];          // queries [q][d]
   __shared__ __attribute__((aligned(16))) uint16_t s_k[kRows * KP];     // keys [row][d]
   __shared__ uint16_t s_v[kRows * D];                                   // values [row][d]
-  __shared__ float s_p[kSummaryMax * kRows];                            // weights [q][row]
-  __shared__ float s_alpha[kSummaryMax];
+  __shared__ float s_p[SMAX * kRows];                                   // weights [q][row]
+  __shared__ float s_alpha[SMAX];
   __shared__ int s_pg[kRows];
 
   const int b = blockIdx.x / a.hkv;
@@ -79,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void summary_fold(SummaryArgs a) {
   }
   // weighted values: thread t owns entries t, t + 256, ... of [q][d]
   static_assert(kThreads % D == 0, "a thread's entries share one dim");
-  constexpr int kOwn = kSummaryMax * D / kThreads;
+  constexpr int kOwn = SMAX * D / kThreads;
   float acc[kOwn];
 #pragma unroll
   for (int e = 0; e < kOwn; ++e) acc[e] = 0.f;
@@ -246,8 +248,11 @@ __global__ __launch_bounds__(kThreads) void summary_fold(SummaryArgs a) {
 
 hipError_t launch_summary(const SummaryArgs& a, int head_dim, hipStream_t s) {
   const dim3 grid(a.batch * a.hkv), block(kThreads);
-  return head_dim == 64 ? launch_kernel(summary_fold<64>, grid, block, s, a)
-                        : launch_kernel(summary_fold<128>, grid, block, s, a);
+  if (a.n_summary <= 16)
+    return head_dim == 64 ? launch_kernel(summary_fold<64, 16>, grid, block, s, a)
+                          : launch_kernel(summary_fold<128, 16>, grid, block, s, a);
+  return head_dim == 64 ? launch_kernel(summary_fold<64, kSummaryMax>, grid, block, s, a)
+                        : launch_kernel(summary_fold<128, kSummaryMax>, grid, block, s, a);
 }
 
 }  // namespace sd

@@ -123,7 +123,7 @@ def _check_summary(z, c, Zr, Cr, tag):
     assert dz <= Z_ATOL and (dc.size == 0 or dc.max() <= C_RTOL)
 
 
-@pytest.mark.parametrize("head_dim,n_summary", [(128, 16), (64, 64)])
+@pytest.mark.parametrize("head_dim,n_summary", [(128, 16), (64, 64), (128, 40), (64, 5)])
 def test_summary_init_then_fold(head_dim, n_summary):
     # every round appends a_b + 1 >= 1 rows; the first request starts empty
     inp = StepInputs(_cfg(head_dim=head_dim, batch=5, ctx=("list", (1, 2, 37, 160, 1000)),
