@@ -84,9 +84,13 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0,
 enum : uint32_t { kStreamDraft = 0, kStreamAccept = 1, kStreamSample = 2 };
 
 // Gumbel noise -log(-log u) for u = (2 (x >> 9) + 1) 2^-24, in (0, 1).
+// u lies in [2^-24, 1 - 2^-24] and -ln u in (2^-24, 17): both normal floats,
+// so the hardware base-2 logarithm applies without the denormal and range
+// handling of logf: -ln(-ln u) = -ln2 log2(-ln2 log2 u).
 __device__ __forceinline__ float gumbel_from_bits(uint32_t x) {
   const float u = static_cast<float>((x >> 9) * 2u + 1u) * 5.9604644775390625e-8f;
-  return -logf(-logf(u));
+  const float e = -kLn2 * __builtin_amdgcn_logf(u);   // -ln u > 0
+  return -kLn2 * __builtin_amdgcn_logf(e);
 }
 
 // Acceptance uniform u = (x >> 8) 2^-24 in [0, 1).
