@@ -36,6 +36,13 @@ def _req(t: torch.Tensor, name: str, dtypes, device=None) -> torch.Tensor:
     return t
 
 
+def _need(t: Optional[torch.Tensor], n: int, name: str) -> None:
+    """Device arrays are never read on the host, so the library cannot check
+    their lengths: the binding does."""
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{name} has {t.numel()} entries, needs at least {n}")
+
+
 _BF16 = (torch.bfloat16,)
 _I32 = (torch.int32,)
 _U32 = (torch.int32, torch.uint32)
@@ -124,12 +131,17 @@ def sd_draft_attn(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_len, q_off,
     hkv = k_blk.shape[1]
     num_pages, _, _, page_size, _ = k_cache.shape
     batch, max_pages = page_table.shape
+    _need(ctx_len, batch, "ctx_len")
+    _need(q_off, batch + 1, "q_off")
+    if tuple(k_blk.shape) != (total_q, hkv, D) or tuple(v_blk.shape) != (total_q, hkv, D):
+        raise ValueError("k_blk and v_blk must be [total_q, Hkv, D]")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     nbytes = lib.sd_draft_attn_workspace_size(batch, hq, hkv, D, max_total_ctx, split_tokens)
     workspace = _workspace(workspace, nbytes, dev)
     if out is None:
         out = torch.empty_like(q)
+    _need(out, q.numel(), "out")
     n_summary = 0
     if summary_keys is not None or summary_values is not None:
         _req(summary_keys, "summary_keys", _BF16, dev)
@@ -172,6 +184,8 @@ def sd_summary_update(summary_queries, k_cache, v_cache, page_table, ctx_len, ac
     if tuple(summary_values.shape) != (batch, hkv, n_summary, D) or \
             tuple(summary_lse.shape) != (batch, hkv, n_summary):
         raise ValueError("summary_values must be [batch, Hkv, S, D] and summary_lse [batch, Hkv, S]")
+    _need(ctx_len, batch, "ctx_len")
+    _need(accepted_len, batch, "accepted_len")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     st = lib.sd_summary_update(_ptr(summary_queries), _ptr(k_cache), _ptr(v_cache),
@@ -202,12 +216,16 @@ def sd_lm_head_probs(hidden, w_vocab, q_off, req_id, seed: int, *, vocab_map=Non
     w_rows = w_vocab.shape[0]
     V = w_rows if vocab_map is None else vocab_map.numel()
     batch = q_off.numel() - 1
+    _need(req_id, batch, "req_id")
     if logits is None:
         logits = torch.empty(M, V, dtype=torch.float32, device=dev)
     if lse is None:
         lse = torch.empty(M, dtype=torch.float32, device=dev)
     if draft_tokens is None:
         draft_tokens = torch.empty(M, dtype=torch.int32, device=dev)
+    _need(logits, M * V, "logits")
+    _need(lse, M, "lse")
+    _need(draft_tokens, M, "draft_tokens")
     nbytes = lib.sd_lm_head_workspace_size(M, V)
     workspace = _workspace(workspace, nbytes, dev)
     st = lib.sd_lm_head_probs(_ptr(hidden), _ptr(w_vocab), M, H, V, _ptr(q_off), batch,
@@ -242,10 +260,14 @@ def sd_markov_sample(logits, anchor_tokens, w_c, e_c, q_off, req_id, seed: int, 
         if vocab_bias.numel() != V:
             raise ValueError("vocab_bias must have V entries")
     batch = q_off.numel() - 1
+    _need(anchor_tokens, batch, "anchor_tokens")
+    _need(req_id, batch, "req_id")
     if lse is None:
         lse = torch.empty(M, dtype=torch.float32, device=dev)
     if draft_tokens is None:
         draft_tokens = torch.empty(M, dtype=torch.int32, device=dev)
+    _need(lse, M, "lse")
+    _need(draft_tokens, M, "draft_tokens")
     workspace = _workspace(workspace, markov_workspace_size(batch, V, max_draft_k), dev)
     st = lib.sd_markov_sample(_ptr(logits), _ptr(lse), _ptr(draft_tokens), _ptr(anchor_tokens),
                               _ptr(w_c), _ptr(e_c), float(alpha),
@@ -302,8 +324,16 @@ def sd_verify(target_logits, t_off, draft_logits, draft_lse, draft_tokens, q_off
     nbytes = lib.sd_verify_workspace_size(batch, total_q, R, V)
     workspace = _workspace(workspace, nbytes, dev)
     v_draft = draft_logits.shape[1] if draft_logits.dim() == 2 else V
+    _need(q_off, batch + 1, "q_off")
+    _need(req_id, batch, "req_id")
+    _need(draft_logits, total_q * v_draft, "draft_logits")
+    _need(draft_lse, total_q, "draft_lse")
+    _need(accepted_len, batch, "accepted_len")
+    _need(next_token, batch, "next_token")
+    _need(accept_ratio, total_q, "accept_ratio")
     if draft_vocab_inv is not None:
         _req(draft_vocab_inv, "draft_vocab_inv", _I32, dev)
+        _need(draft_vocab_inv, V, "draft_vocab_inv")
     st = lib.sd_verify(_ptr(target_logits), _ptr(t_off), _ptr(draft_logits), _ptr(draft_lse),
                        _ptr(draft_tokens), _ptr(q_off), batch, total_q, R, V,
                        _ptr(draft_vocab_inv), v_draft, int(bool(greedy)), _ptr(req_id),

@@ -251,3 +251,24 @@ def test_probe_validation(lib):
     assert lib.sd_probe_mfma(10, None, None) == 1
     assert lib.sd_probe_mfma_flops(1) == 512 * 4 * 8 * 2 * 32 * 32 * 16
     assert lib.sd_probe_mfma_flops(0) == 0
+
+
+def test_python_binding_checks_array_lengths():
+    # device arrays are never read on the host: the binding checks lengths
+    import torch
+    bf, i32 = torch.bfloat16, torch.int32
+    z = torch.zeros(8, 100)
+    w = torch.zeros(100, 16, dtype=bf)
+    q_off = torch.tensor([0, 4, 8], dtype=i32)
+    with pytest.raises(ValueError, match="anchor_tokens"):
+        sd.sd_markov_sample(z, torch.zeros(1, dtype=i32), w, w, q_off, torch.zeros(2, dtype=i32),
+                            1, max_draft_k=4)
+    with pytest.raises(ValueError, match="req_id"):
+        sd.sd_markov_sample(z, torch.zeros(2, dtype=i32), w, w, q_off, torch.zeros(1, dtype=i32),
+                            1, max_draft_k=4)
+    h = torch.zeros(8, 64, dtype=bf)
+    wv = torch.zeros(100, 64, dtype=bf)
+    with pytest.raises(ValueError, match="req_id"):
+        sd.sd_lm_head_probs(h, wv, q_off, torch.zeros(1, dtype=i32), 0)
+    with pytest.raises(ValueError, match="lse"):
+        sd.sd_lm_head_probs(h, wv, q_off, torch.zeros(2, dtype=i32), 0, lse=torch.zeros(3))
