@@ -47,12 +47,13 @@ namespace sd {
 
 int32_t attn_split_tokens(int32_t hkv, int64_t max_total_ctx, int32_t requested) {
   if (requested > 0) return requested;
-  // aim for ~2048 prefix work items (8 per CU), at least 256 tokens each and
-  // at most the page ids one workgroup stages in LDS
+  // aim for ~2048 prefix work items (8 per CU), at least 2048 tokens each
+  // (shorter items measured slower: more partials and per-item overhead for
+  // the same bytes) and at most the page ids one workgroup stages in LDS
   const int64_t target_items = 2048;
   int64_t s = (static_cast<int64_t>(hkv) * max_total_ctx + target_items - 1) / target_items;
   s = (s + 255) / 256 * 256;
-  if (s < 256) s = 256;
+  if (s < 2048) s = 2048;
   if (s > kAttnMaxSplitPages * 16) s = kAttnMaxSplitPages * 16;
   return static_cast<int32_t>(s);
 }
