@@ -46,12 +46,13 @@ def correction(w_c, e_c, token: int):
 
 
 def markov_sample(base_logits, q_off, anchor, w_c, e_c, req_id, seed: int, requests=None,
-                  alpha: float = 1.0, vocab_bias=None):
+                  alpha: float = 1.0, vocab_bias=None, greedy: bool = False):
     """Sequential correction and sampling of every request (or ``requests``).
     ``base_logits [M, V]`` are l^(0) of the packed draft rows; ``alpha``
     scales the correction and ``vocab_bias [V]`` (optional) is added to every
-    row.  Returns dict (logits [M, V] corrected, lse [M], tokens [M],
-    gap [M]); rows of other requests stay NaN / -1."""
+    row; ``greedy`` draws the argmax of each corrected row (temperature 0,
+    smallest index on ties).  Returns dict (logits [M, V] corrected, lse [M],
+    tokens [M], gap [M]); rows of other requests stay NaN / -1."""
     M, V = base_logits.shape
     W = bf16_bits_to_f64(w_c)
     E = bf16_bits_to_f64(e_c)
@@ -67,7 +68,8 @@ def markov_sample(base_logits, q_off, anchor, w_c, e_c, req_id, seed: int, reque
             if vocab_bias is not None:
                 z[m] = z[m] + np.asarray(vocab_bias, np.float64)
             lse[m] = logsumexp_rows(z[m][None])[0]
-            t, g = draft_tokens(z[m][None], np.array([b]), np.array([j]), req_id, seed)
+            t, g = draft_tokens(z[m][None], np.array([b]), np.array([j]), req_id, seed,
+                                greedy=greedy)
             tok[m], gap[m] = t[0], g[0]
             prev = int(tok[m])
     return dict(logits=z, lse=lse, tokens=tok, gap=gap)

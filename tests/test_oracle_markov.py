@@ -13,6 +13,9 @@ sec. 2.3, eqs. (7)-(8)).
 * long logits equal to the log prior, minus the prior (beta = 1, alpha = 0),
   leave a flat row: lse = log V exactly (a sign error would double the prior);
 * alpha = 2 equals doubling W_M (exact in bf16).
+
+Temperature 0: every draw is torch.argmax of the corrected row, and the next
+row's correction follows that argmax.
 """
 import numpy as np
 import torch
@@ -112,3 +115,16 @@ def test_alpha_scales_the_correction():
     b = omk.markov_sample(base, q_off, anchor, w2, e_c, req_id, 17)
     np.testing.assert_array_equal(a["tokens"], b["tokens"])
     np.testing.assert_allclose(a["logits"], b["logits"], rtol=0, atol=1e-13)
+
+
+def test_greedy_draws_follow_the_argmax():
+    base, q_off, anchor, w_c, e_c, req_id = _problem(6)
+    got = omk.markov_sample(base, q_off, anchor, w_c, e_c, req_id, 3, greedy=True)
+    W = torch.from_numpy(bf16_bits_to_f64(w_c))
+    E = torch.from_numpy(bf16_bits_to_f64(e_c))
+    for b in range(len(q_off) - 1):
+        prev = int(anchor[b])
+        for m in range(q_off[b], q_off[b + 1]):
+            row = torch.from_numpy(base[m].astype(np.float64)) + W @ E[prev]
+            assert got["tokens"][m] == int(torch.argmax(row))
+            prev = int(got["tokens"][m])
