@@ -238,8 +238,8 @@ def sd_lm_head_probs(hidden, w_vocab, q_off, req_id, seed: int, *, vocab_map=Non
 
 
 def sd_markov_sample(logits, anchor_tokens, w_c, e_c, q_off, req_id, seed: int, *,
-                     max_draft_k: int, alpha: float = 1.0, vocab_bias=None, lse=None,
-                     draft_tokens=None, workspace=None, stream=None):
+                     max_draft_k: int, alpha: float = 1.0, vocab_bias=None, greedy: bool = False,
+                     lse=None, draft_tokens=None, workspace=None, stream=None):
     """Sequential correction of the draft logits (in place) and sampling;
     see ``sd_markov_sample`` in include/sd.h (``alpha`` and ``vocab_bias``
     give the logit fusion).  Returns (logits, lse, tokens)."""
@@ -271,7 +271,8 @@ def sd_markov_sample(logits, anchor_tokens, w_c, e_c, q_off, req_id, seed: int, 
     workspace = _workspace(workspace, markov_workspace_size(batch, V, max_draft_k), dev)
     st = lib.sd_markov_sample(_ptr(logits), _ptr(lse), _ptr(draft_tokens), _ptr(anchor_tokens),
                               _ptr(w_c), _ptr(e_c), float(alpha),
-                              None if vocab_bias is None else _ptr(vocab_bias), _ptr(q_off),
+                              None if vocab_bias is None else _ptr(vocab_bias), int(bool(greedy)),
+                              _ptr(q_off),
                               batch, M, V, r, int(max_draft_k),
                               _ptr(req_id), int(seed) & ((1 << 64) - 1), _ptr(workspace),
                               workspace.numel(), _stream_handle(stream))

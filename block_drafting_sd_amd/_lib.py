@@ -42,8 +42,8 @@ SIGNATURES = {
     "sd_lm_head_probs": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _u64,
                                 _vp, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sd_markov_workspace_size": (_sz, [_i32, _i32, _i32]),
-    "sd_markov_sample": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _i32, _i32, _i32, _i32,
-                                _i32, _vp, _u64, _vp, _sz, _vp]),
+    "sd_markov_sample": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _vp, _i32, _i32, _i32,
+                                _i32, _i32, _vp, _u64, _vp, _sz, _vp]),
     "sd_log_prior_bias": (_i32, [_vp, _i32, C.c_double, _f32, _vp, _vp]),
     "sd_verify_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
     "sd_verify": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,

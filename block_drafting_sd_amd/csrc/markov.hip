@@ -196,12 +196,14 @@ __global__ __launch_bounds__(256) void markov_step(MarkovArgs a, int j) {
             if (v + e < a.V) row[v + e] = x[e];
         }
         if (v < a.V) {
-          const u32x4 w = philox4x32_10(u32x4{static_cast<uint32_t>(v >> 2), static_cast<uint32_t>(j),
-                                              rid, kStreamDraft},
-                                        a.key0, a.key1);
+          // Gumbel-max keys; temperature 0 ranks the corrected logits themselves
+          const u32x4 w = a.greedy ? u32x4{0u, 0u, 0u, 0u}
+                                   : philox4x32_10(u32x4{static_cast<uint32_t>(v >> 2), static_cast<uint32_t>(j),
+                                                         rid, kStreamDraft},
+                                                   a.key0, a.key1);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (v + e < a.V) fold_entry(x[e], gumbel_from_bits(w[e]), v + e, mx, se, best);
+            if (v + e < a.V) fold_entry(x[e], a.greedy ? 0.f : gumbel_from_bits(w[e]), v + e, mx, se, best);
         }
       }
     }

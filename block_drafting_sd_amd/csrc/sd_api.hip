@@ -402,7 +402,7 @@ size_t sd_markov_workspace_size(int32_t batch, int32_t V, int32_t max_draft_k) {
 
 sd_status sd_markov_sample(float* logits, float* lse, int32_t* draft_tokens,
                            const int32_t* anchor_tokens, const void* w_c, const void* e_c,
-                           float alpha, const float* vocab_bias, const int32_t* q_off, int32_t batch, int32_t M, int32_t V, int32_t r,
+                           float alpha, const float* vocab_bias, int32_t greedy, const int32_t* q_off, int32_t batch, int32_t M, int32_t V, int32_t r,
                            int32_t max_draft_k, const uint32_t* req_id, uint64_t seed,
                            void* workspace, size_t workspace_bytes, void* stream) {
   if (!logits || !lse || !draft_tokens || !anchor_tokens || !w_c || !e_c || !q_off || !req_id)
@@ -410,7 +410,8 @@ sd_status sd_markov_sample(float* logits, float* lse, int32_t* draft_tokens,
   if (batch < 1 || M < 0 || V < 1 || r < 16 || r % 16 != 0 || r > 65536 || max_draft_k < 0 ||
       max_draft_k > 4096)
     return SD_ERR_SHAPE;
-  if (!aligned16(w_c) || !aligned16(e_c) || !isfinite(alpha)) return SD_ERR_SHAPE;
+  if (!aligned16(w_c) || !aligned16(e_c) || !isfinite(alpha) || (greedy != 0 && greedy != 1))
+    return SD_ERR_SHAPE;
   if (static_cast<int64_t>(max_draft_k) * batch * sd::markov_parts(V) > (int64_t(1) << 31) - 1)
     return SD_ERR_SHAPE;
   if (M == 0 || max_draft_k == 0) return SD_OK;
@@ -425,6 +426,7 @@ sd_status sd_markov_sample(float* logits, float* lse, int32_t* draft_tokens,
   a.e_c = static_cast<const uint16_t*>(e_c);
   a.vbias = vocab_bias;
   a.alpha = alpha;
+  a.greedy = greedy;
   a.q_off = q_off;
   a.req_id = req_id;
   const size_t cells = static_cast<size_t>(max_draft_k) * batch;

@@ -164,6 +164,7 @@ struct MarkovArgs {
   const uint16_t* e_c;        // [V][r]
   const float* vbias;         // [V] added to every row, or null
   float alpha;                // scale of the correction
+  int32_t greedy;             // 1: draws are the argmax of the corrected logits
   const int32_t* q_off;       // [batch + 1]
   const uint32_t* req_id;     // [batch]
   float2* part;               // [max_k][batch][n_parts] (max, sum exp) (workspace)

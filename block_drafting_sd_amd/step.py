@@ -54,9 +54,8 @@ class StepOptions:
     prior_beta: float = 0.0      # fusion: subtract beta x log unigram prior (t["vocab_bias"])
 
     def __post_init__(self):
-        if self.markov_rank and (self.greedy or self.draft_vocab):
-            raise ValueError("the sequential correction samples over the full drafter "
-                             "vocabulary at temperature 1")
+        if self.markov_rank and self.draft_vocab:
+            raise ValueError("the sequential correction works on the full drafter vocabulary")
 
 
 class DraftVerifyStep:
@@ -130,6 +129,7 @@ class DraftVerifyStep:
         return sd_markov_sample(self.logits, t["anchor"], t["markov_w_c"], t["markov_e_c"],
                                 t["q_off"], t["req_id"], seed,
                                 max_draft_k=self.shape.max_draft_k, alpha=o.markov_alpha,
+                                greedy=o.greedy,
                                 vocab_bias=t["vocab_bias"] if o.prior_beta else None, lse=self.lse,
                                 draft_tokens=self.tokens, workspace=self.ws_markov,
                                 stream=stream)

@@ -391,6 +391,7 @@ sd_status sd_lm_head_probs(const void* hidden, const void* w_vocab, int32_t M,
  *   lse[m] = log sum_v exp(logits[m, v])
  *   draft_tokens[m] = y_j = argmax_v (logits[m, v] - log(-log u_v)), the
  *   stream-0 uniforms of (request b, position j), as sd_lm_head_probs draws
+ *   (greedy = 1: argmax_v logits[m, v], no uniforms; smallest index on ties)
  * so W_c = 0 (or alpha = 0) without a bias gives exactly the draws of
  * sd_lm_head_probs.  LongSpark: alpha = 1, vocab_bias = NULL.  DeLS-Spec:
  * vocab_bias = -beta log p~_0 from sd_log_prior_bias.  The positions run in
@@ -405,12 +406,13 @@ sd_status sd_lm_head_probs(const void* hidden, const void* w_vocab, int32_t M,
  *   w_c, e_c bf16 [V, r]  (r a multiple of 16, 16-byte aligned)
  *   alpha    finite scale of the correction
  *   vocab_bias fp32 [V] or NULL
+ *   greedy   0 (sample) or 1 (temperature 0)
  *   q_off    int32 [batch+1]; positions beyond max_draft_k (host bound,
  *            0..4096) are left untouched
  *   req_id, seed: as for sd_lm_head_probs
  *   workspace sd_markov_workspace_size(batch, V, max_draft_k) bytes
  * Errors: NULL -> SD_ERR_NULL; sizes out of range, unaligned tables or a
- * non-finite alpha -> SD_ERR_SHAPE; M == 0 or max_draft_k == 0 -> SD_OK with
+ * non-finite alpha, greedy not 0 or 1 -> SD_ERR_SHAPE; M == 0 or max_draft_k == 0 -> SD_OK with
  * nothing launched; short or unaligned workspace -> SD_ERR_WORKSPACE.
  * ------------------------------------------------------------------------ */
 size_t sd_markov_workspace_size(int32_t batch, int32_t V, int32_t max_draft_k);
@@ -418,7 +420,7 @@ size_t sd_markov_workspace_size(int32_t batch, int32_t V, int32_t max_draft_k);
 sd_status sd_markov_sample(float* logits, float* lse, int32_t* draft_tokens,
                            const int32_t* anchor_tokens, const void* w_c,
                            const void* e_c, float alpha, const float* vocab_bias,
-                           const int32_t* q_off, int32_t batch,
+                           int32_t greedy, const int32_t* q_off, int32_t batch,
                            int32_t M, int32_t V, int32_t r, int32_t max_draft_k,
                            const uint32_t* req_id, uint64_t seed,
                            void* workspace, size_t workspace_bytes, void* stream);

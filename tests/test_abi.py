@@ -205,19 +205,20 @@ def test_schedule_verify_validation(lib, kw, status):
 
 def _mk(lib, **kw):
     a = dict(z=FAKE, lse=FAKE, tok=FAKE, anchor=FAKE, wc=FAKE, ec=FAKE, alpha=1.0, bias=None,
-             qoff=FAKE, batch=2, M=8, V=1000, r=32, k=4, req=FAKE, seed=5, ws=FAKE,
+             greedy=0, qoff=FAKE, batch=2, M=8, V=1000, r=32, k=4, req=FAKE, seed=5, ws=FAKE,
              ws_bytes=1 << 40)
     a.update(kw)
     return lib.sd_markov_sample(a["z"], a["lse"], a["tok"], a["anchor"], a["wc"], a["ec"],
-                                a["alpha"], a["bias"], a["qoff"], a["batch"], a["M"], a["V"],
-                                a["r"], a["k"], a["req"], a["seed"], a["ws"], a["ws_bytes"], None)
+                                a["alpha"], a["bias"], a["greedy"], a["qoff"], a["batch"], a["M"],
+                                a["V"], a["r"], a["k"], a["req"], a["seed"], a["ws"], a["ws_bytes"],
+                                None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(z=None), 1), (dict(anchor=None), 1), (dict(wc=None), 1), (dict(req=None), 1),
     (dict(batch=0), 2), (dict(M=-1), 2), (dict(V=0), 2), (dict(r=0), 2), (dict(r=24), 2),
     (dict(k=-1), 2), (dict(k=5000), 2), (dict(wc=ODD), 2), (dict(ec=ODD), 2),
-    (dict(alpha=float("inf")), 2), (dict(alpha=float("nan")), 2),
+    (dict(alpha=float("inf")), 2), (dict(alpha=float("nan")), 2), (dict(greedy=2), 2),
     (dict(ws=None), 3), (dict(ws_bytes=16), 3), (dict(ws=ODD), 3),
     (dict(M=0), 0), (dict(k=0), 0), (dict(k=0, ws=None), 0),          # nothing to launch
 ])

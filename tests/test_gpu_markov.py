@@ -76,6 +76,27 @@ def test_markov_small(V, r):
     _compare(got, ref, q_off, range(len(d)), f"markov V={V} r={r}")
 
 
+def test_markov_greedy():
+    # temperature 0: each draw is the argmax of the corrected row
+    V, r = 3001, 64
+    rng = np.random.default_rng(55)
+    d = np.array([16, 7, 1])
+    q_off = np.concatenate([[0], np.cumsum(d)]).astype(np.int32)
+    base = rng.normal(0, 2.0, (int(q_off[-1]), V)).astype(np.float32)
+    anchor = rng.integers(0, V, len(d)).astype(np.int32)
+    req_id = rng.integers(0, 2**32, len(d), dtype=np.uint64).astype(np.uint32)
+    w_c, e_c = _tables(V, r, 8, scale=0.4)
+    z = sdev.f32(base, DEV)
+    _, lse, tok = sd.sd_markov_sample(z, sdev.i32(anchor, DEV), sdev.bf16(w_c, DEV),
+                                      sdev.bf16(e_c, DEV), sdev.i32(q_off, DEV),
+                                      sdev.i32(req_id.view(np.int32), DEV), 9, max_draft_k=16,
+                                      greedy=True)
+    torch.cuda.synchronize()
+    got = (z.cpu().numpy(), lse.cpu().numpy(), tok.cpu().numpy())
+    ref = omk.markov_sample(base, q_off, anchor, w_c, e_c, req_id, 9, greedy=True)
+    _compare(got, ref, q_off, range(len(d)), "markov greedy")
+
+
 def test_zero_correction_reproduces_the_lm_head_draws():
     cfg = C1_32K.with_(batch=4, ctx=16, draft_k=(16, 5, 1, 9), hidden=256, vocab=5000, seed=3)
     inp = StepInputs(cfg)
@@ -198,7 +219,7 @@ def _chain_cfg():
                         num_heads_kv=2, head_dim=64, hidden=256, vocab=4100, seed=777)
 
 
-@pytest.mark.parametrize("path", ["longspark", "dels"])
+@pytest.mark.parametrize("path", ["longspark", "dels", "longspark_greedy"])
 def test_step_with_correction_chain(path):
     """Attention -> LM head -> sequential correction -> verification through
     DraftVerifyStep, each stage compared with the oracle on the previous
@@ -210,8 +231,8 @@ def test_step_with_correction_chain(path):
     inp = StepInputs(cfg)
     b = inp.budgets
     r = 64
-    if path == "longspark":
-        opts = StepOptions(window=256, n_summary=16, markov_rank=r)
+    if path.startswith("longspark"):
+        opts = StepOptions(window=256, n_summary=16, markov_rank=r, greedy=path.endswith("greedy"))
     else:
         opts = StepOptions(markov_rank=r, markov_alpha=0.3, prior_beta=0.3)
     t = {}
@@ -265,13 +286,14 @@ def test_step_with_correction_chain(path):
     got = (step.logits.cpu().numpy(), step.lse.cpu().numpy(), step.tokens.cpu().numpy())
     ref_m = omk.markov_sample(base, b.q_off, anchor, w_c, e_c, inp.req_id, seed,
                               alpha=opts.markov_alpha,
-                              vocab_bias=None if bias is None else t["vocab_bias"].cpu().numpy())
+                              vocab_bias=None if bias is None else t["vocab_bias"].cpu().numpy(),
+                              greedy=opts.greedy)
     log(f"{path} chain: base logits max-abs {dz:.2e}")
     assert dz <= 1e-5
     _compare(got, ref_m, b.q_off, reqs, f"{path} chain: correction")
     # 4. verification of the device's corrected drafts
     ref_v = overify.verify(inp.target_logits, b.t_off, got[0].astype(np.float64), got[2], b.q_off,
-                           inp.req_id, seed, requests=list(reqs))
+                           inp.req_id, seed, requests=list(reqs), greedy=opts.greedy)
     rep = compare.verify_report(step.accepted.cpu().numpy(), step.next_token.cpu().numpy(), ref_v,
                                 reqs)
     log(f"{path} chain: verify {rep}")
