@@ -273,8 +273,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is "
-                                   "described in DESIGN.md, not implemented",
+        print(json.dumps({"error": "one GPU only: the step is not sharded across GPUs "
+                                   "(each GPU would run its own requests or KV heads)",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 

@@ -273,3 +273,14 @@ def test_python_binding_checks_array_lengths():
         sd.sd_lm_head_probs(h, wv, q_off, torch.zeros(1, dtype=i32), 0)
     with pytest.raises(ValueError, match="lse"):
         sd.sd_lm_head_probs(h, wv, q_off, torch.zeros(2, dtype=i32), 0, lse=torch.zeros(3))
+
+
+def test_bench_refuses_several_gpus():
+    import json
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
