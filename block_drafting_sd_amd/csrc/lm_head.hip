@@ -3,21 +3,23 @@
 // and App. A.1, Fig. 6: the frozen target vocabulary head produces every
 // slot's base logits in parallel and each slot is sampled independently).
 //
-// lm_gemm<WV>: one workgroup (2 x WV waves) computes a 64 WV-vocab x 256-row
-// tile (128 x 256 with 4 waves for one row tile; 256 x 256 with 8 waves when
-// there are several) of logits^T = W * hidden^T with MFMA 32x32x16 bf16 (fp32
-// accumulation); each wave owns a 64 x 128 sub-tile (8 accumulator tiles).
-// Both operands are H-contiguous.  They stream through a ring of LDS stages
-// of 32 hidden dims (W rows, then 16 KiB of hidden rows, per stage), filled by
-// direct-to-LDS loads: each 1 KiB wave load covers 16 rows x 64 bytes, so
-// global reads stay coalesced, and rows are stored with a 16-byte-chunk XOR
-// swizzle so the MFMA operand reads (32 rows, one chunk) are conflict-free.
-// With 4 waves the ring (3 x 24 KiB) lets two workgroups share a CU: each
-// SIMD then runs two waves whose barriers are independent, so one
-// workgroup's MFMAs cover the other's waits for loads and its epilogue; with
-// 8 waves one workgroup (4 x 32 KiB) fills the CU with the same two waves per
-// SIMD and re-reads the hidden rows half as often.  At up
-// to 256 draft rows the whole W (1.2 GB) is read from HBM exactly once.
+// lm_gemm<WV, BK>: one workgroup (2 x WV waves) computes a 64 WV-vocab x
+// 256-row tile (128 x 256 with 4 waves for one row tile; 256 x 256 with 8
+// waves when there are several) of logits^T = W * hidden^T with MFMA
+// 32x32x16 bf16 (fp32 accumulation); each wave owns a 64 x 128 sub-tile (8
+// accumulator tiles).  Both operands are H-contiguous.  They stream through
+// a ring of LDS stages of BK hidden dims (W rows, then hidden rows, per
+// stage), filled by direct-to-LDS loads: each 1 KiB wave load covers whole
+// BK-dim row segments (16 rows x 64 bytes at BK = 32, 8 rows x 128 bytes at
+// BK = 64), so global reads stay coalesced, and rows are stored with a
+// 16-byte-chunk XOR swizzle so the MFMA operand reads (32 rows, one chunk)
+// are conflict-free.  With 4 waves the ring (3 x 24 KiB) lets two workgroups
+// share a CU: each SIMD then runs two waves whose barriers are independent,
+// so one workgroup's MFMAs cover the other's waits for loads and its
+// epilogue; with 8 waves one workgroup (2 x 64 KiB stages of 64 dims) fills
+// the CU with the same two waves per SIMD, re-reads the hidden rows half as
+// often, loads whole 128-byte lines and passes half as many stage barriers.
+// At up to 256 draft rows the whole W (1.2 GB) is read from HBM exactly once.
 // Tiles are ordered so that all row tiles of one vocab tile, and a compact
 // block of vocab tiles, run together on one XCD (blockIdx % 8 picks the XCD),
 // which keeps every W and hidden slice in that XCD's L2 across row tiles.
@@ -38,36 +40,47 @@ namespace {
 
 constexpr int kThreads = 256;                       // lm_row_reduce: 4 waves
 
-// Workgroup shape by the number of waves along the vocabulary (WV): 2 x WV
-// waves, each owning 64 vocab x 128 rows; a tile is 64 WV vocab x 256 rows.
-//   WV = 2: 128 x 256 tiles, 4 waves, 24 KiB stages, 3 stages: two
+// Workgroup shape by the number of waves along the vocabulary (WV) and the
+// hidden dims per pipeline stage (BK): 2 x WV waves, each owning 64 vocab x
+// 128 rows; a tile is 64 WV vocab x 256 rows.  (Measured at M = 1024: the
+// 256 x 256 tiles with 64-dim stages beat 32-dim stages by 1-3%; at one row
+// tile the 128 x 256 tiles stay ahead.)
+//   WV = 2, BK = 32: 128 x 256 tiles, 4 waves, 24 KiB stages, 3 stages: two
 //           workgroups per CU.
-//   WV = 4: 256 x 256 tiles, 8 waves, 32 KiB stages, 4 stages: one
+//   WV = 4, BK = 64: 256 x 256 tiles, 8 waves, 64 KiB stages, 2 stages: one
 //           workgroup per CU with the same waves per SIMD, a third less
-//           operand traffic per output (hidden is re-read per vocab tile)
-//           and one more stage of lookahead.
-template <int WV>
+//           operand traffic per output (hidden is re-read per vocab tile),
+//           whole 128-byte row segments per load and half as many stage
+//           barriers per MFMA.
+template <int WV, int BK>
 struct LmTile {
   static constexpr int Waves = 2 * WV;
   static constexpr int Threads = 64 * Waves;
   static constexpr int BV = 64 * WV;                      // vocab rows per tile
-  static constexpr int NS = WV == 2 ? 3 : 4;              // LDS stages
-  static constexpr int WBytes = BV * kLmBK * 2;           // W rows of one stage
-  static constexpr int HBytes = kLmBM * kLmBK * 2;        // hidden rows of one stage: 16 KiB
+  static constexpr int RowBytes = 2 * BK;                 // one row of a stage
+  static constexpr int Chunks = BK / 8;                   // 16-byte chunks per row
+  static constexpr int RowsPerLoad = 1024 / RowBytes;     // rows one wave load covers
+  static constexpr int KSteps = BK / 16;                  // MFMA k-steps per stage
+  static constexpr int WBytes = BV * RowBytes;            // W rows of one stage
+  static constexpr int HBytes = kLmBM * RowBytes;         // hidden rows of one stage
   static constexpr int StageBytes = WBytes + HBytes;
+  static constexpr int NS = BK == 32 ? 3 : 2;             // LDS stages (ring)
   static constexpr int WLoads = WBytes / 1024 / Waves;    // direct-to-LDS loads per wave per stage
   static constexpr int HLoads = HBytes / 1024 / Waves;
   static constexpr int Loads = WLoads + HLoads;
+  // 16-byte chunk c of row r of a staged tile sits at byte
+  // RowBytes r + 16 (c ^ swz(r)).  A 256-byte span of LDS covers all 64
+  // banks; the rows sharing one span (256 / RowBytes of them) keep their
+  // chunks in place and consecutive spans rotate them, so 16 consecutive rows
+  // of one chunk fall in 16 different 16-byte bank groups.
+  static __device__ __forceinline__ int swz(int r) { return (r / (256 / RowBytes)) & (Chunks - 1); }
 };
-static_assert(kLmBM == 256 && kLmBK == 32, "stage layout assumes 256-row tiles of 32 dims");
-static_assert(LmTile<2>::BV == kLmBV, "the workspace is sized for the 128-vocab tiles");
-static_assert(LmTile<2>::WLoads == 2 && LmTile<2>::HLoads == 4 && LmTile<4>::WLoads == 2 &&
-              LmTile<4>::HLoads == 2, "loads per wave per stage");
-
-// 16-byte chunk c (of 4) of row r of a staged tile sits at byte
-// 64 r + 16 (c ^ swz(r)): eight consecutive rows of one chunk then fall in
-// eight different 16-byte bank groups.
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+static_assert(kLmBM == 256 && kLmHMultiple % 64 == 0, "stage layout assumes 256-row tiles, H a multiple of 64");
+static_assert(LmTile<2, 32>::BV == kLmBV, "the workspace is sized for the 128-vocab tiles");
+static_assert(LmTile<2, 32>::NS * LmTile<2, 32>::StageBytes == 72 * 1024 &&
+              LmTile<4, 64>::NS * LmTile<4, 64>::StageBytes == 128 * 1024, "two narrow or one wide workgroup per CU");
+static_assert(LmTile<2, 32>::WLoads == 2 && LmTile<2, 32>::HLoads == 4 && LmTile<4, 64>::WLoads == 4 &&
+              LmTile<4, 64>::HLoads == 4, "loads per wave per stage");
 
 __device__ __forceinline__ void row_owner(const LmArgs& a, int m, uint32_t& rid, uint32_t& pos) {
   // request b with q_off[b] <= m < q_off[b+1]
@@ -87,11 +100,12 @@ __device__ __forceinline__ void row_owner(const LmArgs& a, int m, uint32_t& rid,
   pos = static_cast<uint32_t>(m - a.q_off[lo] + 1);
 }
 
-template <int WV>
-__global__ __launch_bounds__(LmTile<WV>::Threads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int WV, int BK>
+__global__ __launch_bounds__((LmTile<WV, BK>::Threads)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void lm_gemm(LmArgs a) {
-  using T = LmTile<WV>;
+  using T = LmTile<WV, BK>;
   constexpr int kNS = T::NS, kStageBytes = T::StageBytes, kWBytes = T::WBytes;
+  constexpr int kRow = T::RowBytes, kChunks = T::Chunks, kRowsPerLoad = T::RowsPerLoad;
   constexpr int kWLoads = T::WLoads, kHLoads = T::HLoads, kLoadsPerWave = T::Loads;
   __shared__ __attribute__((aligned(1024))) char smem[kNS * kStageBytes];
   const int P = blockIdx.x;
@@ -104,18 +118,19 @@ void lm_gemm(LmArgs a) {
   const int wv = wave % WV, wm = wave / WV, h = lane >> 5;
 
   // ------------------------------------------------ direct-to-LDS loads
-  // Wave w fetches W rows 32 w .. 32 w + 31 (loads q = 2 w, 2 w + 1) and
-  // its share of the hidden rows (loads q = HLoads w ..); load q covers
-  // rows 16 q .. 16 q + 15 of its tile and lane l fetches chunk
-  // (l & 3) ^ swz(row) of row 16 q + l / 4.  Rows past V (or M) read the last
-  // row instead and are never stored.
+  // Wave w fetches its share of the W rows (loads q = WLoads w ..) and of
+  // the hidden rows (loads q = HLoads w ..); load q covers rows
+  // RowsPerLoad q .. RowsPerLoad (q + 1) - 1 of its tile, lane l fetching
+  // chunk (l % Chunks) ^ swz(row) of row RowsPerLoad q + l / Chunks, so the
+  // lanes of one row read its whole BK-dim segment.  Rows past V (or M) read
+  // the last row instead and are never stored.
   const uint16_t* src[kLoadsPerWave];
 #pragma unroll
   for (int i = 0; i < kLoadsPerWave; ++i) {
     const bool is_w = i < kWLoads;
     const int q = is_w ? kWLoads * wave + i : kHLoads * wave + (i - kWLoads);
-    const int r = 16 * q + (lane >> 2);
-    const int c = (lane & 3) ^ swz(r);
+    const int r = kRowsPerLoad * q + lane / kChunks;
+    const int c = (lane % kChunks) ^ T::swz(r);
     const int wr = min(v0 + r, a.V - 1);   // drafter vocab entry -> row of W
     src[i] = is_w ? a.w + static_cast<size_t>(a.vmap ? clampi(a.vmap[wr], 0, a.w_rows - 1) : wr) * a.H + 8 * c
                   : a.hidden + static_cast<size_t>(min(m0 + r, a.M - 1)) * a.H + 8 * c;
@@ -127,20 +142,20 @@ void lm_gemm(LmArgs a) {
       constexpr bool is_w = i < kWLoads;
       const uint32_t dst = is_w ? base + (kWLoads * wave + i) * 1024
                                 : base + kWBytes + (kHLoads * wave + (i - kWLoads)) * 1024;
-      dma16(src[i] + kt * kLmBK, dst);
+      dma16(src[i] + kt * BK, dst);
     });
   };
 
   // ---------------------------------------------------- operand offsets
   // A operand (W row 64 wv + 32 tv + l % 32) and B operand (hidden row
-  // 128 wm + 32 tm + l % 32), chunk 2 s + h of the stage's 32 dims.
+  // 128 wm + 32 tm + l % 32), chunk 2 s + h of the stage's BK dims.
   const int rr = lane & 31;
-  const int sw = swz(rr);   // swz(32 k + rr) == swz(rr)
-  int offA[2], offB[2];
+  const int sw = T::swz(rr);   // swz(32 k + rr) == swz(rr)
+  int offA[T::KSteps], offB[T::KSteps];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    offA[s] = (64 * wv + rr) * 64 + (((2 * s + h) ^ sw) << 4);
-    offB[s] = kWBytes + (128 * wm + rr) * 64 + (((2 * s + h) ^ sw) << 4);
+  for (int s = 0; s < T::KSteps; ++s) {
+    offA[s] = (64 * wv + rr) * kRow + (((2 * s + h) ^ sw) << 4);
+    offB[s] = kWBytes + (128 * wm + rr) * kRow + (((2 * s + h) ^ sw) << 4);
   }
 
   f32x16 acc[2][4];
@@ -149,7 +164,7 @@ void lm_gemm(LmArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  const int nk = a.H / kLmBK;
+  const int nk = a.H / BK;
 #pragma unroll
   for (int t = 0; t < kNS - 1; ++t)
     if (t < nk) issue(t);
@@ -161,14 +176,14 @@ void lm_gemm(LmArgs a) {
     if (kt + kNS - 1 < nk) issue(kt + kNS - 1);
     const char* st = smem + (kt % kNS) * kStageBytes;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < T::KSteps; ++s) {
       bf16x8 af[2], bfr[4];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        af[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + offA[s] + t * 32 * 64));
+        af[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + offA[s] + t * 32 * kRow));
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        bfr[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + offB[s] + t * 32 * 64));
+        bfr[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + offB[s] + t * 32 * kRow));
 #pragma unroll
       for (int tv = 0; tv < 2; ++tv)
 #pragma unroll
@@ -290,19 +305,19 @@ __global__ __launch_bounds__(kThreads) void lm_row_reduce(LmArgs a) {
 
 }  // namespace
 
-template <int WV>
+template <int WV, int BK>
 hipError_t launch_gemm(LmArgs& b, hipStream_t s) {
-  b.n_vt = (b.V + LmTile<WV>::BV - 1) / LmTile<WV>::BV;
+  b.n_vt = (b.V + LmTile<WV, BK>::BV - 1) / LmTile<WV, BK>::BV;
   const int slots = (b.n_vt + 7) / 8 * b.n_mt;
-  return launch_kernel(lm_gemm<WV>, dim3(slots * 8), dim3(LmTile<WV>::Threads), s, b);
+  return launch_kernel(lm_gemm<WV, BK>, dim3(slots * 8), dim3(LmTile<WV, BK>::Threads), s, b);
 }
 
 hipError_t launch_lm_head(const LmArgs& a, hipStream_t s) {
-  // several row tiles (M > 256): 256-vocab tiles (measured ~4% faster at
-  // M = 1024); one row tile: 128-vocab tiles, whose 1,187 tiles at V =
-  // 151,936 spread over twice as many resident workgroups
+  // several row tiles (M > 256): 256 x 256 tiles with 64-dim stages; one
+  // row tile: 128-vocab tiles, whose 1,187 tiles at V = 151,936 spread over
+  // twice as many resident workgroups (measured ahead at M = 256)
   LmArgs b = a;
-  hipError_t e = a.n_mt > 1 ? launch_gemm<4>(b, s) : launch_gemm<2>(b, s);
+  hipError_t e = a.n_mt > 1 ? launch_gemm<4, 64>(b, s) : launch_gemm<2, 32>(b, s);
   if (e == hipSuccess) e = launch_kernel(lm_row_reduce, dim3(b.M), dim3(kThreads), s, b);
   return e;
 }

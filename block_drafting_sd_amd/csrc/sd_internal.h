@@ -149,7 +149,6 @@ struct LmArgs {
 
 constexpr int kLmBV = 128;   // vocab rows per workgroup tile
 constexpr int kLmBM = 256;   // draft rows per workgroup tile
-constexpr int kLmBK = 32;    // hidden dims per pipeline stage
 constexpr int kLmHMultiple = 64;   // H must be a multiple of this
 
 hipError_t launch_lm_head(const LmArgs& a, hipStream_t s);

@@ -65,7 +65,8 @@ def test_attention_mha_and_small_groups():
 @pytest.mark.parametrize("M,H,V", [(16, 256, 1024), (5, 64, 1000), (130, 128, 1001),
                                    (257, 512, 4096), (256, 64, 768), (600, 128, 1001),
                                    (1024, 64, 5000),
-                                   (16, 64, 70001), (256, 64, 65600)])
+                                   (16, 64, 70001), (256, 64, 65600),
+                                   (16, 256, 70001), (600, 128, 65600)])
 def test_lm_head_shapes(M, H, V):
     cfg = C0_TINY.with_(name="lm", batch=1, draft_k=M, hidden=H, vocab=V, seed=M * 7 + V)
     inp = StepInputs(cfg)
