@@ -179,6 +179,34 @@ def measured_peaks(dev, read_gib: float = 4.0, mfma_iters: int = 20000, reps: in
             "method": "sd_probe_read / sd_probe_mfma, best of %d launches" % reps}
 
 
+def library_gemm(hidden, w, reps: int = 5, calls: int = 10):
+    """Reference point for the LM head, not a step of the path: the vendor
+    library's plain GEMM (torch.mm -> hipBLASLt) of the same bf16 operands
+    with fp32 output, no softmax statistics or sampling.  Median of ``reps``
+    timings of ``calls`` back-to-back calls (HIP events, current stream)."""
+    import numpy as np
+    import torch
+    out = torch.empty(hidden.shape[0], w.shape[0], dtype=torch.float32, device=hidden.device)
+    wt = w.t()
+    for _ in range(3):
+        torch.mm(hidden, wt, out_dtype=torch.float32, out=out)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(calls):
+            torch.mm(hidden, wt, out_dtype=torch.float32, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1) / calls)
+    del out
+    med = float(np.median(ms))
+    flops = 2.0 * hidden.shape[0] * hidden.shape[1] * w.shape[0]
+    return {"op": "torch.mm bf16 x bf16 -> fp32 (hipBLASLt), same operands, no epilogue",
+            "ms": round(med, 4), "tflops": round(flops / (med * 1e-3) / 1e12, 1)}
+
+
 def bench_schedule(args):
     """ForeSpark's scheduler between verification and drafting: pre-draft
     estimation + joint schedule, then post-draft estimation + budget
@@ -265,7 +293,8 @@ def main():
                          "Markov local head of rank 256, alpha = beta = 0.3)")
     ap.add_argument("--greedy", action="store_true", help="temperature 0 on both sides")
     ap.add_argument("--no-peaks", action="store_true",
-                    help="skip the measured HBM-read and MFMA ceilings (library probes, untimed)")
+                    help="skip the measured HBM-read and MFMA ceilings (library probes, untimed) "
+                         "and the library-GEMM reference of the LM head")
     ap.add_argument("--schedule", action="store_true",
                     help="time the draft / verification scheduler instead of the step "
                          "(192 requests, K = 16, d_h = 4096, r = 256)")
@@ -376,6 +405,8 @@ def main():
     log(f"[bench] timed {args.steps} steps in {elapsed:.3f}s")
 
     peaks = None if args.no_peaks else measured_peaks(dev)
+    lib_gemm = (library_gemm(t["hidden"], t["w_vocab"])
+                if not args.no_peaks and not opts.draft_vocab else None)
     attn_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     lm_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
     mk_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
@@ -445,7 +476,8 @@ def main():
         "lm_head": {"tflops": round(lm_tflops, 1),
                     "frac_mfma_bf16": round(lm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                     "frac_of_measured_mfma": peaks and round(lm_tflops / peaks["mfma_bf16_tflops"], 4),
-                    "w_hbm_gbs": round(v_draft * c.hidden * 2 / (float(lm_ms.mean()) * 1e-3) / 1e9, 1)},
+                    "w_hbm_gbs": round(v_draft * c.hidden * 2 / (float(lm_ms.mean()) * 1e-3) / 1e9, 1),
+                    "library_gemm": lib_gemm},
         "measured_peaks": peaks,
         "emitted_tokens_per_step_last": emitted,
         # one drafter attention layer per step is timed; projections for the
