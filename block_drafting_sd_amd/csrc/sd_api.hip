@@ -33,7 +33,7 @@ struct AttnLayout {
 AttnLayout attn_layout(int32_t batch, int32_t hkv, int32_t head_dim, int64_t max_total_ctx,
                        int32_t split_tokens) {
   AttnLayout L;
-  L.split = sd::attn_split_tokens(hkv, max_total_ctx, split_tokens);
+  L.split = sd::attn_split_tokens(batch, hkv, max_total_ctx, split_tokens);
   L.max_items = sd::attn_max_items(batch, hkv, max_total_ctx, L.split);
   L.off_item_off = 0;
   L.off_lse = align_up(static_cast<size_t>(batch + 1) * sizeof(int32_t));
