@@ -45,7 +45,7 @@ struct AttnArgs {
 constexpr int kAttnRows = 64;        // query rows per (request, kv head) item
 constexpr int kAttnTile = 32;        // keys per inner tile (two 16-token pages)
 constexpr int kAttnStages = 4;       // LDS ring stages of the prefix stream
-constexpr int kAttnMaxSplitPages = 1024;   // split_tokens <= 1024 * 16
+constexpr int kAttnMaxSplitPages = 2048;   // split_tokens <= 2048 * 16
 constexpr int kAttnMaxSummary = 64;  // summary entries per KV head
 
 int64_t attn_max_items(int32_t batch, int32_t hkv, int64_t max_total_ctx,

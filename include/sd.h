@@ -148,9 +148,9 @@ sd_status sd_probe_mfma(int32_t iters, void* sink, void* stream);
  *   head_dim     64 or 128
  *   max_total_ctx  host upper bound on sum_b N_b (sizes the launch)
  *   split_tokens   prefix tokens per split-K work item; 0 lets the library
- *                  choose (a power of two in [2048, 16384] from batch,
+ *                  choose (a power of two in [2048, 32768] from batch,
  *                  num_heads_kv and max_total_ctx); otherwise a multiple of
- *                  64, at most 16384
+ *                  64, at most 32768
  *   softmax_scale  > 0, usually 1/sqrt(head_dim)
  *   block_mask     SD_MASK_NONE or SD_MASK_CAUSAL
  *   window         0 (whole prefix) or W > 0 (the last W prefix tokens)

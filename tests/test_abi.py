@@ -49,8 +49,8 @@ def test_status_strings_and_version(lib):
 def test_workspace_sizes(lib):
     n = lib.sd_draft_attn_workspace_size(16, 32, 8, 128, 16 * 131072, 0)
     # fp32 partials (64 rows x 128 dims) of every prefix item at the automatic
-    # split for 16 x 128K prefixes (16384 tokens)
-    assert n > 16 * 131072 // 16384 * 8 * 64 * 128 * 4
+    # split for 16 x 128K prefixes (32768 tokens)
+    assert n > 16 * 131072 // 32768 * 8 * 64 * 128 * 4
     assert lib.sd_draft_attn_workspace_size(0, 32, 8, 128, 1, 0) == 0
     assert lib.sd_lm_head_workspace_size(256, 151936) >= 256 * (-(-151936 // 128)) * 16
     assert lib.sd_lm_head_workspace_size(0, 10) == 0
