@@ -382,24 +382,27 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    # HIP events on the calls' stream mark the stage boundaries.  Each record
+    # costs a few microseconds of idle GPU between kernels, so only the
+    # boundaries of stages that run are recorded, and a step's first event
+    # also closes the previous step's last stage (one more event ends the
+    # timed region).
+    stages = ["attention", "lm_head"] + (["markov"] if opts.markov_rank else []) + ["verify"] + \
+             (["summary_fold"] if opts.n_summary else [])
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in stages] for _ in range(args.steps)]
+    ev_end = torch.cuda.Event(enable_timing=True)
+    run_stage = {"attention": lambda i: step.attention(t),
+                 "lm_head": lambda i: step.lm_head(t, seed + 1000 + i),
+                 "markov": lambda i: step.markov(t, seed + 1000 + i),
+                 "verify": lambda i: step.verify(t, seed + 1000 + i),
+                 "summary_fold": lambda i: step.summary_fold(t)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        e = ev[i]
-        e[0].record()
-        step.attention(t)
-        e[1].record()
-        step.lm_head(t, seed + 1000 + i)
-        e[2].record()
-        if opts.markov_rank:
-            step.markov(t, seed + 1000 + i)
-        e[3].record()
-        step.verify(t, seed + 1000 + i)
-        e[4].record()
-        if opts.n_summary:
-            step.summary_fold(t)
-        e[5].record()
+        for e, name in zip(ev[i], stages):
+            e.record()
+            run_stage[name](i)
+    ev_end.record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     log(f"[bench] timed {args.steps} steps in {elapsed:.3f}s")
@@ -407,11 +410,13 @@ def main():
     peaks = None if args.no_peaks else measured_peaks(dev)
     lib_gemm = (library_gemm(t["hidden"], t["w_vocab"])
                 if not args.no_peaks and not opts.draft_vocab else None)
-    attn_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    lm_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
-    mk_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
-    ver_ms = np.array([e[3].elapsed_time(e[4]) for e in ev])
-    fold_ms = np.array([e[4].elapsed_time(e[5]) for e in ev])
+    bounds = [e for row in ev for e in row] + [ev_end]
+    durs = [bounds[k].elapsed_time(bounds[k + 1]) for k in range(len(bounds) - 1)]
+    stage_ms = {name: np.array(durs[j::len(stages)]) for j, name in enumerate(stages)}
+    zero = np.zeros(args.steps)
+    attn_ms, lm_ms, ver_ms = stage_ms["attention"], stage_ms["lm_head"], stage_ms["verify"]
+    mk_ms = stage_ms.get("markov", zero)
+    fold_ms = stage_ms.get("summary_fold", zero)
     tokens_per_step = int(b.draft_k.sum())
     ms_per_step = elapsed * 1e3 / args.steps
     value = tokens_per_step * args.steps / elapsed
