@@ -46,6 +46,24 @@ def test_status_strings_and_version(lib):
     assert sd.sd_version() == "0.1.0"
 
 
+@pytest.mark.parametrize("batch,hkv,total,split", [
+    (16, 8, 16 * 131072, 32768),     # 16 x 128K: 512 prefix items of 32K tokens
+    (16, 8, 16 * 32768, 8192),       # 16 x 32K: 512 items of 8K (32K would leave 128)
+    (64, 8, 64 * 4096, 2048),        # 64 x 4K: at most half the mean prefix
+    (128, 8, 3_430_000, 8192),       # ragged mix, mean ~26.8K: half the mean caps it
+    (1, 1, 512, 2048),               # tiny: the 2048-token floor
+])
+def test_automatic_attention_split(lib, batch, hkv, total, split):
+    """The automatic split (largest power of two in [2048, 32768] tokens with
+    at least 512 prefix items and at most half the mean prefix) sizes the
+    workspace exactly as the explicit split does, and unlike its neighbours."""
+    auto = lib.sd_draft_attn_workspace_size(batch, 4 * hkv, hkv, 128, total, 0)
+    assert auto == lib.sd_draft_attn_workspace_size(batch, 4 * hkv, hkv, 128, total, split)
+    for other in (split // 2, split * 2):
+        if 2048 <= other <= 32768 and total // other != total // split:
+            assert auto != lib.sd_draft_attn_workspace_size(batch, 4 * hkv, hkv, 128, total, other)
+
+
 def test_workspace_sizes(lib):
     n = lib.sd_draft_attn_workspace_size(16, 32, 8, 128, 16 * 131072, 0)
     # fp32 partials (64 rows x 128 dims) of every prefix item at the automatic
