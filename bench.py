@@ -59,9 +59,12 @@ def cpu_baseline(inp, n_req: int, target, opts, extra):
     from oracle import step as ostep, summary as osum, verify as overify
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in pools] or [1])
+        blas = ", ".join(sorted({f"{i.get('internal_api', '?')} {i.get('version') or ''}".strip()
+                                 for i in pools})) or "unknown"
     except Exception:  # pragma: no cover
-        threads = 1
+        threads, blas = 1, "unknown"
     b = inp.budgets
     c = inp.cfg
     reqs = list(range(n_req))
@@ -105,7 +108,7 @@ def cpu_baseline(inp, n_req: int, target, opts, extra):
     t4 = time.perf_counter()
     tokens = int(sum(b.draft_k[r] for r in reqs))
     return {"value": tokens / (t4 - t0), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "blas": blas,
             "sample": (f"{n_req} of {c.batch} requests: attention over all "
                        f"{c.num_heads_kv} KV heads at N={int(b.ctx_len[0])}, LM head on "
                        f"{len(rows)} rows x {lm['logits'].shape[1]}"
