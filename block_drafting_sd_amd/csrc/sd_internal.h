@@ -34,7 +34,7 @@ struct AttnArgs {
   const uint16_t* sum_k;  // [hkv][n_summary][D] summary keys, or null
   const float* sum_v;     // [batch][hkv][n_summary][D] summary values
   int32_t n_summary;      // 0 when there is no summary
-  int32_t split_tokens;   // prefix tokens per work item (multiple of 64, <= 8192)
+  int32_t split_tokens;   // prefix tokens per work item (multiple of 64, <= 32768)
   int32_t max_items;      // work items the partial buffers hold
   float scale_log2;       // softmax_scale * log2(e)
   int32_t* item_off;      // [batch + 1] first work item of each request
