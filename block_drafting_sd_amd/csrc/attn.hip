@@ -95,43 +95,76 @@ __device__ __forceinline__ ReqInfo request_info(const AttnArgs& a, int b) {
   return r;
 }
 
-// Exclusive prefix sum of the work items of every request (one workgroup).
+// Work units of a request, by kind: its block (and summary) units, its
+// full-length prefix splits and its shorter last split (0 or 1).
+__device__ __forceinline__ void unit_counts(const AttnArgs& a, const ReqInfo& r, int (&v)[3]) {
+  v[0] = v[1] = v[2] = 0;
+  if (r.kb <= 0) return;
+  v[1] = (r.n - r.a0) / a.split_tokens;
+  v[2] = r.ns - v[1];
+  v[0] = r.per - r.ns;
+}
+
+// Exclusive prefix sums over the requests (one workgroup): of each kind of
+// unit (the execution order) and of the work items (the partials' slots).
 __global__ __launch_bounds__(1024) void attn_worklist(AttnArgs a) {
-  __shared__ int sh[1024];
-  __shared__ int carry;
-  if (threadIdx.x == 0) carry = 0;
+  __shared__ int sh[3][1024];
+  __shared__ int carry[3];
+  const int tid = threadIdx.x;
+  if (tid < 3) carry[tid] = 0;
   __syncthreads();
   for (int base = 0; base < a.batch; base += 1024) {
-    const int b = base + threadIdx.x;
-    int v = 0;
-    if (b < a.batch) {
-      const ReqInfo r = request_info(a, b);
-      v = r.kb > 0 ? a.hkv * r.per : 0;
-    }
-    sh[threadIdx.x] = v;
+    const int b = base + tid;
+    int v[3] = {0, 0, 0};
+    if (b < a.batch) unit_counts(a, request_info(a, b), v);
+#pragma unroll
+    for (int c = 0; c < 3; ++c) sh[c][tid] = v[c];
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
-      const int t = threadIdx.x >= off ? sh[threadIdx.x - off] : 0;
+      int t[3];
+#pragma unroll
+      for (int c = 0; c < 3; ++c) t[c] = tid >= off ? sh[c][tid - off] : 0;
       __syncthreads();
-      sh[threadIdx.x] += t;
+#pragma unroll
+      for (int c = 0; c < 3; ++c) sh[c][tid] += t[c];
       __syncthreads();
     }
-    if (b < a.batch) a.item_off[b] = carry + sh[threadIdx.x] - v;
+    if (b < a.batch) {
+      int units = 0;
+#pragma unroll
+      for (int c = 0; c < 3; ++c) {
+        const int ex = carry[c] + sh[c][tid] - v[c];
+        a.unit_off[c * (a.batch + 1) + b] = ex;
+        units += ex;
+      }
+      a.item_off[b] = a.hkv * units;
+    }
     __syncthreads();
-    if (threadIdx.x == 1023) carry += sh[1023];
+    if (tid == 1023)
+#pragma unroll
+      for (int c = 0; c < 3; ++c) carry[c] += sh[c][1023];
     __syncthreads();
   }
-  if (threadIdx.x == 0) a.item_off[a.batch] = carry;
+  if (tid == 0) {
+#pragma unroll
+    for (int c = 0; c < 3; ++c) a.unit_off[c * (a.batch + 1) + a.batch] = carry[c];
+    a.item_off[a.batch] = a.hkv * (carry[0] + carry[1] + carry[2]);
+  }
 }
 
 // Work item of a workgroup.  A unit is one (request, split) -- a prefix split,
-// the draft block or the summary; its hkv items
-// (one per kv head) read the same pages, whose per-head slices are adjacent
-// in the cache ([page][hkv][...]).  Workgroups are dealt to the 8 XCDs round
-// robin, so blockIdx x runs on XCD x % 8; the mapping below gives the hkv
-// items of a unit consecutive slots on one XCD: they run side by side, share
-// that XCD's L2 and address translations, and fetch each page as one
-// contiguous hkv-slice block.  Returns false past the last item.
+// the draft block or the summary; its hkv items (one per kv head) read the
+// same pages, whose per-head slices are adjacent in the cache
+// ([page][hkv][...]).  Units run in three groups: every block and summary
+// unit (short), then every full-length prefix split, then the requests'
+// shorter last splits, so that with ragged prefix lengths the last
+// workgroups to start are short ones and the kernel's tail stays short.
+// Workgroups are dealt to the 8 XCDs round robin, so blockIdx x runs on XCD
+// x % 8; the mapping below gives the hkv items of a unit consecutive slots on
+// one XCD: they run side by side, share that XCD's L2 and address
+// translations, and fetch each page as one contiguous hkv-slice block.  The
+// item (the slot of its partials) is item_off[b] + g per + split, whatever
+// the order.  Returns false past the last item.
 struct ItemLoc {
   int b, g, sp, item;
   ReqInfo r;
@@ -140,20 +173,28 @@ struct ItemLoc {
 __device__ __forceinline__ bool locate_item(const AttnArgs& a, int block, ItemLoc& L) {
   const int x = block & 7;
   const int k = block >> 3;
-  const int u = (k / a.hkv) * 8 + x;       // unit
+  const int u = (k / a.hkv) * 8 + x;       // unit, in execution order
   L.g = k % a.hkv;
   const int total = min(a.item_off[a.batch], a.max_items);
-  if (u * a.hkv >= total) return false;
-  // request owning the unit: largest b with item_off[b] <= u * hkv
+  const int* eo = a.unit_off;                   // block and summary units
+  const int* fo = eo + (a.batch + 1);           // full-length prefix splits
+  const int* po = fo + (a.batch + 1);           // shorter last splits
+  const int ne = eo[a.batch], nf = fo[a.batch], np = po[a.batch];
+  if (u >= ne + nf + np) return false;
+  const int kind = u < ne ? 0 : (u < ne + nf ? 1 : 2);
+  const int* off = kind == 0 ? eo : (kind == 1 ? fo : po);
+  const int uu = u - (kind == 0 ? 0 : (kind == 1 ? ne : ne + nf));
+  // request owning the unit: largest b with off[b] <= uu (it has a unit of
+  // this kind, since off[b + 1] > uu)
   int lo = 0, hi = a.batch;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (a.item_off[mid] <= u * a.hkv) lo = mid;
+    if (off[mid] <= uu) lo = mid;
     else hi = mid;
   }
   L.b = lo;
   L.r = request_info(a, lo);
-  L.sp = u - a.item_off[lo] / a.hkv;
+  L.sp = kind == 0 ? L.r.ns + (uu - off[lo]) : (kind == 1 ? uu - off[lo] : L.r.ns - 1);
   L.item = a.item_off[lo] + L.g * L.r.per + L.sp;
   return L.item < total;   // item_off beyond the buffers (lengths above max_total_ctx)
 }

@@ -27,7 +27,7 @@ sd_status from_hip(hipError_t e) {
 struct AttnLayout {
   int32_t split;
   int64_t max_items;
-  size_t off_item_off, off_lse, off_o, total;
+  size_t off_item_off, off_unit_off, off_lse, off_o, total;
 };
 
 AttnLayout attn_layout(int32_t batch, int32_t hkv, int32_t head_dim, int64_t max_total_ctx,
@@ -36,7 +36,8 @@ AttnLayout attn_layout(int32_t batch, int32_t hkv, int32_t head_dim, int64_t max
   L.split = sd::attn_split_tokens(batch, hkv, max_total_ctx, split_tokens);
   L.max_items = sd::attn_max_items(batch, hkv, max_total_ctx, L.split);
   L.off_item_off = 0;
-  L.off_lse = align_up(static_cast<size_t>(batch + 1) * sizeof(int32_t));
+  L.off_unit_off = align_up(static_cast<size_t>(batch + 1) * sizeof(int32_t));
+  L.off_lse = L.off_unit_off + align_up(3 * static_cast<size_t>(batch + 1) * sizeof(int32_t));
   L.off_o = L.off_lse + align_up(static_cast<size_t>(L.max_items) * sd::kAttnRows * sizeof(float));
   L.total = L.off_o + align_up(static_cast<size_t>(L.max_items) * sd::kAttnRows * head_dim * sizeof(float));
   return L;
@@ -178,6 +179,7 @@ sd_status sd_draft_attn(const void* q, const void* k_blk, const void* v_blk, con
   a.max_items = static_cast<int32_t>(L.max_items);
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.item_off = reinterpret_cast<int32_t*>(ws + L.off_item_off);
+  a.unit_off = reinterpret_cast<int32_t*>(ws + L.off_unit_off);
   a.part_lse = reinterpret_cast<float*>(ws + L.off_lse);
   a.part_o = reinterpret_cast<float*>(ws + L.off_o);
   return from_hip(sd::launch_draft_attn(a, head_dim, static_cast<hipStream_t>(stream)));

@@ -38,6 +38,8 @@ struct AttnArgs {
   int32_t max_items;      // work items the partial buffers hold
   float scale_log2;       // softmax_scale * log2(e)
   int32_t* item_off;      // [batch + 1] first work item of each request
+  int32_t* unit_off;      // [3][batch + 1] first unit of each request among the block
+                          // (+ summary) units, the full-length and the last prefix splits
   float* part_lse;        // [max_items][64]       (log2 units)
   float* part_o;          // [max_items][D/4][64][4]
 };
