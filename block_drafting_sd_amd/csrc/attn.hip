@@ -107,42 +107,46 @@ __device__ __forceinline__ void unit_counts(const AttnArgs& a, const ReqInfo& r,
 
 // Exclusive prefix sums over the requests (one workgroup): of each kind of
 // unit (the execution order) and of the work items (the partials' slots).
+// 1024 requests per round: a shuffle scan inside each wave, then the sums of
+// the preceding waves.
 __global__ __launch_bounds__(1024) void attn_worklist(AttnArgs a) {
-  __shared__ int sh[3][1024];
+  __shared__ int wsum[3][16];
   __shared__ int carry[3];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if (tid < 3) carry[tid] = 0;
   __syncthreads();
   for (int base = 0; base < a.batch; base += 1024) {
     const int b = base + tid;
     int v[3] = {0, 0, 0};
     if (b < a.batch) unit_counts(a, request_info(a, b), v);
+    int inc[3] = {v[0], v[1], v[2]};
 #pragma unroll
-    for (int c = 0; c < 3; ++c) sh[c][tid] = v[c];
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      int t[3];
-#pragma unroll
-      for (int c = 0; c < 3; ++c) t[c] = tid >= off ? sh[c][tid - off] : 0;
-      __syncthreads();
-#pragma unroll
-      for (int c = 0; c < 3; ++c) sh[c][tid] += t[c];
-      __syncthreads();
-    }
-    if (b < a.batch) {
-      int units = 0;
+    for (int off = 1; off < 64; off <<= 1)
 #pragma unroll
       for (int c = 0; c < 3; ++c) {
-        const int ex = carry[c] + sh[c][tid] - v[c];
-        a.unit_off[c * (a.batch + 1) + b] = ex;
-        units += ex;
+        const int t = __shfl_up(inc[c], off, 64);
+        if (lane >= off) inc[c] += t;
       }
-      a.item_off[b] = a.hkv * units;
-    }
+    if (lane == 63)
+#pragma unroll
+      for (int c = 0; c < 3; ++c) wsum[c][w] = inc[c];
     __syncthreads();
+    int ex[3];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      int acc = carry[c];
+      for (int i = 0; i < w; ++i) acc += wsum[c][i];
+      ex[c] = acc + inc[c] - v[c];
+    }
+    if (b < a.batch) {
+#pragma unroll
+      for (int c = 0; c < 3; ++c) a.unit_off[c * (a.batch + 1) + b] = ex[c];
+      a.item_off[b] = a.hkv * (ex[0] + ex[1] + ex[2]);
+    }
+    __syncthreads();   // every thread has read carry and wsum
     if (tid == 1023)
 #pragma unroll
-      for (int c = 0; c < 3; ++c) carry[c] += sh[c][1023];
+      for (int c = 0; c < 3; ++c) carry[c] = ex[c] + v[c];
     __syncthreads();
   }
   if (tid == 0) {
@@ -525,15 +529,15 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   const int first = a.item_off[b] + g * r.per;
   const int n = min(r.per, a.max_items - first);
   if (n <= 0) return;
-  // Loads are issued eight partials at a time (indices clamped to the last
-  // partial, duplicates weighted zero) so their latencies overlap.
+  // Loads are issued eight partials at a time so their latencies overlap;
+  // past the last partial (a uniform condition) nothing is loaded.
   constexpr int U = 8;
   const float* lse = a.part_lse + static_cast<size_t>(first) * kAttnRows + qi;
   float mx = -INFINITY;
   for (int s0 = 0; s0 < n; s0 += U) {
     float l[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) l[u] = lse[static_cast<size_t>(min(s0 + u, n - 1)) * kAttnRows];
+    for (int u = 0; u < U; ++u) l[u] = s0 + u < n ? lse[static_cast<size_t>(s0 + u) * kAttnRows] : -INFINITY;
 #pragma unroll
     for (int u = 0; u < U; ++u) mx = fmaxf(mx, l[u]);
   }
@@ -546,9 +550,9 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
     f32x4 o[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const size_t it = static_cast<size_t>(min(s0 + u, n - 1));
-      l[u] = lse[it * kAttnRows];
-      o[u] = *reinterpret_cast<const f32x4*>(po + it * kItemStride);
+      const size_t it = static_cast<size_t>(s0 + u);
+      l[u] = s0 + u < n ? lse[it * kAttnRows] : -INFINITY;
+      o[u] = s0 + u < n ? *reinterpret_cast<const f32x4*>(po + it * kItemStride) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {

@@ -140,7 +140,9 @@ sd_status sd_probe_mfma(int32_t iters, void* sink, void* stream);
  *            of logical page n / 16
  *   ctx_len  int32 [batch]  N_b >= 0, N_b <= max_pages * page_size
  *   q_off    int32 [batch+1] non-decreasing, q_off[0] = 0,
- *            q_off[batch] = total_q, 1 <= K_b <= max_draft_k
+ *            q_off[batch] = total_q, 0 <= K_b <= max_draft_k (a request
+ *            with K_b = 0, e.g. one the scheduler gives no drafts, has no
+ *            rows and no work)
  *   max_draft_k  host bound on K_b; (Hq/Hkv) * max_draft_k <= 64
  *   num_pages    rows of the caches (page ids are clamped to it)
  *   page_size    16

@@ -39,6 +39,21 @@ def test_attention_edge_shapes(head_dim, split):
     assert rep["ok"] and rep["rel_l2"] < 1e-2
 
 
+def test_attention_many_requests():
+    """1,100 ragged requests: the work list is built over two 1,024-request
+    rounds, and with 64-token splits the block units, full-length splits and
+    shorter last splits all occur (empty prefixes and K_b = 0 included)."""
+    B = 1100
+    ctx = tuple((0, 17, 64, 100, 300, 1)[i % 6] for i in range(B))
+    kb = tuple((1, 2, 4, 0, 3)[i % 5] for i in range(B))
+    inp = StepInputs(_edge_cfg(batch=B, ctx=("list", ctx), draft_k=("list", kb), num_heads_q=4,
+                               num_heads_kv=1, head_dim=64, seed=1100))
+    log("attention many requests B=1100 split=64")
+    rep = compare.attention_report(gpu_attention(inp, split_tokens=64), oracle_attention(inp))
+    log(str(rep))
+    assert rep["ok"] and rep["rel_l2"] < 1e-2
+
+
 def test_attention_tiny_workload():
     inp = StepInputs(C0_TINY)
     rep = compare.attention_report(gpu_attention(inp), oracle_attention(inp))
