@@ -477,6 +477,9 @@ def main():
                          "markov": round(float(mk_ms.mean()), 4),
                          "verify": round(float(ver_ms.mean()), 4),
                          "summary_fold": round(float(fold_ms.mean()), 4)},
+        "breakdown_median_ms": {k: round(float(np.median(v)), 4)
+                                for k, v in (("attention", attn_ms), ("lm_head", lm_ms),
+                                             ("verify", ver_ms))},
         "breakdown_p10_p90_ms": {k: [round(float(np.percentile(v, 10)), 4),
                                      round(float(np.percentile(v, 90)), 4)]
                                  for k, v in (("attention", attn_ms), ("lm_head", lm_ms),
