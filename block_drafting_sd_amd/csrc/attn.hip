@@ -91,7 +91,9 @@ __device__ __forceinline__ ReqInfo request_info(const AttnArgs& a, int b) {
   r.q0 = clampi(a.q_off[b], 0, a.total_q);
   r.kb = min(clampi(a.q_off[b + 1], r.q0, a.total_q) - r.q0, a.max_draft_k);
   r.ns = (r.n - r.a0 + a.split_tokens - 1) / a.split_tokens;
-  r.per = r.ns + 1 + (a.n_summary > 0 ? 1 : 0);
+  // the draft block rides on the last prefix split; only an empty prefix
+  // needs a block item of its own
+  r.per = r.ns + (r.ns == 0 ? 1 : 0) + (a.n_summary > 0 ? 1 : 0);
   return r;
 }
 
@@ -421,6 +423,22 @@ __device__ __forceinline__ void write_partial(const AttnArgs& a, const AttnState
   }
 }
 
+// The draft block's keys and values for this wave's query rows (attended by
+// the last prefix split of the request, or by its own item when the prefix
+// is empty); with the causal mask, block row j sees block keys 0..j.
+template <int D>
+__device__ __forceinline__ void attend_block(const AttnArgs& a, const ReqInfo& r, int g,
+                                             AttnState<D>& st, int wave, int lane, float sl2) {
+  const int qi = 32 * wave + (lane & 31);
+  const int j = qi / a.group;
+  for (int base = 0; base < r.kb; base += kAttnTile) {
+    KvTile<D> t;
+    load_block_tile<D>(a, g, r.q0, r.kb, base, lane, t);
+    const int hi = min(kAttnTile, r.kb - base);
+    attend_tile<D>(st, t, 0, a.block_mask ? min(hi, j - base + 1) : hi, sl2, lane);
+  }
+}
+
 // One workgroup (two waves) per work item; wave w owns query rows
 // 32w .. 32w+31 of the item's (up to) 64 rows.
 template <int D, int NS>
@@ -490,17 +508,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         attend_tile<D>(st, kv, max(0, r.n0 - first), min(kAttnTile, t_end - first), sl2, lane);
       }
     }
-  } else if (sp == r.ns) {
-    // the draft block; with the causal mask, block row j sees block keys 0..j
+    if (sp == r.ns - 1 && active) attend_block<D>(a, r, g, st, wave, lane, sl2);
+  } else if (sp == r.ns && r.ns == 0) {
+    // an empty prefix: the draft block alone
     if (!active) return;
-    const int qi = 32 * wave + (lane & 31);
-    const int j = qi / a.group;
-    for (int base = 0; base < r.kb; base += kAttnTile) {
-      KvTile<D> t;
-      load_block_tile<D>(a, g, r.q0, r.kb, base, lane, t);
-      const int hi = min(kAttnTile, r.kb - base);
-      attend_tile<D>(st, t, 0, a.block_mask ? min(hi, j - base + 1) : hi, sl2, lane);
-    }
+    attend_block<D>(a, r, g, st, wave, lane, sl2);
   } else {
     // the summary entries
     if (!active) return;
