@@ -48,18 +48,18 @@ namespace sd {
 int32_t attn_split_tokens(int32_t batch, int32_t hkv, int64_t max_total_ctx, int32_t requested) {
   if (requested > 0) return requested;
   // The largest power of two in [2048, 32768] tokens that still leaves at
-  // least 512 prefix items (two per CU) and at most half the mean prefix
-  // length (every request's prefix then spreads over at least two items,
-  // which keeps ragged mixes balanced).  Measured on MI355X (attention call,
-  // % of 8 TB/s): 16 x 32K: 2048 60%, 4096 65%, 8192 67%, 16384 52%;
-  // 16 x 128K: 8192 71%, 16384 73.3%, 32768 73.9%; 64 x 4K: 2048 54%,
-  // 4096 47%; 128 ragged 1K-128K: 4096 66%, 8192 67%, 16384 66%, 32768 56%.
+  // least 512 prefix items (two per CU) and at most the mean prefix length
+  // (a ragged mix's long requests then spread over several items).
+  // Measured on MI355X (attention call, % of 8 TB/s): 16 x 32K: 4096 66%,
+  // 8192 69%, 16384 61%; 16 x 128K: 16384 73.8%, 32768 74.8%; 64 x 4K:
+  // 1024 55%, 2048 60%, 4096 66%; 128 ragged 1K-128K: 4096 68%, 8192 70.0%,
+  // 16384 70.5% (32768 56% before the block keys rode on the last split).
   // Powers of two divide the usual prefix lengths, so no request ends in a
   // short split (6144 at 32K: 54%).
   const int64_t work = static_cast<int64_t>(hkv) * max_total_ctx;
   const int64_t mean = batch > 0 ? max_total_ctx / batch : 0;
   int64_t s = 32768;
-  while (s > 2048 && (work / s < 512 || s > mean / 2)) s >>= 1;
+  while (s > 2048 && (work / s < 512 || s > mean)) s >>= 1;
   static_assert(32768 <= kAttnMaxSplitPages * 16, "split pages staged in LDS");
   return static_cast<int32_t>(s);
 }

@@ -49,13 +49,14 @@ def test_status_strings_and_version(lib):
 @pytest.mark.parametrize("batch,hkv,total,split", [
     (16, 8, 16 * 131072, 32768),     # 16 x 128K: 512 prefix items of 32K tokens
     (16, 8, 16 * 32768, 8192),       # 16 x 32K: 512 items of 8K (32K would leave 128)
-    (64, 8, 64 * 4096, 2048),        # 64 x 4K: at most half the mean prefix
-    (128, 8, 3_430_000, 8192),       # ragged mix, mean ~26.8K: half the mean caps it
+    (64, 8, 64 * 4096, 4096),        # 64 x 4K: at most the mean prefix
+    (128, 8, 3_430_000, 16384),      # ragged mix, mean ~26.8K: the mean caps it
+    (64, 8, 64 * 3000, 2048),        # mean 3000 < 4096
     (1, 1, 512, 2048),               # tiny: the 2048-token floor
 ])
 def test_automatic_attention_split(lib, batch, hkv, total, split):
     """The automatic split (largest power of two in [2048, 32768] tokens with
-    at least 512 prefix items and at most half the mean prefix) sizes the
+    at least 512 prefix items and at most the mean prefix) sizes the
     workspace exactly as the explicit split does, and unlike its neighbours."""
     auto = lib.sd_draft_attn_workspace_size(batch, 4 * hkv, hkv, 128, total, 0)
     assert auto == lib.sd_draft_attn_workspace_size(batch, 4 * hkv, hkv, 128, total, split)
