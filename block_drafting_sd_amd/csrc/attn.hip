@@ -11,7 +11,8 @@
 //   query rows of (b, g) share one item, so every prefix KV byte is read from
 //   HBM exactly once.  Each item writes fp32 partial results (normalised
 //   output and log-sum-exp), which `attn_combine` merges with the log-sum-exp
-//   rule of "LongSpark", App. A.2, eq. (11).  The hkv items of one
+//   rule of "LongSpark", App. A.2, eq. (11); a (b, g) with a single item
+//   writes its bf16 output directly and the merge skips it.  The hkv items of one
 //   (request, split) are given neighbouring workgroup slots on one XCD
 //   (`locate_item`): they walk the same pages, whose per-head slices are
 //   adjacent in the cache, so each page is fetched as one contiguous block
@@ -401,6 +402,33 @@ __device__ __forceinline__ void read_stage(const uint16_t* stage, int lane, KvTi
       t.v[m][p] = load_bf16x8(stage + (D / 16 + p * (D / 32) + m) * 512 + lane * 8);
 }
 
+// The normalised output of one 32-row half written straight to `out` (bf16,
+// nearest even) when the request's KV head has a single work item: the
+// merge of one partial would reproduce exactly these values.
+template <int D>
+__device__ __forceinline__ void write_output(const AttnArgs& a, const AttnState<D>& st, const ReqInfo& r,
+                                             int g, int half, int lane) {
+  const int h = lane >> 5;
+  const float l = st.l + xor_shuffle(st.l, 32);
+  const float inv = 1.f / l;
+  const int qi = 32 * half + (lane & 31);
+  if (qi >= a.group * r.kb) return;
+  const int j = qi / a.group, hh = qi % a.group;
+  uint16_t* op = a.out + (static_cast<size_t>(r.q0 + j) * a.hq + g * a.group + hh) * D;
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt) {
+#pragma unroll
+    for (int ar = 0; ar < 4; ++ar) {
+      const int d4 = 8 * mt + 2 * ar + h;
+      const float v0 = st.o[mt][4 * ar] * inv, v1 = st.o[mt][4 * ar + 1] * inv;
+      const float v2 = st.o[mt][4 * ar + 2] * inv, v3 = st.o[mt][4 * ar + 3] * inv;
+      const uint32_t lo = f32_to_bf16_bits(v0) | (static_cast<uint32_t>(f32_to_bf16_bits(v1)) << 16);
+      const uint32_t hi2 = f32_to_bf16_bits(v2) | (static_cast<uint32_t>(f32_to_bf16_bits(v3)) << 16);
+      *reinterpret_cast<uint2*>(op + 4 * d4) = make_uint2(lo, hi2);
+    }
+  }
+}
+
 // Normalised partial output and log2-sum-exp2 of one 32-row half.
 template <int D>
 __device__ __forceinline__ void write_partial(const AttnArgs& a, const AttnState<D>& st, int item,
@@ -524,7 +552,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   if (!active) return;
 
-  write_partial<D>(a, st, item, wave, lane);
+  if (r.per == 1) write_output<D>(a, st, r, g, wave, lane);
+  else write_partial<D>(a, st, item, wave, lane);
 }
 
 // Merge the partials of one (request, kv head) with the log-sum-exp rule and
@@ -537,7 +566,7 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   const int qi = threadIdx.x & 63;
   const int d4 = blockIdx.y * 4 + (threadIdx.x >> 6);
   const ReqInfo r = request_info(a, b);
-  if (r.kb <= 0 || qi >= a.group * r.kb) return;
+  if (r.kb <= 0 || qi >= a.group * r.kb || r.per == 1) return;   // a single item wrote its rows
   const int first = a.item_off[b] + g * r.per;
   const int n = min(r.per, a.max_items - first);
   if (n <= 0) return;
