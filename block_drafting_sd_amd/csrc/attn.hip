@@ -7,13 +7,15 @@
 //
 // Work decomposition (split-K, flash-decoding style):
 //   item = (request b, kv head g, split s); splits 0..ns_b-1 cover the prefix
-//   in chunks of `split_tokens`, split ns_b covers the draft block.  All G*K_b
+//   in chunks of `split_tokens`, and the last of them also attends the K_b
+//   draft-block keys (an empty prefix gets one item for the block alone; the
+//   fixed-cost context adds one item for the summary entries).  All G*K_b
 //   query rows of (b, g) share one item, so every prefix KV byte is read from
 //   HBM exactly once.  Each item writes fp32 partial results (normalised
 //   output and log-sum-exp), which `attn_combine` merges with the log-sum-exp
 //   rule of "LongSpark", App. A.2, eq. (11); a (b, g) with a single item
-//   writes its bf16 output directly and the merge skips it.  The hkv items of one
-//   (request, split) are given neighbouring workgroup slots on one XCD
+//   writes its bf16 output directly and the merge skips it.  The hkv items of
+//   one (request, split) are given neighbouring workgroup slots on one XCD
 //   (`locate_item`): they walk the same pages, whose per-head slices are
 //   adjacent in the cache, so each page is fetched as one contiguous block
 //   through one L2 and one set of address translations.  With a shuffled
@@ -42,7 +44,6 @@
 #include "sd_internal.h"
 
 #include <float.h>
-
 
 namespace sd {
 
