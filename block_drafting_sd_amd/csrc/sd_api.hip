@@ -60,7 +60,7 @@ LmLayout lm_layout(int32_t M, int32_t V) {
 // ---------------------------------------------------------------- verify
 struct VerifyLayout {
   int32_t n_chunks, n_schunks;
-  size_t off_row, off_samp, total;
+  size_t off_row, off_samp, off_dec, total;
 };
 
 VerifyLayout verify_layout(int32_t batch, int32_t total_q, int32_t R, int32_t V) {
@@ -69,7 +69,8 @@ VerifyLayout verify_layout(int32_t batch, int32_t total_q, int32_t R, int32_t V)
   L.n_schunks = (V + sd::kSampleChunk - 1) / sd::kSampleChunk;
   L.off_row = 0;
   L.off_samp = align_up(static_cast<size_t>(R + total_q) * L.n_chunks * sizeof(float4));
-  L.total = L.off_samp + align_up(static_cast<size_t>(batch) * L.n_schunks * 2 * sizeof(float4));
+  L.off_dec = L.off_samp + align_up(static_cast<size_t>(batch) * L.n_schunks * 2 * sizeof(float4));
+  L.total = L.off_dec + align_up(static_cast<size_t>(batch) * sizeof(float4));
   return L;
 }
 
@@ -497,6 +498,7 @@ sd_status sd_verify(const float* target_logits, const int32_t* t_off, const floa
   a.accept_ratio = accept_ratio;
   a.row_part = reinterpret_cast<float4*>(ws + L.off_row);
   a.samp_part = reinterpret_cast<float4*>(ws + L.off_samp);
+  a.decision = reinterpret_cast<float4*>(ws + L.off_dec);
   a.batch = batch;
   a.total_q = total_q;
   a.R = total_target_rows;

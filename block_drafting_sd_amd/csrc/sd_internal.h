@@ -202,6 +202,7 @@ struct VerifyArgs {
   float* accept_ratio;      // [total_q] or null
   float4* row_part;         // [(R + total_q) * n_chunks] (max, sumexp, argmax, -)
   float4* samp_part;        // [batch * n_schunks * 2]
+  float4* decision;         // [batch] (accepted as int bits or -1, lse_p, lse_q, tested as int bits)
   int32_t batch, total_q, R, V, n_chunks, n_schunks;
   uint32_t key0, key1;
 };

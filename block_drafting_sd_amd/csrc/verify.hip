@@ -6,19 +6,22 @@
 // decoding) and a pruned drafter vocabulary (q_j is zero outside it; "H-Spec",
 // App. B.2).
 //
-// Three launches, no host synchronisation:
+// Three or four launches, no host synchronisation:
 //   1. verify_rowstats  grid (rows x 8192-entry chunks): per chunk (max, sum
 //      exp) of every target row (and of every draft row when no draft lse is
 //      given).  Each thread issues its eight 16-byte loads at once, so the
 //      logits stream through in one pass: HBM-bound.
-//   2. verify_sample    grid (requests x 2048-entry chunks): every workgroup
-//      of a request merges the row statistics it needs, evaluates all of the
-//      request's ratio tests in parallel, takes the first rejection, and
-//      draws Gumbel-max candidates of its vocab chunk from the residual
-//      [p_j - q_j]_+ (and from p_j as the fallback), or from p_{b+1}.  Only
-//      one row per request is read, so the chunks are small to spread that
-//      row over many CUs.
-//   3. verify_finalize  one wavefront per request merges the chunk candidates.
+//   2. verify_decide    one workgroup per request: merges the row statistics
+//      it needs, evaluates all of the request's ratio tests in parallel and
+//      takes the first rejection.  Only for batches of kDecideBatch requests
+//      or more: below that every sampling workgroup takes the decision itself
+//      and the launch is saved.
+//   3. verify_sample    grid (requests x 2048-entry chunks): every workgroup
+//      of a request reads the decision and draws Gumbel-max candidates of its
+//      vocab chunk from the residual [p_j - q_j]_+ (and from p_j as the
+//      fallback), or from p_{b+1}.  Only one row per request is read, so the
+//      chunks are small to spread that row over many CUs.
+//   4. verify_finalize  one wavefront per request merges the chunk candidates.
 #include "sd_common.h"
 #include "sd_internal.h"
 
@@ -29,6 +32,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxVerify = 255;   // b_b handled per request
+// Batch from which the decision gets its own kernel (timed: -13 us at 128
+// requests, -4 us at 64, +3 us at 16 for the extra launch).
+constexpr int kDecideBatch = 48;
 
 // (max, sum exp(x - max), first index of the max) of one vocab chunk of one
 // row.  Thread t holds entries 4 (t + 256 j) + e of the chunk.
@@ -104,28 +110,30 @@ __device__ float merge_row(const float4* part, int n, int& amax) {
   return mx + logf(s);
 }
 
-__global__ __launch_bounds__(kThreads) void verify_sample(VerifyArgs a) {
-  __shared__ float s_lse_p[kMaxVerify + 1];
-  __shared__ int s_amax_p[kMaxVerify + 1];
-  __shared__ float s_lse_q[kMaxVerify];
-  __shared__ int s_ok[kMaxVerify + 1];
-  __shared__ int s_a;
-  __shared__ float shk[kThreads / 64];
-  __shared__ int shi[kThreads / 64];
+// Shared memory of one request's decision.
+struct DecideSmem {
+  float lse_p[kMaxVerify + 1];
+  int amax_p[kMaxVerify + 1];
+  float lse_q[kMaxVerify];
+  int ok[kMaxVerify + 1];
+  float4 dec;   // (accepted as int bits or -1, lse_p, lse_q, tested as int bits)
+};
 
-  const int b = blockIdx.x / a.n_schunks;
-  const int c = blockIdx.x % a.n_schunks;
+// Row statistics, every ratio test and the first rejection of request b, by
+// one workgroup; on return sm.dec holds the decision for every thread.  With
+// `writer` set the workgroup also stores accepted[b] and the accept ratios.
+__device__ void decide_request(const VerifyArgs& a, int b, bool writer, DecideSmem& sm) {
   const int tid = threadIdx.x;
   const int t0 = clampi(a.t_off[b], 0, a.R);
   const int t1 = clampi(a.t_off[b + 1], t0, a.R);
   const int q0 = clampi(a.q_off[b], 0, a.total_q);
   const int kb = clampi(a.q_off[b + 1], q0, a.total_q) - q0;
   if (t1 == t0) {   // no target row: nothing to verify (contract violation)
-    if (c == 0 && tid == 0) a.accepted[b] = 0;
     if (tid == 0) {
-      a.samp_part[blockIdx.x * 2] = make_float4(-FLT_MAX, __int_as_float(-1), 0.f, 0.f);
-      a.samp_part[blockIdx.x * 2 + 1] = make_float4(-FLT_MAX, __int_as_float(-1), 0.f, 0.f);
+      if (writer) a.accepted[b] = 0;
+      sm.dec = make_float4(__int_as_float(-1), 0.f, 0.f, __int_as_float(0));
     }
+    __syncthreads();
     return;
   }
   const int nv = min(min(t1 - t0 - 1, kb), kMaxVerify);
@@ -133,13 +141,13 @@ __global__ __launch_bounds__(kThreads) void verify_sample(VerifyArgs a) {
 
   // A: log-normalisers of the rows this request may touch
   for (int i = tid; i <= nv; i += kThreads)
-    s_lse_p[i] = merge_row(a.row_part + static_cast<size_t>(t0 + i) * a.n_chunks, a.n_chunks,
-                           s_amax_p[i]);
+    sm.lse_p[i] = merge_row(a.row_part + static_cast<size_t>(t0 + i) * a.n_chunks, a.n_chunks,
+                            sm.amax_p[i]);
   for (int i = tid; i < nv; i += kThreads) {
     int unused;
-    s_lse_q[i] = a.draft_lse ? a.draft_lse[q0 + i]
-                             : merge_row(a.row_part + static_cast<size_t>(a.R + q0 + i) * a.n_chunks,
-                                         a.n_chunks, unused);
+    sm.lse_q[i] = a.draft_lse ? a.draft_lse[q0 + i]
+                              : merge_row(a.row_part + static_cast<size_t>(a.R + q0 + i) * a.n_chunks,
+                                          a.n_chunks, unused);
   }
   __syncthreads();
 
@@ -150,21 +158,21 @@ __global__ __launch_bounds__(kThreads) void verify_sample(VerifyArgs a) {
     const int y = clampi(a.tokens[q0 + i], 0, a.V - 1);
     float r = 1.f;
     if (a.greedy) {
-      r = y == s_amax_p[i] ? 1.f : 0.f;
+      r = y == sm.amax_p[i] ? 1.f : 0.f;
     } else {
       const int iy = a.vinv ? a.vinv[y] : y;   // y in the drafter's vocabulary
-      const float lp = a.target[static_cast<size_t>(t0 + i) * a.V + y] - s_lse_p[i];
+      const float lp = a.target[static_cast<size_t>(t0 + i) * a.V + y] - sm.lse_p[i];
       const float lq = iy >= 0 && iy < a.v_draft
-                           ? a.draft[static_cast<size_t>(q0 + i) * a.v_draft + iy] - s_lse_q[i]
+                           ? a.draft[static_cast<size_t>(q0 + i) * a.v_draft + iy] - sm.lse_q[i]
                            : -INFINITY;
       if (expf(lq) > 0.f) r = fminf(1.f, expf(lp - lq));
     }
     const u32x4 w = philox4x32_10(u32x4{0u, static_cast<uint32_t>(j), rid, kStreamAccept},
                                   a.key0, a.key1);
-    s_ok[i] = accept_from_bits(w[0]) < r;
-    if (c == 0 && a.accept_ratio) a.accept_ratio[q0 + i] = r;
+    sm.ok[i] = accept_from_bits(w[0]) < r;
+    if (writer && a.accept_ratio) a.accept_ratio[q0 + i] = r;
   }
-  if (c == 0 && a.accept_ratio)
+  if (writer && a.accept_ratio)
     for (int i = nv + tid; i < kb; i += kThreads) a.accept_ratio[q0 + i] = __int_as_float(0x7fc00000);
   __syncthreads();
 
@@ -172,21 +180,64 @@ __global__ __launch_bounds__(kThreads) void verify_sample(VerifyArgs a) {
   if (tid == 0) {
     int acc = nv;
     for (int i = 0; i < nv; ++i)
-      if (!s_ok[i]) {
+      if (!sm.ok[i]) {
         acc = i;
         break;
       }
-    s_a = acc;
-    if (c == 0) a.accepted[b] = acc;
+    if (writer) a.accepted[b] = acc;
+    const bool residual = !a.greedy && acc < nv;
+    sm.dec = make_float4(__int_as_float(acc), sm.lse_p[acc], residual ? sm.lse_q[acc] : 0.f,
+                         __int_as_float(nv));
   }
   __syncthreads();
-  const int acc = s_a;
+}
+
+// Large batches: one workgroup per request decides once and stores the
+// decision for the request's sampling workgroups.
+__global__ __launch_bounds__(kThreads) void verify_decide(VerifyArgs a) {
+  __shared__ DecideSmem sm;
+  decide_request(a, blockIdx.x, true, sm);
+  if (threadIdx.x == 0) a.decision[blockIdx.x] = sm.dec;
+}
+
+// Every workgroup of a request draws Gumbel-max candidates of its vocab chunk
+// after the request's decision: from the residual [p_j - q_j]_+ (and from p_j
+// as the fallback) at the first rejection, or from p_{b+1} when every test
+// passed.  kDecided: the decision comes from verify_decide; otherwise every
+// workgroup takes it itself (one launch fewer, for small batches).
+template <bool kDecided>
+__global__ __launch_bounds__(kThreads) void verify_sample(VerifyArgs a) {
+  __shared__ float shk[kThreads / 64];
+  __shared__ int shi[kThreads / 64];
+  const int b = blockIdx.x / a.n_schunks;
+  const int c = blockIdx.x % a.n_schunks;
+  const int tid = threadIdx.x;
+  float4 dec;
+  if constexpr (kDecided) {
+    dec = a.decision[b];
+  } else {
+    __shared__ DecideSmem sm;
+    decide_request(a, b, c == 0, sm);
+    dec = sm.dec;
+  }
+  const int acc = __float_as_int(dec.x);
+  if (acc < 0) {   // no target row
+    if (tid == 0) {
+      a.samp_part[blockIdx.x * 2] = make_float4(-FLT_MAX, __int_as_float(-1), 0.f, 0.f);
+      a.samp_part[blockIdx.x * 2 + 1] = make_float4(-FLT_MAX, __int_as_float(-1), 0.f, 0.f);
+    }
+    return;
+  }
+  const int nv = __float_as_int(dec.w);
+  const int t0 = clampi(a.t_off[b], 0, a.R);
+  const int q0 = clampi(a.q_off[b], 0, a.total_q);
+  const uint32_t rid = a.req_id[b];
   const bool residual = !a.greedy && acc < nv;
   const int j = acc + 1;                      // position of the drawn token
   const float* xrow = a.target + static_cast<size_t>(t0 + acc) * a.V;
   const float* zrow = a.draft + static_cast<size_t>(q0 + acc) * a.v_draft;
-  const float lse_p = s_lse_p[acc];
-  const float lse_q = residual ? s_lse_q[acc] : 0.f;
+  const float lse_p = dec.y;
+  const float lse_q = dec.z;
 
   // D: Gumbel-max candidates of this vocab chunk; thread t holds entries
   // 4 (t + 256 j) + e of the chunk
@@ -274,7 +325,13 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t s) {
   const int rows = a.R + (a.draft_lse ? 0 : a.total_q);
   hipError_t e = hipSuccess;
   if (rows > 0) e = launch_kernel(verify_rowstats, dim3(rows * a.n_chunks), dim3(kThreads), s, a);
-  if (e == hipSuccess) e = launch_kernel(verify_sample, dim3(a.batch * a.n_schunks), dim3(kThreads), s, a);
+  const dim3 sgrid(a.batch * a.n_schunks);
+  if (a.batch >= kDecideBatch) {
+    if (e == hipSuccess) e = launch_kernel(verify_decide, dim3(a.batch), dim3(kThreads), s, a);
+    if (e == hipSuccess) e = launch_kernel(verify_sample<true>, sgrid, dim3(kThreads), s, a);
+  } else if (e == hipSuccess) {
+    e = launch_kernel(verify_sample<false>, sgrid, dim3(kThreads), s, a);
+  }
   if (e == hipSuccess)
     e = launch_kernel(verify_finalize, dim3(a.batch), dim3(64), s, a);
   return e;

@@ -137,9 +137,10 @@ def test_verify_only_random_drafts(verify_mode, V):
     assert rep["ok"] and rr["max_abs"] < 1e-5
 
 
-def test_verify_drafts_from_q_accept_often():
+@pytest.mark.parametrize("batch", [32, 64])
+def test_verify_drafts_from_q_accept_often(batch):
     # target = draft logits + small noise: long accepted runs, bonus tokens
-    cfg = C0_TINY.with_(name="verify_close", batch=32, ctx=16, draft_k=8, verify="full",
+    cfg = C0_TINY.with_(name="verify_close", batch=batch, ctx=16, draft_k=8, verify="full",
                         vocab=3000, seed=5, target=("normal", 1.0))
     inp = StepInputs(cfg)
     b = inp.budgets
@@ -156,6 +157,25 @@ def test_verify_drafts_from_q_accept_often():
     rep = compare.verify_report(acc, nxt, ref, range(cfg.batch))
     log(f"verify close {rep}")
     assert rep["ok"] and rep["mean_accepted"] > 4
+
+
+@pytest.mark.parametrize("batch", [47, 48, 130])
+def test_verify_either_side_of_the_decision_kernel(batch):
+    # below 48 requests every sampling workgroup takes its request's decision;
+    # from 48 on a separate kernel decides once per request
+    cfg = C0_TINY.with_(name="verify_batches", batch=batch, ctx=16, draft_k=(0, 1, 5, 16),
+                        verify="full", vocab=9000, seed=batch, target=("normal", 1.0))
+    inp = StepInputs(cfg)
+    b = inp.budgets
+    dl = inp.random_draft_logits(sigma=1.0)
+    dt = inp.random_draft_tokens()
+    acc, nxt, ratio = _verify_gpu(inp, dl, dt)
+    ref = overify.verify(inp.target_logits, b.t_off, dl, dt, b.q_off, inp.req_id,
+                         inp.philox_seed)
+    rep = compare.verify_report(acc, nxt, ref, range(cfg.batch))
+    rr = compare.ratio_report(ratio, ref, b.q_off, range(cfg.batch))
+    log(f"verify batch={batch} {rep} ratio {rr}")
+    assert rep["ok"] and rr["max_abs"] < 1e-5
 
 
 # ---------------------------------------------------------------- whole step

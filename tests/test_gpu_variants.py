@@ -246,9 +246,10 @@ def _verify_inputs(inp, rng, vd=None):
     return z, tok, vmap
 
 
+@pytest.mark.parametrize("batch", [24, 56])
 @pytest.mark.parametrize("mode", ["greedy", "pruned", "greedy_pruned"])
-def test_verify_greedy_and_pruned(mode):
-    inp = StepInputs(_lm_cfg(batch=24, ctx=16, draft_k=(16, 7, 1), verify="uniform",
+def test_verify_greedy_and_pruned(mode, batch):
+    inp = StepInputs(_lm_cfg(batch=batch, ctx=16, draft_k=(16, 7, 1), verify="uniform",
                              vocab=20000, seed=3131))
     b = inp.budgets
     greedy = mode.startswith("greedy")
