@@ -85,10 +85,10 @@ def sd_probe_mfma(iters: int, sink=None, device=None, stream=None):
     return int(lib.sd_probe_mfma_flops(int(iters)))
 
 
-def draft_attn_workspace_size(batch, num_heads_q, num_heads_kv, head_dim, max_total_ctx,
-                              split_tokens=0) -> int:
+def draft_attn_workspace_size(batch, num_heads_q, num_heads_kv, head_dim, max_draft_k,
+                              max_total_ctx, split_tokens=0) -> int:
     return int(load().sd_draft_attn_workspace_size(batch, num_heads_q, num_heads_kv, head_dim,
-                                                   max_total_ctx, split_tokens))
+                                                   max_draft_k, max_total_ctx, split_tokens))
 
 
 def lm_head_workspace_size(M, V) -> int:
@@ -137,7 +137,8 @@ def sd_draft_attn(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_len, q_off,
         raise ValueError("k_blk and v_blk must be [total_q, Hkv, D]")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
-    nbytes = lib.sd_draft_attn_workspace_size(batch, hq, hkv, D, max_total_ctx, split_tokens)
+    nbytes = lib.sd_draft_attn_workspace_size(batch, hq, hkv, D, max_draft_k, max_total_ctx,
+                                              split_tokens)
     workspace = _workspace(workspace, nbytes, dev)
     if out is None:
         out = torch.empty_like(q)
@@ -324,7 +325,17 @@ def sd_verify(target_logits, t_off, draft_logits, draft_lse, draft_tokens, q_off
         accept_ratio = torch.empty(total_q, dtype=torch.float32, device=dev)
     nbytes = lib.sd_verify_workspace_size(batch, total_q, R, V)
     workspace = _workspace(workspace, nbytes, dev)
-    v_draft = draft_logits.shape[1] if draft_logits.dim() == 2 else V
+    if draft_logits.dim() != 2:
+        raise ValueError("draft_logits must be [total_q, V] (or [total_q, V_draft] with "
+                         "draft_vocab_inv)")
+    v_draft = draft_logits.shape[1]
+    if draft_vocab_inv is None and v_draft != V:
+        # without a vocabulary map the library reads draft rows with the
+        # target's row length
+        raise ValueError(f"draft_logits has rows of {v_draft} entries; without draft_vocab_inv "
+                         f"they must have V = {V}")
+    if draft_vocab_inv is not None and draft_lse is None:
+        raise ValueError("a pruned drafter vocabulary (draft_vocab_inv) needs draft_lse")
     _need(q_off, batch + 1, "q_off")
     _need(req_id, batch, "req_id")
     _need(draft_logits, total_q * v_draft, "draft_logits")

@@ -24,7 +24,7 @@ SIGNATURES = {
     "sd_probe_read": (_i32, [_vp, _sz, _vp, _vp]),
     "sd_probe_mfma_flops": (_i64, [_i32]),
     "sd_probe_mfma": (_i32, [_i32, _vp, _vp]),
-    "sd_draft_attn_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i64, _i32]),
+    "sd_draft_attn_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i64, _i32]),
     "sd_draft_attn": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                              _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                              _i64, _i32, _f32, _i32, _i32, _vp, _vp, _i32,

@@ -63,13 +63,19 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
                    f"-I{INCLUDE}", f"-I{CSRC}", "-c", s, "-o", o]
             if verbose:
                 print(" ".join(cmd), flush=True)
-            procs.append((s, subprocess.Popen(cmd, stdout=subprocess.PIPE,
-                                              stderr=subprocess.STDOUT, text=True)))
+            # compiler output goes to a file: a pipe nobody reads while
+            # waiting for another job would stall a chatty compile
+            log = open(o + ".log", "w+")
+            procs.append((s, subprocess.Popen(cmd, stdout=log, stderr=subprocess.STDOUT,
+                                              text=True), log))
             objs.append(o)
-            while len([p for _, p in procs if p.poll() is None]) >= jobs:
-                procs[0][1].wait()
-        for s, p in procs:
-            out, _ = p.communicate()
+            while len([p for _, p, _ in procs if p.poll() is None]) >= jobs:
+                next(p for _, p, _ in procs if p.poll() is None).wait()
+        for s, p, log in procs:
+            p.wait()
+            log.seek(0)
+            out = log.read()
+            log.close()
             keep = [l for l in out.splitlines() if "packed-fp32-ops" not in l]
             if p.returncode != 0:
                 raise RuntimeError(f"hipcc failed on {s}:\n" + "\n".join(keep))

@@ -68,9 +68,11 @@ int32_t attn_split_tokens(int32_t batch, int32_t hkv, int64_t max_total_ctx, int
 
 int64_t attn_max_items(int32_t batch, int32_t hkv, int64_t max_total_ctx,
                        int32_t split_tokens) {
-  // sum_b (ceil(N_b / S) + 2) <= sum_b N_b / S + 3 * batch (a window only
-  // shortens the streamed range)
-  return static_cast<int64_t>(hkv) * (max_total_ctx / split_tokens + 3 * static_cast<int64_t>(batch));
+  // A request has ceil(N_b / S) prefix items (one block item instead when
+  // N_b = 0) and at most one summary item: fewer than N_b / S + 2 (exactly
+  // that at N_b = 0), so the integer sum is at most floor(sum_b N_b / S) +
+  // 2 * batch (a window only shortens the streamed range)
+  return static_cast<int64_t>(hkv) * (max_total_ctx / split_tokens + 2 * static_cast<int64_t>(batch));
 }
 
 namespace {
@@ -183,7 +185,11 @@ __device__ __forceinline__ bool locate_item(const AttnArgs& a, int block, ItemLo
   const int k = block >> 3;
   const int u = (k / a.hkv) * 8 + x;       // unit, in execution order
   L.g = k % a.hkv;
-  const int total = min(a.item_off[a.batch], a.max_items);
+  // Work items beyond the partials' capacity (the prefix lengths add up to
+  // more than the host bound) make the whole call invalid: nothing is
+  // computed and attn_combine marks every row
+  if (a.item_off[a.batch] > a.max_items) return false;
+  const int total = a.item_off[a.batch];
   const int* eo = a.unit_off;                   // block and summary units
   const int* fo = eo + (a.batch + 1);           // full-length prefix splits
   const int* po = fo + (a.batch + 1);           // shorter last splits
@@ -204,7 +210,7 @@ __device__ __forceinline__ bool locate_item(const AttnArgs& a, int block, ItemLo
   L.r = request_info(a, lo);
   L.sp = kind == 0 ? L.r.ns + (uu - off[lo]) : (kind == 1 ? uu - off[lo] : L.r.ns - 1);
   L.item = a.item_off[lo] + L.g * L.r.per + L.sp;
-  return L.item < total;   // item_off beyond the buffers (lengths above max_total_ctx)
+  return L.item < total;
 }
 
 // Workgroups covering every item under locate_item's mapping.
@@ -367,6 +373,7 @@ constexpr int stage_elems() { return (D / 8) * 512; }
 //          fetches dims 16 c + 8 h .. +8 of the key that S^T row rho holds.
 //  wave 1: value chunk (page p, dims 32 m ..): lane l fetches 8 tokens
 //          8 h .. 8 h + 7 of dim 32 m + l % 32.
+//  other waves: nothing.
 template <int D>
 __device__ __forceinline__ void issue_stage(const AttnArgs& a, int g, int pg0, int pg1, int wave,
                                             int lane, uint16_t* stage) {
@@ -379,7 +386,7 @@ __device__ __forceinline__ void issue_stage(const AttnArgs& a, int g, int pg0, i
     const uint16_t* src =
         a.k_cache + (static_cast<size_t>(pg) * a.hkv + g) * (D * 16) + h * 128 + slot * 8;
     static_for<0, D / 16>([&](auto c) { dma16(src + c * 256, lds + c * 1024); });
-  } else {
+  } else if (wave == 1) {
     const size_t col = (lane & 31) * 16 + 8 * h;
     const uint16_t* src0 = a.v_cache + (static_cast<size_t>(pg0) * a.hkv + g) * (D * 16) + col;
     const uint16_t* src1 = a.v_cache + (static_cast<size_t>(pg1) * a.hkv + g) * (D * 16) + col;
@@ -401,6 +408,34 @@ __device__ __forceinline__ void read_stage(const uint16_t* stage, int lane, KvTi
 #pragma unroll
     for (int p = 0; p < 2; ++p)
       t.v[m][p] = load_bf16x8(stage + (D / 16 + p * (D / 32) + m) * 512 + lane * 8);
+}
+
+// Value rows of the keys outside [lo, hi) of a staged tile are set to zero.
+// Their weights are already zero, but a cache slot past a request's last
+// token (or outside its window) holds whatever the target left there, and a
+// NaN or infinity times a zero weight would still reach the output.  Element
+// e of v[m][p] is key 16 p + 8 h + e of the tile (h = lane / 32); each 32-bit
+// word holds two consecutive keys, the lower one in its low half.
+template <int D>
+__device__ __forceinline__ void zero_values_outside(KvTile<D>& t, int lo, int hi, int lane) {
+  const int h = lane >> 5;
+  uint32_t keep[2][4];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int k = 16 * p + 8 * h + 2 * w;
+      keep[p][w] = (k >= lo && k < hi ? 0x0000ffffu : 0u) | (k + 1 >= lo && k + 1 < hi ? 0xffff0000u : 0u);
+    }
+#pragma unroll
+  for (int m = 0; m < D / 32; ++m)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      u32x4 v = __builtin_bit_cast(u32x4, t.v[m][p]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) v[w] &= keep[p][w];
+      t.v[m][p] = __builtin_bit_cast(bf16x8, v);
+    }
 }
 
 // The normalised output of one 32-row half written straight to `out` (bf16,
@@ -435,11 +470,12 @@ template <int D>
 __device__ __forceinline__ void write_partial(const AttnArgs& a, const AttnState<D>& st, int item,
                                               int half, int lane) {
   const int h = lane >> 5;
-  float* po = a.part_o + static_cast<size_t>(item) * (D / 4) * kAttnRows * 4;
+  const int R = a.rows;
+  float* po = a.part_o + static_cast<size_t>(item) * (D / 4) * R * 4;
   const float l = st.l + xor_shuffle(st.l, 32);
   const float inv = 1.f / l;
   const int qi = 32 * half + (lane & 31);
-  if (h == 0) a.part_lse[static_cast<size_t>(item) * kAttnRows + qi] = st.m + log2f(l);
+  if (h == 0) a.part_lse[static_cast<size_t>(item) * R + qi] = st.m + log2f(l);
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) {
 #pragma unroll
@@ -447,7 +483,7 @@ __device__ __forceinline__ void write_partial(const AttnArgs& a, const AttnState
       const int d4 = 8 * mt + 2 * ar + h;
       f32x4 v = {st.o[mt][4 * ar] * inv, st.o[mt][4 * ar + 1] * inv, st.o[mt][4 * ar + 2] * inv,
                  st.o[mt][4 * ar + 3] * inv};
-      *reinterpret_cast<f32x4*>(po + (static_cast<size_t>(d4) * kAttnRows + qi) * 4) = v;
+      *reinterpret_cast<f32x4*>(po + (static_cast<size_t>(d4) * R + qi) * 4) = v;
     }
   }
 }
@@ -468,11 +504,15 @@ __device__ __forceinline__ void attend_block(const AttnArgs& a, const ReqInfo& r
   }
 }
 
-// One workgroup (two waves) per work item; wave w owns query rows
-// 32w .. 32w+31 of the item's (up to) 64 rows.
-template <int D, int NS>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_splitk(AttnArgs a) {
+// One workgroup (W waves) per work item; wave w owns query rows
+// 32w .. 32w+31 of the item's (up to) 32 W rows.  Waves 0 and 1 load the
+// stages (keys, values); with W = 4 (more than 64 rows: large GQA groups)
+// the two other waves only compute, from the same stages, so every KV byte
+// is still read once per (request, KV head).
+template <int D, int NS, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_splitk(AttnArgs a) {
   static_assert(NS >= 2, "at least two stages");
+  static_assert(W == 2 || W == 4, "two or four waves");
   __shared__ __attribute__((aligned(1024))) uint16_t s_kv[NS * stage_elems<D>()];
   __shared__ int s_pages[kAttnMaxSplitPages];
 
@@ -509,7 +549,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int t_end = min(r.n, t_begin + a.split_tokens);
     const int n_pages = (t_end - t_begin + 15) >> 4;
     const int* pt = a.page_table + static_cast<size_t>(b) * a.max_pages + (t_begin >> 4);
-    for (int i = threadIdx.x; i < 2 * ((n_pages + 1) >> 1); i += 128)
+    for (int i = threadIdx.x; i < 2 * ((n_pages + 1) >> 1); i += 64 * W)
       s_pages[i] = clampi(pt[min(i, n_pages - 1)], 0, a.num_pages - 1);
     // Q operands loaded (a wait the compiler sees, so that it does not keep
     // a wait for them inside the stream loop) and page ids visible
@@ -534,7 +574,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         KvTile<D> kv;
         read_stage<D>(s_kv + (t % NS) * stage_elems<D>(), lane, kv);
         const int first = t_begin + t * kAttnTile;
-        attend_tile<D>(st, kv, max(0, r.n0 - first), min(kAttnTile, t_end - first), sl2, lane);
+        const int lo = max(0, r.n0 - first), hi = min(kAttnTile, t_end - first);
+        if (lo > 0 || hi < kAttnTile) zero_values_outside<D>(kv, lo, hi, lane);
+        attend_tile<D>(st, kv, lo, hi, sl2, lane);
       }
     }
     if (sp == r.ns - 1 && active) attend_block<D>(a, r, g, st, wave, lane, sl2);
@@ -558,33 +600,44 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // Merge the partials of one (request, kv head) with the log-sum-exp rule and
-// write bf16 outputs.  Block: 64 query rows x 4 float4 columns.
+// write bf16 outputs.  Block: 64 query rows (the z-th 64 of the item's rows)
+// x 4 float4 columns.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   const int pair = blockIdx.x;
   const int b = pair / a.hkv;
   const int g = pair % a.hkv;
-  const int qi = threadIdx.x & 63;
+  const int qi = 64 * blockIdx.z + (threadIdx.x & 63);
   const int d4 = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int R = a.rows;
   const ReqInfo r = request_info(a, b);
-  if (r.kb <= 0 || qi >= a.group * r.kb || r.per == 1) return;   // a single item wrote its rows
+  if (r.kb <= 0 || qi >= a.group * r.kb) return;
   const int first = a.item_off[b] + g * r.per;
-  const int n = min(r.per, a.max_items - first);
-  if (n <= 0) return;
+  const int j = qi / a.group, hh = qi % a.group;
+  uint16_t* op = a.out + (static_cast<size_t>(r.q0 + j) * a.hq + g * a.group + hh) * D + 4 * d4;
+  if (a.item_off[a.batch] > a.max_items) {
+    // The work items did not fit the partials (the prefix lengths add up to
+    // more than the host bound they were sized for) and nothing was
+    // computed: every row is marked NaN rather than left stale.
+    *reinterpret_cast<uint2*>(op) = make_uint2(0x7fc07fc0u, 0x7fc07fc0u);
+    return;
+  }
+  if (r.per == 1) return;   // a single item wrote its rows
+  const int n = r.per;
   // Loads are issued eight partials at a time so their latencies overlap;
   // past the last partial (a uniform condition) nothing is loaded.
   constexpr int U = 8;
-  const float* lse = a.part_lse + static_cast<size_t>(first) * kAttnRows + qi;
+  const float* lse = a.part_lse + static_cast<size_t>(first) * R + qi;
   float mx = -INFINITY;
   for (int s0 = 0; s0 < n; s0 += U) {
     float l[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) l[u] = s0 + u < n ? lse[static_cast<size_t>(s0 + u) * kAttnRows] : -INFINITY;
+    for (int u = 0; u < U; ++u) l[u] = s0 + u < n ? lse[static_cast<size_t>(s0 + u) * R] : -INFINITY;
 #pragma unroll
     for (int u = 0; u < U; ++u) mx = fmaxf(mx, l[u]);
   }
-  const float* po = a.part_o + ((static_cast<size_t>(first) * (D / 4) + d4) * kAttnRows + qi) * 4;
-  constexpr size_t kItemStride = static_cast<size_t>(D / 4) * kAttnRows * 4;
+  const float* po = a.part_o + ((static_cast<size_t>(first) * (D / 4) + d4) * R + qi) * 4;
+  const size_t item_stride = static_cast<size_t>(D / 4) * R * 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   for (int s0 = 0; s0 < n; s0 += U) {
@@ -593,8 +646,8 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const size_t it = static_cast<size_t>(s0 + u);
-      l[u] = s0 + u < n ? lse[it * kAttnRows] : -INFINITY;
-      o[u] = s0 + u < n ? *reinterpret_cast<const f32x4*>(po + it * kItemStride) : f32x4{0.f, 0.f, 0.f, 0.f};
+      l[u] = s0 + u < n ? lse[it * R] : -INFINITY;
+      o[u] = s0 + u < n ? *reinterpret_cast<const f32x4*>(po + it * item_stride) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -604,8 +657,6 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
     }
   }
   acc *= 1.f / wsum;
-  const int j = qi / a.group, hh = qi % a.group;
-  uint16_t* op = a.out + (static_cast<size_t>(r.q0 + j) * a.hq + g * a.group + hh) * D + 4 * d4;
   const uint32_t lo = f32_to_bf16_bits(acc[0]) | (static_cast<uint32_t>(f32_to_bf16_bits(acc[1])) << 16);
   const uint32_t hi2 = f32_to_bf16_bits(acc[2]) | (static_cast<uint32_t>(f32_to_bf16_bits(acc[3])) << 16);
   *reinterpret_cast<uint2*>(op) = make_uint2(lo, hi2);
@@ -615,8 +666,10 @@ template <int D>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
   hipError_t e = launch_kernel(attn_worklist, dim3(1), dim3(1024), s, a);
   if (e == hipSuccess && a.max_items > 0)
-    e = launch_kernel(attn_splitk<D, kAttnStages>, dim3(attn_grid(a)), dim3(128), s, a);
-  if (e == hipSuccess) e = launch_kernel(attn_combine<D>, dim3(a.batch * a.hkv, D / 16), dim3(256), s, a);
+    e = a.rows > 64 ? launch_kernel(attn_splitk<D, kAttnStages, 4>, dim3(attn_grid(a)), dim3(256), s, a)
+                    : launch_kernel(attn_splitk<D, kAttnStages, 2>, dim3(attn_grid(a)), dim3(128), s, a);
+  if (e == hipSuccess)
+    e = launch_kernel(attn_combine<D>, dim3(a.batch * a.hkv, D / 16, a.rows / 64), dim3(256), s, a);
   return e;
 }
 

@@ -1,7 +1,9 @@
-// C ABI of the draft-and-verify step (declared in include/sd.h): host-side
+// C ABI of the draft-and-verify step (declared in include/sd.h, the ceiling
+// probes in include/sd_probe.h): host-side
 // validation, workspace layout and kernel launches.  No allocation, no
 // synchronisation, no reads of device memory.
 #include "sd.h"
+#include "sd_probe.h"
 
 #include <math.h>
 
@@ -25,21 +27,22 @@ sd_status from_hip(hipError_t e) {
 
 // ------------------------------------------------------------ attention
 struct AttnLayout {
-  int32_t split;
+  int32_t split, rows;
   int64_t max_items;
   size_t off_item_off, off_unit_off, off_lse, off_o, total;
 };
 
-AttnLayout attn_layout(int32_t batch, int32_t hkv, int32_t head_dim, int64_t max_total_ctx,
-                       int32_t split_tokens) {
+AttnLayout attn_layout(int32_t batch, int32_t group, int32_t hkv, int32_t head_dim,
+                       int32_t max_draft_k, int64_t max_total_ctx, int32_t split_tokens) {
   AttnLayout L;
   L.split = sd::attn_split_tokens(batch, hkv, max_total_ctx, split_tokens);
+  L.rows = sd::attn_item_rows(group, max_draft_k);
   L.max_items = sd::attn_max_items(batch, hkv, max_total_ctx, L.split);
   L.off_item_off = 0;
   L.off_unit_off = align_up(static_cast<size_t>(batch + 1) * sizeof(int32_t));
   L.off_lse = L.off_unit_off + align_up(3 * static_cast<size_t>(batch + 1) * sizeof(int32_t));
-  L.off_o = L.off_lse + align_up(static_cast<size_t>(L.max_items) * sd::kAttnRows * sizeof(float));
-  L.total = L.off_o + align_up(static_cast<size_t>(L.max_items) * sd::kAttnRows * head_dim * sizeof(float));
+  L.off_o = L.off_lse + align_up(static_cast<size_t>(L.max_items) * L.rows * sizeof(float));
+  L.total = L.off_o + align_up(static_cast<size_t>(L.max_items) * L.rows * head_dim * sizeof(float));
   return L;
 }
 
@@ -111,11 +114,13 @@ sd_status sd_probe_mfma(int32_t iters, void* sink, void* stream) {
 }
 
 size_t sd_draft_attn_workspace_size(int32_t batch, int32_t num_heads_q, int32_t num_heads_kv,
-                                    int32_t head_dim, int64_t max_total_ctx, int32_t split_tokens) {
-  (void)num_heads_q;
-  if (batch < 1 || num_heads_kv < 1 || head_dim < 1 || max_total_ctx < 0 || split_tokens < 0)
+                                    int32_t head_dim, int32_t max_draft_k, int64_t max_total_ctx,
+                                    int32_t split_tokens) {
+  if (batch < 1 || num_heads_kv < 1 || num_heads_q < num_heads_kv || head_dim < 1 ||
+      max_draft_k < 1 || max_total_ctx < 0 || split_tokens < 0)
     return 0;
-  return attn_layout(batch, num_heads_kv, head_dim, max_total_ctx, split_tokens).total;
+  return attn_layout(batch, num_heads_q / num_heads_kv, num_heads_kv, head_dim, max_draft_k,
+                     max_total_ctx, split_tokens).total;
 }
 
 sd_status sd_draft_attn(const void* q, const void* k_blk, const void* v_blk, const void* k_cache,
@@ -141,13 +146,14 @@ sd_status sd_draft_attn(const void* q, const void* k_blk, const void* v_blk, con
       split_tokens > sd::kAttnMaxSplitPages * 16 || !isfinite(softmax_scale))
     return SD_ERR_SHAPE;
   const int32_t group = num_heads_q / num_heads_kv;
-  if (static_cast<int64_t>(group) * max_draft_k > sd::kAttnRows) return SD_ERR_SHAPE;
+  if (static_cast<int64_t>(group) * max_draft_k > sd::kAttnMaxRows) return SD_ERR_SHAPE;
   if (static_cast<int64_t>(max_pages) * page_size > (int64_t(1) << 30)) return SD_ERR_SHAPE;
   if (static_cast<int64_t>(batch) * max_pages > (int64_t(1) << 31) - 1) return SD_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_cache) ||
       !aligned16(v_cache) || !aligned16(out))
     return SD_ERR_SHAPE;
-  const AttnLayout L = attn_layout(batch, num_heads_kv, head_dim, max_total_ctx, split_tokens);
+  const AttnLayout L = attn_layout(batch, group, num_heads_kv, head_dim, max_draft_k, max_total_ctx,
+                                   split_tokens);
   if (L.max_items > (int64_t(1) << 31) - 1) return SD_ERR_SHAPE;
   if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return SD_ERR_WORKSPACE;
   if (total_q == 0) return SD_OK;
@@ -178,6 +184,7 @@ sd_status sd_draft_attn(const void* q, const void* k_blk, const void* v_blk, con
   a.n_summary = n_summary;
   a.split_tokens = L.split;
   a.max_items = static_cast<int32_t>(L.max_items);
+  a.rows = L.rows;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.item_off = reinterpret_cast<int32_t*>(ws + L.off_item_off);
   a.unit_off = reinterpret_cast<int32_t*>(ws + L.off_unit_off);

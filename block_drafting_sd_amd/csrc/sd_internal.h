@@ -36,15 +36,20 @@ struct AttnArgs {
   int32_t n_summary;      // 0 when there is no summary
   int32_t split_tokens;   // prefix tokens per work item (multiple of 64, <= 32768)
   int32_t max_items;      // work items the partial buffers hold
+  int32_t rows;           // query rows per work item: 64 (two waves) or 128 (four)
   float scale_log2;       // softmax_scale * log2(e)
   int32_t* item_off;      // [batch + 1] first work item of each request
   int32_t* unit_off;      // [3][batch + 1] first unit of each request among the block
                           // (+ summary) units, the full-length and the last prefix splits
-  float* part_lse;        // [max_items][64]       (log2 units)
-  float* part_o;          // [max_items][D/4][64][4]
+  float* part_lse;        // [max_items][rows]       (log2 units)
+  float* part_o;          // [max_items][D/4][rows][4]
 };
 
-constexpr int kAttnRows = 64;        // query rows per (request, kv head) item
+constexpr int kAttnMaxRows = 128;    // query rows of one (request, kv head): G * K_b
+// Query rows per work item for a group size and draft-budget bound.
+inline int32_t attn_item_rows(int32_t group, int32_t max_draft_k) {
+  return static_cast<int64_t>(group) * max_draft_k <= 64 ? 64 : 128;
+}
 constexpr int kAttnTile = 32;        // keys per inner tile (two 16-token pages)
 constexpr int kAttnStages = 4;       // LDS ring stages of the prefix stream
 constexpr int kAttnMaxSplitPages = 2048;   // split_tokens <= 2048 * 16

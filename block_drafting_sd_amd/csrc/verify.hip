@@ -12,8 +12,8 @@
 //      given).  Each thread issues its eight 16-byte loads at once, so the
 //      logits stream through in one pass: HBM-bound.
 //   2. verify_decide    one workgroup per request: merges the row statistics
-//      it needs, evaluates all of the request's ratio tests in parallel and
-//      takes the first rejection.  Only for batches of kDecideBatch requests
+//      it needs, evaluates the request's ratio tests in parallel (256
+//      positions per pass) and takes the first rejection.  Only for batches of kDecideBatch requests
 //      or more: below that every sampling workgroup takes the decision itself
 //      and the launch is saved.
 //   3. verify_sample    grid (requests x 2048-entry chunks): every workgroup
@@ -31,7 +31,9 @@ namespace sd {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxVerify = 255;   // b_b handled per request
+// Positions whose ratio tests one pass of the decision holds in LDS; a
+// request with more verified drafts takes several passes.
+constexpr int kDecideChunk = 256;
 // Batch from which the decision gets its own kernel (timed: -13 us at 128
 // requests, -4 us at 64, +3 us at 16 for the extra launch).
 constexpr int kDecideBatch = 48;
@@ -112,16 +114,20 @@ __device__ float merge_row(const float4* part, int n, int& amax) {
 
 // Shared memory of one request's decision.
 struct DecideSmem {
-  float lse_p[kMaxVerify + 1];
-  int amax_p[kMaxVerify + 1];
-  float lse_q[kMaxVerify];
-  int ok[kMaxVerify + 1];
+  float lse_p[kDecideChunk + 1];   // the pass's rows, and the bonus row after the last one
+  int amax_p[kDecideChunk + 1];
+  float lse_q[kDecideChunk];
+  int ok[kDecideChunk];
+  int reject;                      // first rejected position (0-based), or nv
+  float lse_p_dec, lse_q_dec;      // normalisers of the row the draw uses
   float4 dec;   // (accepted as int bits or -1, lse_p, lse_q, tested as int bits)
 };
 
 // Row statistics, every ratio test and the first rejection of request b, by
 // one workgroup; on return sm.dec holds the decision for every thread.  With
 // `writer` set the workgroup also stores accepted[b] and the accept ratios.
+// The tests run kDecideChunk positions per pass; every tested position gets
+// its ratio, and the first rejection over all passes decides.
 __device__ void decide_request(const VerifyArgs& a, int b, bool writer, DecideSmem& sm) {
   const int tid = threadIdx.x;
   const int t0 = clampi(a.t_off[b], 0, a.R);
@@ -136,57 +142,78 @@ __device__ void decide_request(const VerifyArgs& a, int b, bool writer, DecideSm
     __syncthreads();
     return;
   }
-  const int nv = min(min(t1 - t0 - 1, kb), kMaxVerify);
+  const int nv = min(t1 - t0 - 1, kb);
   const uint32_t rid = a.req_id[b];
+  if (tid == 0) sm.reject = nv;
 
-  // A: log-normalisers of the rows this request may touch
-  for (int i = tid; i <= nv; i += kThreads)
-    sm.lse_p[i] = merge_row(a.row_part + static_cast<size_t>(t0 + i) * a.n_chunks, a.n_chunks,
-                            sm.amax_p[i]);
-  for (int i = tid; i < nv; i += kThreads) {
-    int unused;
-    sm.lse_q[i] = a.draft_lse ? a.draft_lse[q0 + i]
-                              : merge_row(a.row_part + static_cast<size_t>(a.R + q0 + i) * a.n_chunks,
-                                          a.n_chunks, unused);
-  }
-  __syncthreads();
-
-  // B: every ratio test in parallel (eq. (1)): r_j = min(1, p_j(y_j)/q_j(y_j));
-  // at temperature 0 both distributions are one-hot and r_j = [y_j = argmax p_j]
-  for (int i = tid; i < nv; i += kThreads) {
-    const int j = i + 1;
-    const int y = clampi(a.tokens[q0 + i], 0, a.V - 1);
-    float r = 1.f;
-    if (a.greedy) {
-      r = y == sm.amax_p[i] ? 1.f : 0.f;
-    } else {
-      const int iy = a.vinv ? a.vinv[y] : y;   // y in the drafter's vocabulary
-      const float lp = a.target[static_cast<size_t>(t0 + i) * a.V + y] - sm.lse_p[i];
-      const float lq = iy >= 0 && iy < a.v_draft
-                           ? a.draft[static_cast<size_t>(q0 + i) * a.v_draft + iy] - sm.lse_q[i]
-                           : -INFINITY;
-      if (expf(lq) > 0.f) r = fminf(1.f, expf(lp - lq));
+  for (int c0 = 0;; c0 += kDecideChunk) {
+    const int n = min(kDecideChunk, nv - c0);
+    const bool last = c0 + n == nv;   // this pass also holds the bonus row nv
+    // A: log-normalisers of the rows this pass touches
+    for (int i = tid; i < n + (last ? 1 : 0); i += kThreads)
+      sm.lse_p[i] = merge_row(a.row_part + static_cast<size_t>(t0 + c0 + i) * a.n_chunks, a.n_chunks,
+                              sm.amax_p[i]);
+    for (int i = tid; i < n; i += kThreads) {
+      int unused;
+      sm.lse_q[i] = a.draft_lse ? a.draft_lse[q0 + c0 + i]
+                                : merge_row(a.row_part + static_cast<size_t>(a.R + q0 + c0 + i) * a.n_chunks,
+                                            a.n_chunks, unused);
     }
-    const u32x4 w = philox4x32_10(u32x4{0u, static_cast<uint32_t>(j), rid, kStreamAccept},
-                                  a.key0, a.key1);
-    sm.ok[i] = accept_from_bits(w[0]) < r;
-    if (writer && a.accept_ratio) a.accept_ratio[q0 + i] = r;
+    __syncthreads();
+
+    // B: the pass's ratio tests in parallel (eq. (1)): r_j = min(1,
+    // p_j(y_j)/q_j(y_j)); at temperature 0 both distributions are one-hot and
+    // r_j = [y_j = argmax p_j]
+    for (int i = tid; i < n; i += kThreads) {
+      const int j = c0 + i + 1;
+      const int y = clampi(a.tokens[q0 + j - 1], 0, a.V - 1);
+      float r = 1.f;
+      if (a.greedy) {
+        r = y == sm.amax_p[i] ? 1.f : 0.f;
+      } else {
+        const int iy = a.vinv ? a.vinv[y] : y;   // y in the drafter's vocabulary
+        const float lp = a.target[static_cast<size_t>(t0 + j - 1) * a.V + y] - sm.lse_p[i];
+        const float lq = iy >= 0 && iy < a.v_draft
+                             ? a.draft[static_cast<size_t>(q0 + j - 1) * a.v_draft + iy] - sm.lse_q[i]
+                             : -INFINITY;
+        if (expf(lq) > 0.f) r = fminf(1.f, expf(lp - lq));
+      }
+      const u32x4 w = philox4x32_10(u32x4{0u, static_cast<uint32_t>(j), rid, kStreamAccept},
+                                    a.key0, a.key1);
+      sm.ok[i] = accept_from_bits(w[0]) < r;
+      if (writer && a.accept_ratio) a.accept_ratio[q0 + j - 1] = r;
+    }
+    __syncthreads();
+
+    // C: the first rejection ends the round; keep the normalisers of the row
+    // the draw will use (the rejected one, or the bonus row)
+    if (tid == 0) {
+      if (sm.reject == nv)
+        for (int i = 0; i < n; ++i)
+          if (!sm.ok[i]) {
+            sm.reject = c0 + i;
+            sm.lse_p_dec = sm.lse_p[i];
+            sm.lse_q_dec = sm.lse_q[i];
+            break;
+          }
+      if (last && sm.reject == nv) {
+        sm.lse_p_dec = sm.lse_p[n];
+        sm.lse_q_dec = 0.f;
+      }
+    }
+    __syncthreads();   // the next pass reuses the arrays
+    // after a rejection, later passes only serve the ratios of the positions
+    // beyond it
+    if (last || (sm.reject < nv && !(writer && a.accept_ratio))) break;
   }
   if (writer && a.accept_ratio)
     for (int i = nv + tid; i < kb; i += kThreads) a.accept_ratio[q0 + i] = __int_as_float(0x7fc00000);
-  __syncthreads();
 
-  // C: the first rejection ends the round
   if (tid == 0) {
-    int acc = nv;
-    for (int i = 0; i < nv; ++i)
-      if (!sm.ok[i]) {
-        acc = i;
-        break;
-      }
+    const int acc = sm.reject;
     if (writer) a.accepted[b] = acc;
     const bool residual = !a.greedy && acc < nv;
-    sm.dec = make_float4(__int_as_float(acc), sm.lse_p[acc], residual ? sm.lse_q[acc] : 0.f,
+    sm.dec = make_float4(__int_as_float(acc), sm.lse_p_dec, residual ? sm.lse_q_dec : 0.f,
                          __int_as_float(nv));
   }
   __syncthreads();

@@ -84,7 +84,7 @@ class DraftVerifyStep:
         self.ratio = torch.empty(s.total_q, dtype=torch.float32, device=dev)
         u8 = dict(dtype=torch.uint8, device=dev)
         self.ws_attn = torch.empty(max(256, draft_attn_workspace_size(
-            s.batch, s.num_heads_q, s.num_heads_kv, s.head_dim, s.max_total_ctx,
+            s.batch, s.num_heads_q, s.num_heads_kv, s.head_dim, s.max_draft_k, s.max_total_ctx,
             s.split_tokens)), **u8)
         self.ws_lm = torch.empty(max(256, lm_head_workspace_size(s.total_q, vd)), **u8)
         if o.n_summary:

@@ -74,23 +74,6 @@ const char* sd_status_str(sd_status s);
 const char* sd_version(void);
 
 /* ------------------------------------------------------------------------
- * Measured ceilings (not part of the method; for the roofline figures).
- *
- * sd_probe_read  streams `bytes` (>= 16) of device memory at `src` (16-byte
- *   aligned) with plain 16-byte loads, 1,024 workgroups each reading
- *   contiguous 16 KiB blocks, and writes nothing (`sink`: a device word that is only written if the XOR of all
- *   words equals a fixed key).  HBM read rate = bytes / kernel time.
- * sd_probe_mfma  512 workgroups of 4 waves each run `iters` (1..2^24)
- *   rounds of 8 independent bf16 MFMA 32x32x16 on register operands;
- *   sd_probe_mfma_flops(iters) is the flop count of one launch (0 if
- *   iters < 1).  `sink`: a device float written only for one impossible sum.
- * Errors: NULL -> SD_ERR_NULL; bad sizes or alignment -> SD_ERR_SHAPE.
- * ------------------------------------------------------------------------ */
-sd_status sd_probe_read(const void* src, size_t bytes, void* sink, void* stream);
-int64_t sd_probe_mfma_flops(int32_t iters);
-sd_status sd_probe_mfma(int32_t iters, void* sink, void* stream);
-
-/* ------------------------------------------------------------------------
  * sd_draft_attn -- draft-block attention over the target's paged KV cache.
  *
  * Defined by: "ForeSpark: Joint draft and verification budget scheduling for
@@ -143,12 +126,19 @@ sd_status sd_probe_mfma(int32_t iters, void* sink, void* stream);
  *            q_off[batch] = total_q, 0 <= K_b <= max_draft_k (a request
  *            with K_b = 0, e.g. one the scheduler gives no drafts, has no
  *            rows and no work)
- *   max_draft_k  host bound on K_b; (Hq/Hkv) * max_draft_k <= 64
+ *   max_draft_k  host bound on K_b; (Hq/Hkv) * max_draft_k <= 128 (the
+ *                query rows of one (request, KV head) share one read of its
+ *                KV: up to 64 rows per work item with two waves, up to 128
+ *                with four)
  *   num_pages    rows of the caches (page ids are clamped to it)
  *   page_size    16
  *   num_heads_q, num_heads_kv  Hq % Hkv == 0
  *   head_dim     64 or 128
- *   max_total_ctx  host upper bound on sum_b N_b (sizes the launch)
+ *   max_total_ctx  host upper bound on sum_b N_b (sizes the launch and the
+ *                  split-K partials in the workspace).  If the lengths on the
+ *                  device add up to more and their work items do not fit the
+ *                  partials, nothing is computed and every output row of the
+ *                  call is set to NaN (never left stale)
  *   split_tokens   prefix tokens per split-K work item; 0 lets the library
  *                  choose (a power of two in [2048, 32768] from batch,
  *                  num_heads_kv and max_total_ctx); otherwise a multiple of
@@ -164,7 +154,8 @@ sd_status sd_probe_mfma(int32_t iters, void* sink, void* stream);
  * ------------------------------------------------------------------------ */
 size_t sd_draft_attn_workspace_size(int32_t batch, int32_t num_heads_q,
                                     int32_t num_heads_kv, int32_t head_dim,
-                                    int64_t max_total_ctx, int32_t split_tokens);
+                                    int32_t max_draft_k, int64_t max_total_ctx,
+                                    int32_t split_tokens);
 
 sd_status sd_draft_attn(const void* q, const void* k_blk, const void* v_blk,
                         const void* k_cache, const void* v_cache,

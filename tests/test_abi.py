@@ -1,7 +1,8 @@
 """C-ABI checks that need no GPU: the library loads, exports every entry point
-include/sd.h declares, and rejects bad arguments before launching anything
+the headers in include/ declare, and rejects bad arguments before launching anything
 (no pointer is dereferenced on the host, so fake device addresses are safe)."""
 import ctypes as C
+import glob
 import os
 import re
 
@@ -11,14 +12,14 @@ import block_drafting_sd_amd as sd
 from block_drafting_sd_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "sd.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 FAKE = 1 << 20        # 16-byte aligned, never dereferenced by validation
 ODD = FAKE + 8        # not 16-byte aligned
 
 
 def _declared():
-    txt = open(HEADER).read()
+    txt = "\n".join(open(h).read() for h in HEADERS)
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     return sorted(set(re.findall(r"\b(sd_[a-z_0-9]+)\s*\(", txt)))
 
@@ -58,19 +59,24 @@ def test_automatic_attention_split(lib, batch, hkv, total, split):
     """The automatic split (largest power of two in [2048, 32768] tokens with
     at least 512 prefix items and at most the mean prefix) sizes the
     workspace exactly as the explicit split does, and unlike its neighbours."""
-    auto = lib.sd_draft_attn_workspace_size(batch, 4 * hkv, hkv, 128, total, 0)
-    assert auto == lib.sd_draft_attn_workspace_size(batch, 4 * hkv, hkv, 128, total, split)
+    auto = lib.sd_draft_attn_workspace_size(batch, 4 * hkv, hkv, 128, 16, total, 0)
+    assert auto == lib.sd_draft_attn_workspace_size(batch, 4 * hkv, hkv, 128, 16, total, split)
     for other in (split // 2, split * 2):
         if 2048 <= other <= 32768 and total // other != total // split:
-            assert auto != lib.sd_draft_attn_workspace_size(batch, 4 * hkv, hkv, 128, total, other)
+            assert auto != lib.sd_draft_attn_workspace_size(batch, 4 * hkv, hkv, 128, 16, total,
+                                                             other)
 
 
 def test_workspace_sizes(lib):
-    n = lib.sd_draft_attn_workspace_size(16, 32, 8, 128, 16 * 131072, 0)
+    n = lib.sd_draft_attn_workspace_size(16, 32, 8, 128, 16, 16 * 131072, 0)
     # fp32 partials (64 rows x 128 dims) of every prefix item at the automatic
     # split for 16 x 128K prefixes (32768 tokens)
     assert n > 16 * 131072 // 32768 * 8 * 64 * 128 * 4
-    assert lib.sd_draft_attn_workspace_size(0, 32, 8, 128, 1, 0) == 0
+    assert lib.sd_draft_attn_workspace_size(0, 32, 8, 128, 16, 1, 0) == 0
+    assert lib.sd_draft_attn_workspace_size(1, 32, 8, 128, 0, 1, 0) == 0
+    # more than 64 query rows per (request, KV head): items of 128 rows
+    n5 = lib.sd_draft_attn_workspace_size(16, 40, 8, 128, 16, 16 * 131072, 0)
+    assert n5 > 2 * n - 2 * 4096
     assert lib.sd_lm_head_workspace_size(256, 151936) >= 256 * (-(-151936 // 128)) * 16
     assert lib.sd_lm_head_workspace_size(0, 10) == 0
     assert lib.sd_verify_workspace_size(16, 256, 272, 151936) > 0
@@ -96,7 +102,8 @@ def _attn(lib, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), 1), (dict(page_table=None), 1), (dict(out=None), 1),
     (dict(batch=0), 2), (dict(page_size=32), 2), (dict(d=96), 2), (dict(hq=6, hkv=4), 2),
-    (dict(max_draft_k=17), 2),            # group 4 * 17 > 64 query rows
+    (dict(max_draft_k=33), 2),            # group 4 * 33 > 128 query rows
+    (dict(hq=16, hkv=2, max_draft_k=17), 2),   # group 8 * 17 > 128
     (dict(split=100), 2), (dict(scale=float("inf")), 2), (dict(scale=0.0), 2), (dict(q=ODD), 2),
     (dict(mask=2), 2), (dict(window=-1), 2), (dict(n_sum=65, sum_k=FAKE, sum_v=FAKE), 2),
     (dict(n_sum=16), 1), (dict(n_sum=16, sum_k=FAKE), 1), (dict(n_sum=16, sum_k=ODD, sum_v=FAKE), 2),
@@ -294,6 +301,30 @@ def test_python_binding_checks_array_lengths():
         sd.sd_lm_head_probs(h, wv, q_off, torch.zeros(1, dtype=i32), 0)
     with pytest.raises(ValueError, match="lse"):
         sd.sd_lm_head_probs(h, wv, q_off, torch.zeros(2, dtype=i32), 0, lse=torch.zeros(3))
+
+
+def test_python_binding_checks_verify_draft_rows():
+    # without a vocabulary map the library reads draft rows with the target's
+    # row length, so shorter or longer rows must be refused before the call
+    import torch
+    i32 = torch.int32
+    tl = torch.zeros(3, 100)
+    t_off = torch.tensor([0, 3], dtype=i32)
+    q_off = torch.tensor([0, 2], dtype=i32)
+    tok = torch.zeros(2, dtype=i32)
+    rid = torch.zeros(1, dtype=i32)
+    with pytest.raises(ValueError, match="V = 100"):
+        sd.sd_verify(tl, t_off, torch.zeros(2, 320), None, tok, q_off, rid, 0)
+    with pytest.raises(ValueError, match="V = 100"):
+        sd.sd_verify(tl, t_off, torch.zeros(2, 50), torch.zeros(2), tok, q_off, rid, 0)
+    with pytest.raises(ValueError, match="draft_lse"):
+        sd.sd_verify(tl, t_off, torch.zeros(2, 50), None, tok, q_off, rid, 0,
+                     draft_vocab_inv=torch.full((100,), -1, dtype=i32))
+    with pytest.raises(ValueError, match="draft_lse"):
+        sd.sd_verify(tl, t_off, torch.zeros(2, 50), torch.zeros(1), tok, q_off, rid, 0,
+                     draft_vocab_inv=torch.full((100,), -1, dtype=i32))
+    with pytest.raises(ValueError, match="total_q"):
+        sd.sd_verify(tl, t_off, torch.zeros(200), None, tok, q_off, rid, 0)
 
 
 def test_bench_refuses_several_gpus():

@@ -7,7 +7,9 @@
   few thousand rows here, compared with the oracle's fp64 definition within
   max-abs 1e-4 on Z (entries of size ~0.1..1) and 1e-4 relative on c;
 * the fixed-cost context of the 128K workload (window 256 + 16 summary
-  entries) at full size, on sampled requests;
+  entries) at full size, on sampled requests: the summary state within
+  max-abs 1e-4 and relative L2 1e-4 of the oracle (entries ~5e-3, 131,072
+  fp32 terms each), the attention as in the parity suite;
 * temperature-0 drafting and verification and the pruned drafter vocabulary:
   probabilities within 1e-5, tokens and accepted lengths exact except
   audited near-ties (as in the main parity suite), including the 128K
@@ -68,6 +70,25 @@ def test_causal_block(head_dim, split):
     inp = StepInputs(_cfg(head_dim=head_dim))
     got = _gpu_attn(inp, split_tokens=split, block_mask=sd.SD_MASK_CAUSAL)
     _check(got, _oracle_attn(inp, block_mask="causal"), tag=f"causal D={head_dim} split={split}")
+
+
+@pytest.mark.parametrize("mode", ["causal", "window", "summary"])
+def test_variants_large_group(mode):
+    """The variants with 128-row work items (GQA group 8, K = 16)."""
+    inp = StepInputs(_cfg(num_heads_q=64, num_heads_kv=8, draft_k=("list", (16, 1, 16, 5, 9)),
+                          seed=818))
+    if mode == "causal":
+        got = _gpu_attn(inp, split_tokens=64, block_mask=sd.SD_MASK_CAUSAL)
+        ref = _oracle_attn(inp, block_mask="causal")
+    elif mode == "window":
+        got = _gpu_attn(inp, split_tokens=64, window=50)
+        ref = _oracle_attn(inp, window=50)
+    else:
+        u, z = inp.summary_queries(16), inp.summary_values(16)
+        got = _gpu_attn(inp, window=256, summary_keys=sdev.bf16(u, DEV),
+                        summary_values=sdev.f32(z, DEV))
+        ref = _oracle_attn(inp, window=256, summary_keys=u, summary_values=z)
+    _check(got, ref, tag=f"large group {mode}")
 
 
 def test_causal_block_mha_two_block_tiles():
@@ -184,9 +205,14 @@ def test_fixed_cost_full_size_128k():
             zr[r, g], cr[r, g] = osum.summary_of_rows(u[g], kl[:, g], vl[:, g], inp.softmax_scale)
     zg, cg = z.cpu().numpy(), c.cpu().numpy()
     dz = max(np.abs(zg[r] - zr[r]).max() for r in reqs)
+    rel = max(np.linalg.norm(zg[r] - zr[r]) / np.linalg.norm(zr[r]) for r in reqs)
     dc = max((np.abs(cg[r] - cr[r]) / np.maximum(1, np.abs(cr[r]))).max() for r in reqs)
-    log(f"128K summary init: Z max-abs {dz:.3g}, c max-rel {dc:.3g}")
-    assert dz <= 1e-3 and dc <= C_RTOL   # 131072 fp32 terms per entry
+    zmag = max(np.abs(zr[r]).max() for r in reqs)
+    log(f"128K summary init: Z max-abs {dz:.3g} (entries up to {zmag:.3g}), rel-L2 {rel:.3g}, "
+        f"c max-rel {dc:.3g}")
+    # 131,072 fp32 terms per entry, merged tile by tile: the relative error of
+    # an fp32 running sum of n terms stays near sqrt(n) * 2^-24 ~ 2e-5
+    assert dz <= Z_ATOL and rel <= 1e-4 and dc <= C_RTOL
     rows = np.concatenate([np.arange(b.q_off[r], b.q_off[r + 1]) for r in reqs])
     ref = _oracle_attn(inp, requests=reqs, window=256, summary_keys=u, summary_values=zg)
     _check(bits(out), ref, rows=rows, tag="128K fixed-cost attention")
