@@ -16,7 +16,7 @@ from ._lib import LIB_PATH, SdError, check, load  # noqa: F401
 
 SD_MASK_NONE, SD_MASK_CAUSAL = 0, 1
 
-__all__ = ["sd_draft_attn", "sd_summary_update", "sd_lm_head_probs", "sd_markov_sample",
+__all__ = ["sd_draft_attn", "sd_draft_attn_noalloc", "sd_summary_update", "sd_lm_head_probs", "sd_markov_sample",
            "sd_verify",
            "sd_schedule_draft", "sd_schedule_verify", "sd_version",
            "SD_MASK_NONE", "SD_MASK_CAUSAL",
@@ -159,6 +159,55 @@ def sd_draft_attn(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_len, q_off,
                            _ptr(summary_values), n_summary,
                            _ptr(out), _ptr(workspace), workspace.numel(), _stream_handle(stream))
     check("sd_draft_attn", st)
+    return out
+
+
+def sd_draft_attn_noalloc(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_len, q_off, *,
+                          max_draft_k: int, max_total_ctx: int,
+                          softmax_scale: Optional[float] = None, split_tokens: int = 0,
+                          block_mask: int = SD_MASK_NONE, window: int = 0, summary_keys=None,
+                          summary_values=None, out=None, stream=None):
+    """Draft-block attention for callers that cannot allocate: the library's
+    own per-GPU scratch array instead of a workspace; see
+    ``sd_draft_attn_noalloc`` in include/sd.h.  ``out`` must be given (this
+    entry point exists for code that allocates nothing)."""
+    lib = load()
+    dev = q.device
+    for t, nm in ((q, "q"), (k_blk, "k_blk"), (v_blk, "v_blk"), (k_cache, "k_cache"),
+                  (v_cache, "v_cache")):
+        _req(t, nm, _BF16, dev)
+    for t, nm in ((page_table, "page_table"), (ctx_len, "ctx_len"), (q_off, "q_off")):
+        _req(t, nm, _I32, dev)
+    if out is None:
+        raise ValueError("out must be given (the no-allocation entry point allocates nothing)")
+    _req(out, "out", _BF16, dev)
+    total_q, hq, D = q.shape
+    hkv = k_blk.shape[1]
+    num_pages, _, _, page_size, _ = k_cache.shape
+    batch, max_pages = page_table.shape
+    _need(ctx_len, batch, "ctx_len")
+    _need(q_off, batch + 1, "q_off")
+    _need(out, q.numel(), "out")
+    if tuple(k_blk.shape) != (total_q, hkv, D) or tuple(v_blk.shape) != (total_q, hkv, D):
+        raise ValueError("k_blk and v_blk must be [total_q, Hkv, D]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    n_summary = 0
+    if summary_keys is not None or summary_values is not None:
+        _req(summary_keys, "summary_keys", _BF16, dev)
+        _req(summary_values, "summary_values", _F32, dev)
+        n_summary = summary_keys.shape[1]
+        if tuple(summary_keys.shape) != (hkv, n_summary, D) or \
+                tuple(summary_values.shape) != (batch, hkv, n_summary, D):
+            raise ValueError("summary_keys must be [Hkv, S, D] and summary_values [batch, Hkv, S, D]")
+    st = lib.sd_draft_attn_noalloc(_ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(k_cache),
+                                   _ptr(v_cache), _ptr(page_table), _ptr(ctx_len), _ptr(q_off),
+                                   batch, total_q, max_draft_k, num_pages, max_pages, page_size,
+                                   hq, hkv, D, int(max_total_ctx), int(split_tokens),
+                                   float(softmax_scale), int(block_mask), int(window),
+                                   _ptr(summary_keys), _ptr(summary_values), n_summary,
+                                   _ptr(out), _stream_handle(stream))
+    check("sd_draft_attn_noalloc", st)
     return out
 
 

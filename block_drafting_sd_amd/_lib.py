@@ -14,7 +14,8 @@ LIB_PATH = os.path.join(PKG, "libsd_amd.so")
 
 SD_OK = 0
 STATUS_NAMES = {0: "SD_OK", 1: "SD_ERR_NULL", 2: "SD_ERR_SHAPE",
-                3: "SD_ERR_WORKSPACE", 4: "SD_ERR_LAUNCH", 5: "SD_ERR_DEVICE"}
+                3: "SD_ERR_WORKSPACE", 4: "SD_ERR_LAUNCH", 5: "SD_ERR_DEVICE",
+                6: "SD_ERR_SCRATCH"}
 
 _vp, _i32, _i64, _sz, _f32, _u64 = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t, C.c_float, C.c_uint64
 
@@ -29,6 +30,11 @@ SIGNATURES = {
                              _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                              _i64, _i32, _f32, _i32, _i32, _vp, _vp, _i32,
                              _vp, _vp, _sz, _vp]),
+    "sd_draft_attn_noalloc_max_scratch": (_sz, []),
+    "sd_draft_attn_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                     _i64, _i32, _f32, _i32, _i32, _vp, _vp, _i32,
+                                     _vp, _vp]),
     "sd_summary_update": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                  _i32, _i32, _i32, _f32, _vp, _vp, _vp]),
     "sd_schedule_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),

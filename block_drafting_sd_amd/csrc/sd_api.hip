@@ -7,7 +7,15 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "sd_internal.h"
+
+// Scratch of sd_draft_attn_noalloc (its work list and split-K partials): a
+// file-scope device array, one copy per GPU, held until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory.
+constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -77,6 +85,107 @@ VerifyLayout verify_layout(int32_t batch, int32_t total_q, int32_t R, int32_t V)
   return L;
 }
 
+// Validation, work-list layout and launches of sd_draft_attn.  The scratch
+// memory comes from `get_ws`: given the bytes the call needs it returns the
+// status and, on SD_OK, a 16-byte aligned device buffer of at least that
+// size (the caller's workspace, or the no-allocation variant's array).
+template <typename GetWs>
+sd_status draft_attn_impl(const void* q, const void* k_blk, const void* v_blk, const void* k_cache,
+                          const void* v_cache, const int32_t* page_table, const int32_t* ctx_len,
+                          const int32_t* q_off, int32_t batch, int32_t total_q, int32_t max_draft_k,
+                          int32_t num_pages, int32_t max_pages, int32_t page_size,
+                          int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                          int64_t max_total_ctx, int32_t split_tokens, float softmax_scale,
+                          int32_t block_mask, int32_t window, const void* summary_keys,
+                          const float* summary_values, int32_t n_summary, void* out,
+                          GetWs get_ws, void* stream) {
+  if (!q || !k_blk || !v_blk || !k_cache || !v_cache || !page_table || !ctx_len || !q_off || !out)
+    return SD_ERR_NULL;
+  if (n_summary > 0 && (!summary_keys || !summary_values)) return SD_ERR_NULL;
+  if ((block_mask != SD_MASK_NONE && block_mask != SD_MASK_CAUSAL) || window < 0 || n_summary < 0 ||
+      n_summary > sd::kAttnMaxSummary || !(softmax_scale > 0.f))
+    return SD_ERR_SHAPE;
+  if (n_summary > 0 && !aligned16(summary_keys)) return SD_ERR_SHAPE;
+  if (batch < 1 || total_q < 0 || max_draft_k < 1 || num_pages < 1 || max_pages < 1 ||
+      page_size != 16 || num_heads_kv < 1 || num_heads_q < num_heads_kv ||
+      num_heads_q % num_heads_kv != 0 || (head_dim != 64 && head_dim != 128) ||
+      max_total_ctx < 0 || split_tokens < 0 || split_tokens % 64 != 0 ||
+      split_tokens > sd::kAttnMaxSplitPages * 16 || !isfinite(softmax_scale))
+    return SD_ERR_SHAPE;
+  const int32_t group = num_heads_q / num_heads_kv;
+  if (static_cast<int64_t>(group) * max_draft_k > sd::kAttnMaxRows) return SD_ERR_SHAPE;
+  if (static_cast<int64_t>(max_pages) * page_size > (int64_t(1) << 30)) return SD_ERR_SHAPE;
+  if (static_cast<int64_t>(batch) * max_pages > (int64_t(1) << 31) - 1) return SD_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(out))
+    return SD_ERR_SHAPE;
+  const AttnLayout L = attn_layout(batch, group, num_heads_kv, head_dim, max_draft_k, max_total_ctx,
+                                   split_tokens);
+  if (L.max_items > (int64_t(1) << 31) - 1) return SD_ERR_SHAPE;
+  char* ws = nullptr;
+  const sd_status wst = get_ws(L.total, &ws);
+  if (wst != SD_OK) return wst;
+  if (total_q == 0) return SD_OK;
+
+  sd::AttnArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_blk = static_cast<const uint16_t*>(k_blk);
+  a.v_blk = static_cast<const uint16_t*>(v_blk);
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.page_table = page_table;
+  a.ctx_len = ctx_len;
+  a.q_off = q_off;
+  a.out = static_cast<uint16_t*>(out);
+  a.batch = batch;
+  a.total_q = total_q;
+  a.max_draft_k = max_draft_k;
+  a.num_pages = num_pages;
+  a.max_pages = max_pages;
+  a.hq = num_heads_q;
+  a.hkv = num_heads_kv;
+  a.group = group;
+  a.block_mask = block_mask;
+  a.window = window;
+  a.sum_k = n_summary > 0 ? static_cast<const uint16_t*>(summary_keys) : nullptr;
+  a.sum_v = n_summary > 0 ? summary_values : nullptr;
+  a.n_summary = n_summary;
+  a.split_tokens = L.split;
+  a.max_items = static_cast<int32_t>(L.max_items);
+  a.rows = L.rows;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.item_off = reinterpret_cast<int32_t*>(ws + L.off_item_off);
+  a.unit_off = reinterpret_cast<int32_t*>(ws + L.off_unit_off);
+  a.part_lse = reinterpret_cast<float*>(ws + L.off_lse);
+  a.part_o = reinterpret_cast<float*>(ws + L.off_o);
+  return from_hip(sd::launch_draft_attn(a, head_dim, static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------ no-allocation variant
+// The device address of `scratch` (below the includes) is looked up once per
+// device, with that device current, and only that address is ever handed to
+// kernels.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device).
+sd_status scratch_of_current_device(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return SD_ERR_DEVICE;
+  if (dev >= kMaxDevices) return SD_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return e == hipSuccess ? SD_ERR_DEVICE : from_hip(e);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return SD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -89,6 +198,7 @@ const char* sd_status_str(sd_status s) {
     case SD_ERR_WORKSPACE: return "workspace is NULL or smaller than required";
     case SD_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
     case SD_ERR_DEVICE: return "the current device cannot run gfx950 code";
+    case SD_ERR_SCRATCH: return "the call needs more scratch than the no-allocation variant's fixed device array holds";
     default: return "unknown status";
   }
 }
@@ -132,65 +242,39 @@ sd_status sd_draft_attn(const void* q, const void* k_blk, const void* v_blk, con
                         int32_t block_mask, int32_t window, const void* summary_keys,
                         const float* summary_values, int32_t n_summary,
                         void* out, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k_blk || !v_blk || !k_cache || !v_cache || !page_table || !ctx_len || !q_off || !out)
-    return SD_ERR_NULL;
-  if (n_summary > 0 && (!summary_keys || !summary_values)) return SD_ERR_NULL;
-  if ((block_mask != SD_MASK_NONE && block_mask != SD_MASK_CAUSAL) || window < 0 || n_summary < 0 ||
-      n_summary > sd::kAttnMaxSummary || !(softmax_scale > 0.f))
-    return SD_ERR_SHAPE;
-  if (n_summary > 0 && !aligned16(summary_keys)) return SD_ERR_SHAPE;
-  if (batch < 1 || total_q < 0 || max_draft_k < 1 || num_pages < 1 || max_pages < 1 ||
-      page_size != 16 || num_heads_kv < 1 || num_heads_q < num_heads_kv ||
-      num_heads_q % num_heads_kv != 0 || (head_dim != 64 && head_dim != 128) ||
-      max_total_ctx < 0 || split_tokens < 0 || split_tokens % 64 != 0 ||
-      split_tokens > sd::kAttnMaxSplitPages * 16 || !isfinite(softmax_scale))
-    return SD_ERR_SHAPE;
-  const int32_t group = num_heads_q / num_heads_kv;
-  if (static_cast<int64_t>(group) * max_draft_k > sd::kAttnMaxRows) return SD_ERR_SHAPE;
-  if (static_cast<int64_t>(max_pages) * page_size > (int64_t(1) << 30)) return SD_ERR_SHAPE;
-  if (static_cast<int64_t>(batch) * max_pages > (int64_t(1) << 31) - 1) return SD_ERR_SHAPE;
-  if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_cache) ||
-      !aligned16(v_cache) || !aligned16(out))
-    return SD_ERR_SHAPE;
-  const AttnLayout L = attn_layout(batch, group, num_heads_kv, head_dim, max_draft_k, max_total_ctx,
-                                   split_tokens);
-  if (L.max_items > (int64_t(1) << 31) - 1) return SD_ERR_SHAPE;
-  if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return SD_ERR_WORKSPACE;
-  if (total_q == 0) return SD_OK;
+  auto ws = [&](size_t need, char** p) -> sd_status {
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SD_ERR_WORKSPACE;
+    *p = static_cast<char*>(workspace);
+    return SD_OK;
+  };
+  return draft_attn_impl(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_len, q_off, batch,
+                         total_q, max_draft_k, num_pages, max_pages, page_size, num_heads_q,
+                         num_heads_kv, head_dim, max_total_ctx, split_tokens, softmax_scale,
+                         block_mask, window, summary_keys, summary_values, n_summary, out, ws,
+                         stream);
+}
 
-  char* ws = static_cast<char*>(workspace);
-  sd::AttnArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k_blk = static_cast<const uint16_t*>(k_blk);
-  a.v_blk = static_cast<const uint16_t*>(v_blk);
-  a.k_cache = static_cast<const uint16_t*>(k_cache);
-  a.v_cache = static_cast<const uint16_t*>(v_cache);
-  a.page_table = page_table;
-  a.ctx_len = ctx_len;
-  a.q_off = q_off;
-  a.out = static_cast<uint16_t*>(out);
-  a.batch = batch;
-  a.total_q = total_q;
-  a.max_draft_k = max_draft_k;
-  a.num_pages = num_pages;
-  a.max_pages = max_pages;
-  a.hq = num_heads_q;
-  a.hkv = num_heads_kv;
-  a.group = group;
-  a.block_mask = block_mask;
-  a.window = window;
-  a.sum_k = n_summary > 0 ? static_cast<const uint16_t*>(summary_keys) : nullptr;
-  a.sum_v = n_summary > 0 ? summary_values : nullptr;
-  a.n_summary = n_summary;
-  a.split_tokens = L.split;
-  a.max_items = static_cast<int32_t>(L.max_items);
-  a.rows = L.rows;
-  a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  a.item_off = reinterpret_cast<int32_t*>(ws + L.off_item_off);
-  a.unit_off = reinterpret_cast<int32_t*>(ws + L.off_unit_off);
-  a.part_lse = reinterpret_cast<float*>(ws + L.off_lse);
-  a.part_o = reinterpret_cast<float*>(ws + L.off_o);
-  return from_hip(sd::launch_draft_attn(a, head_dim, static_cast<hipStream_t>(stream)));
+size_t sd_draft_attn_noalloc_max_scratch(void) { return kNoAllocScratchBytes; }
+
+sd_status sd_draft_attn_noalloc(const void* q, const void* k_blk, const void* v_blk,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* page_table, const int32_t* ctx_len,
+                                const int32_t* q_off, int32_t batch, int32_t total_q,
+                                int32_t max_draft_k, int32_t num_pages, int32_t max_pages,
+                                int32_t page_size, int32_t num_heads_q, int32_t num_heads_kv,
+                                int32_t head_dim, int64_t max_total_ctx, int32_t split_tokens,
+                                float softmax_scale, int32_t block_mask, int32_t window,
+                                const void* summary_keys, const float* summary_values,
+                                int32_t n_summary, void* out, void* stream) {
+  auto ws = [](size_t need, char** p) -> sd_status {
+    if (need > kNoAllocScratchBytes) return SD_ERR_SCRATCH;
+    return scratch_of_current_device(p);
+  };
+  return draft_attn_impl(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_len, q_off, batch,
+                         total_q, max_draft_k, num_pages, max_pages, page_size, num_heads_q,
+                         num_heads_kv, head_dim, max_total_ctx, split_tokens, softmax_scale,
+                         block_mask, window, summary_keys, summary_values, n_summary, out, ws,
+                         stream);
 }
 
 sd_status sd_summary_update(const void* summary_queries, const void* k_cache, const void* v_cache,

@@ -28,8 +28,9 @@
  *     kernels clamp page ids, lengths and offsets to the host-given sizes.
  *   - bf16 is IEEE binary32 truncated to its upper 16 bits (bfloat16);
  *     fp32 is IEEE binary32.  All arrays are dense, row-major, unpadded.
- *   - Re-entrant: the library holds no global state.  Calls that share a
- *     workspace must not overlap in time.
+ *   - Re-entrant: the library holds no global state (apart from the device
+ *     array of sd_draft_attn_noalloc).  Calls that share a workspace must not
+ *     overlap in time.
  *
  * Randomness: every random decision uses Philox-4x32-10 (Salmon et al.,
  * "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11) keyed by
@@ -58,7 +59,9 @@ enum {
   SD_ERR_SHAPE = 2,     /* a size argument is out of the supported range     */
   SD_ERR_WORKSPACE = 3, /* workspace NULL or smaller than required           */
   SD_ERR_LAUNCH = 4,    /* the HIP runtime rejected a launch                 */
-  SD_ERR_DEVICE = 5     /* no gfx950 device is current                       */
+  SD_ERR_DEVICE = 5,    /* no gfx950 device is current                       */
+  SD_ERR_SCRATCH = 6    /* sd_draft_attn_noalloc: the call needs more scratch
+                           than its fixed device array holds                  */
 };
 
 /* Attention among the draft block's own rows (sd_draft_attn block_mask). */
@@ -170,6 +173,43 @@ sd_status sd_draft_attn(const void* q, const void* k_blk, const void* v_blk,
                         const void* summary_keys, const float* summary_values,
                         int32_t n_summary, void* out,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * sd_draft_attn_noalloc -- sd_draft_attn for callers that cannot allocate.
+ *
+ * For code that must not call hipMalloc or any allocating routine: work
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, operation, results (bit for bit) and errors as
+ * sd_draft_attn, without workspace arguments: the work list and split-K
+ * partials live in a device array inside the library,
+ * sd_draft_attn_noalloc_max_scratch() bytes (128 MiB) per GPU, created when
+ * the library's code is loaded on that GPU and held until the process ends.
+ * A call whose sd_draft_attn_workspace_size(...) exceeds that size returns
+ * SD_ERR_SCRATCH before anything is launched (e.g. 16 requests of 128K
+ * tokens need about 24 MiB, 64 requests of 4K about 48 MiB, 128 requests of
+ * 1K-128K, 3.2M tokens in all, about 113 MiB).
+ *
+ * The array is shared by every call on the same GPU and keeps the last
+ * call's contents (nothing in it needs to start at zero).  Calls that
+ * overlap in time on one GPU (e.g. on two streams, or from two threads
+ * without ordering) race on it and give undefined results; calls on
+ * different GPUs do not interact.  The first call on a GPU looks up the
+ * array's device address (hipGetSymbolAddress); it allocates nothing.
+ * ------------------------------------------------------------------------ */
+size_t sd_draft_attn_noalloc_max_scratch(void);
+
+sd_status sd_draft_attn_noalloc(const void* q, const void* k_blk, const void* v_blk,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* page_table, const int32_t* ctx_len,
+                                const int32_t* q_off, int32_t batch, int32_t total_q,
+                                int32_t max_draft_k, int32_t num_pages,
+                                int32_t max_pages, int32_t page_size,
+                                int32_t num_heads_q, int32_t num_heads_kv,
+                                int32_t head_dim, int64_t max_total_ctx,
+                                int32_t split_tokens, float softmax_scale,
+                                int32_t block_mask, int32_t window,
+                                const void* summary_keys, const float* summary_values,
+                                int32_t n_summary, void* out, void* stream);
 
 /* ------------------------------------------------------------------------
  * sd_summary_update -- maintain the global context summary.

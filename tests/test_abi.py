@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    for s in range(6):
+    for s in range(7):
         assert lib.sd_status_str(s)
     assert lib.sd_status_str(99) == b"unknown status"
     assert sd.sd_version() == "0.1.0"
@@ -113,6 +113,28 @@ def _attn(lib, **kw):
 ])
 def test_draft_attn_validation(lib, kw, status):
     assert _attn(lib, **kw) == status
+
+
+def test_noalloc_rejects_before_any_device_call(lib):
+    """The no-allocation attention validates like sd_draft_attn and refuses a
+    call whose scratch exceeds its fixed array, all before it touches a
+    device (so these run without a GPU)."""
+    cap = lib.sd_draft_attn_noalloc_max_scratch()
+    assert cap == 128 << 20
+    def call(**kw):
+        a = dict(q=FAKE, batch=2, total_q=8, max_draft_k=4, hq=8, hkv=2, max_total_ctx=100)
+        a.update(kw)
+        return lib.sd_draft_attn_noalloc(a["q"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                         a["batch"], a["total_q"], a["max_draft_k"], 10, 5, 16,
+                                         a["hq"], a["hkv"], 128, a["max_total_ctx"], 0, 0.088,
+                                         0, 0, None, None, 0, FAKE, None)
+    assert call(q=None) == 1
+    assert call(max_draft_k=33) == 2
+    # 16 x 2M tokens of prefix need far more partials than the array holds
+    big = 16 * (1 << 21)
+    assert lib.sd_draft_attn_workspace_size(16, 32, 8, 128, 16, big, 0) > cap
+    assert call(batch=16, hq=32, hkv=8, max_draft_k=16, max_total_ctx=big) == 6
+    assert lib.sd_status_str(6).startswith(b"the call needs more scratch")
 
 
 def _sum(lib, **kw):
