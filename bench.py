@@ -410,6 +410,16 @@ def main():
     elapsed = time.perf_counter() - t0
     log(f"[bench] timed {args.steps} steps in {elapsed:.3f}s")
 
+    # Emitted tokens (sum_b (a_b + 1), the committed tokens of a round): every
+    # timed step used its own seed, so the steps are replayed untimed, in the
+    # same order, and their accepted lengths read back one by one.
+    emitted_steps = []
+    for i in range(args.steps):
+        for name in stages:
+            run_stage[name](i)
+        emitted_steps.append(int(step.accepted.sum().item()) + cfg.batch)
+    emitted_total = int(sum(emitted_steps))
+
     peaks = None if args.no_peaks else measured_peaks(dev)
     lib_gemm = (library_gemm(t["hidden"], t["w_vocab"])
                 if not args.no_peaks and not opts.draft_vocab else None)
@@ -423,7 +433,6 @@ def main():
     tokens_per_step = int(b.draft_k.sum())
     ms_per_step = elapsed * 1e3 / args.steps
     value = tokens_per_step * args.steps / elapsed
-    emitted = int(step.accepted.sum().item()) + cfg.batch
 
     c = cfg
     n_read = b.ctx_len.astype(np.int64)
@@ -490,7 +499,10 @@ def main():
                     "w_hbm_gbs": round(v_draft * c.hidden * 2 / (float(lm_ms.mean()) * 1e-3) / 1e9, 1),
                     "library_gemm": lib_gemm},
         "measured_peaks": peaks,
-        "emitted_tokens_per_step_last": emitted,
+        # secondary metric: committed tokens (accepted drafts + the correction
+        # or bonus token of every request) per second of the same timed steps
+        "emitted_tokens_per_s": round(emitted_total / elapsed, 1),
+        "emitted_tokens_per_step_mean": round(emitted_total / args.steps, 3),
         # one drafter attention layer per step is timed; projections for the
         # 3 attention modules of "H-Spec" and the 5 draft layers of "LongSpark"
         "projection_tokens_per_s": {

@@ -10,7 +10,9 @@ import ctypes as C
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libsd_amd.so")
+# SD_LIB_PATH selects another build of the same library (the host-sanitized
+# one of the checking build); there is no fallback of any kind.
+LIB_PATH = os.environ.get("SD_LIB_PATH") or os.path.join(PKG, "libsd_amd.so")
 
 SD_OK = 0
 STATUS_NAMES = {0: "SD_OK", 1: "SD_ERR_NULL", 2: "SD_ERR_SHAPE",

@@ -51,15 +51,44 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every source and link ``libsd_amd.so``; returns its path."""
+# Host-side sanitizers for a checking build of the C ABI's validation layer:
+# AddressSanitizer and UndefinedBehaviorSanitizer on the host code only
+# (-Xarch_host before each -fsanitize=; the device code is built as usual).
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host",
+                  "-fno-sanitize-recover=undefined"]
+SANITIZED_LIB_PATH = os.path.join(PKG, "libsd_amd_sanitized.so")
+
+
+def clangxx() -> str:
+    c = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "lib", "llvm", "bin",
+                     "clang++")
+    for cand in (c, "/opt/rocm/lib/llvm/bin/clang++"):
+        if os.path.exists(cand):
+            return cand
+    raise RuntimeError("ROCm's clang++ not found")
+
+
+def asan_runtime() -> str:
+    """The shared AddressSanitizer runtime a host process preloads to run
+    the sanitized library."""
+    return subprocess.run([clangxx(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                          capture_output=True, text=True, check=True).stdout.strip()
+
+
+def build(verbose: bool = False, jobs: int = 8, sanitize: bool = False) -> str:
+    """Compile every source and link ``libsd_amd.so`` (or, with
+    ``sanitize``, the host-sanitized ``libsd_amd_sanitized.so``); returns its
+    path."""
     cc = hipcc()
     srcs = sources()
+    out_path = SANITIZED_LIB_PATH if sanitize else LIB_PATH
+    extra = SANITIZE_FLAGS if sanitize else []
     with tempfile.TemporaryDirectory(prefix="sd_amd_build_") as tmp:
         objs, procs = [], []
         for s in srcs:
             o = os.path.join(tmp, os.path.basename(s) + ".o")
-            cmd = [cc, *HIP_FLAGS, *FILE_FLAGS.get(os.path.basename(s), []),
+            cmd = [cc, *HIP_FLAGS, *FILE_FLAGS.get(os.path.basename(s), []), *extra,
                    f"-I{INCLUDE}", f"-I{CSRC}", "-c", s, "-o", o]
             if verbose:
                 print(" ".join(cmd), flush=True)
@@ -81,17 +110,23 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
                 raise RuntimeError(f"hipcc failed on {s}:\n" + "\n".join(keep))
             if keep and verbose:
                 print("\n".join(keep))
-        tmp_lib = os.path.join(tmp, LIB_NAME)
-        cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib]
+        tmp_lib = os.path.join(tmp, os.path.basename(out_path))
+        if sanitize:
+            # host link with the sanitizer runtimes as shared libraries
+            rocm_lib = os.path.join(os.path.dirname(os.path.realpath(cc)), "..", "lib")
+            cmd = [clangxx(), "-shared", "-fPIC", "-fsanitize=address,undefined", "-shared-libsan",
+                   *objs, f"-L{rocm_lib}", "-lamdhip64", "-o", tmp_lib]
+        else:
+            cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
         if r.returncode != 0:
             raise RuntimeError("link failed:\n" + r.stdout)
-        shutil.copyfile(tmp_lib, LIB_PATH + ".tmp")
-        os.replace(LIB_PATH + ".tmp", LIB_PATH)
-    return LIB_PATH
+        shutil.copyfile(tmp_lib, out_path + ".tmp")
+        os.replace(out_path + ".tmp", out_path)
+    return out_path
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))
