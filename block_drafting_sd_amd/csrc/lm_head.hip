@@ -3,30 +3,35 @@
 // and App. A.1, Fig. 6: the frozen target vocabulary head produces every
 // slot's base logits in parallel and each slot is sampled independently).
 //
-// lm_gemm<WV, BK>: one workgroup (2 x WV waves) computes a 64 WV-vocab x
-// 256-row tile (128 x 256 with 4 waves for one row tile; 256 x 256 with 8
-// waves when there are several) of logits^T = W * hidden^T with MFMA
-// 32x32x16 bf16 (fp32 accumulation); each wave owns a 64 x 128 sub-tile (8
-// accumulator tiles).  Both operands are H-contiguous.  They stream through
-// a ring of LDS stages of BK hidden dims (W rows, then hidden rows, per
-// stage), filled by direct-to-LDS loads: each 1 KiB wave load covers whole
-// BK-dim row segments (16 rows x 64 bytes at BK = 32, 8 rows x 128 bytes at
-// BK = 64), so global reads stay coalesced, and rows are stored with a
-// 16-byte-chunk XOR swizzle so the MFMA operand reads (32 rows, one chunk)
-// are conflict-free.  With 4 waves the ring (3 x 24 KiB) lets two workgroups
-// share a CU: each SIMD then runs two waves whose barriers are independent,
-// so one workgroup's MFMAs cover the other's waits for loads and its
-// epilogue; with 8 waves one workgroup (2 x 64 KiB stages of 64 dims) fills
-// the CU with the same two waves per SIMD, re-reads the hidden rows half as
-// often, loads whole 128-byte lines and passes half as many stage barriers.
-// At up to 256 draft rows the whole W (1.2 GB) is read from HBM exactly once.
+// lm_gemm<Shape>: one workgroup computes a BV-vocab x 256-row tile of
+// logits^T = W * hidden^T with MFMA 32x32x16 bf16 (fp32 accumulation); each
+// wave owns a (32 TV) x (32 TM) sub-tile.  Both operands are H-contiguous.
+// They stream through a ring of LDS stages of BK hidden dims (W rows, then
+// hidden rows, per stage), filled by direct-to-LDS loads: each 1 KiB wave
+// load covers whole BK-dim row segments (16 rows x 64 bytes at BK = 32, 8
+// rows x 128 bytes at BK = 64), so global reads stay coalesced, and rows are
+// stored with a 16-byte-chunk XOR swizzle so the MFMA operand reads (32 rows,
+// one chunk) are conflict-free.  Two shapes:
+//   Tall   (320 x 256, 8 waves of 160 x 64, 64-dim stages, 2 x 72 KiB ring,
+//           one workgroup per CU): the fewest operand bytes per output that
+//           the registers allow (160 accumulators per lane), and at a
+//           151,936-entry vocabulary 475 vocab tiles, under two rounds over
+//           the 256 CUs.  Used whenever it yields at least one tile per CU.
+//   Narrow (128 x 256, 4 waves of 64 x 128, 32-dim stages, 3 x 24 KiB ring,
+//           two workgroups per CU): more, smaller tiles for launches too
+//           small to fill the CUs with the tall tiles (e.g. a 32,000-entry
+//           pruned vocabulary at 256 rows: 250 tiles against 100).
+// The per-CU rate at which the operand loads arrive, not the MFMAs (the
+// LDS-to-MFMA loop alone runs at the MFMA ceiling), bounds this kernel, so
+// the tile shape that moves the fewest bytes per output wins: measured at
+// 151,936 x 4096, 0.48 -> 0.39 ms at 256 rows and 1.45 -> 1.38 ms at 1,024
+// rows against 256 x 256 tiles of 64 x 128 per wave.
 // Tiles are ordered so that all row tiles of one vocab tile, and a compact
 // block of vocab tiles, run together on one XCD (blockIdx % 8 picks the XCD),
 // which keeps every W and hidden slice in that XCD's L2 across row tiles.
 // The epilogue stores the fp32 logits and writes per (row, vocab tile) the
 // max, the sum of exp relative to it and the best Gumbel-max candidate
-// (Philox stream 0); with two workgroups per CU its ALU work overlaps the
-// other workgroup's stream.
+// (Philox stream 0).
 //
 // lm_row_reduce: merges the per-tile statistics of a row into lse and the
 // draft token.
@@ -40,34 +45,28 @@ namespace {
 
 constexpr int kThreads = 256;                       // lm_row_reduce: 4 waves
 
-// Workgroup shape by the number of waves along the vocabulary (WV) and the
-// hidden dims per pipeline stage (BK): 2 x WV waves, each owning 64 vocab x
-// 128 rows; a tile is 64 WV vocab x 256 rows.  (Measured at M = 1024: the
-// 256 x 256 tiles with 64-dim stages beat 32-dim stages by 1-3%; at one row
-// tile the 128 x 256 tiles stay ahead.)
-//   WV = 2, BK = 32: 128 x 256 tiles, 4 waves, 24 KiB stages, 3 stages: two
-//           workgroups per CU.
-//   WV = 4, BK = 64: 256 x 256 tiles, 8 waves, 64 KiB stages, 2 stages: one
-//           workgroup per CU with the same waves per SIMD, a third less
-//           operand traffic per output (hidden is re-read per vocab tile),
-//           whole 128-byte row segments per load and half as many stage
-//           barriers per MFMA.
-template <int WV, int BK>
-struct LmTile {
-  static constexpr int Waves = 2 * WV;
+// Tile shape: TV x TM MFMA tiles (32 x 32) per wave, WVN x WMN waves (vocab x
+// rows), BK hidden dims per stage, NS stages in the LDS ring.
+template <int TV_, int TM_, int WVN_, int WMN_, int BK_, int NS_>
+struct LmShape {
+  static constexpr int TV = TV_, TM = TM_, WVN = WVN_, WMN = WMN_, BK = BK_, NS = NS_;
+  static constexpr int Waves = WVN * WMN;
   static constexpr int Threads = 64 * Waves;
-  static constexpr int BV = 64 * WV;                      // vocab rows per tile
+  static constexpr int BV = 32 * TV * WVN;                // vocab rows per tile
+  static constexpr int BM = 32 * TM * WMN;                // draft rows per tile
   static constexpr int RowBytes = 2 * BK;                 // one row of a stage
   static constexpr int Chunks = BK / 8;                   // 16-byte chunks per row
   static constexpr int RowsPerLoad = 1024 / RowBytes;     // rows one wave load covers
   static constexpr int KSteps = BK / 16;                  // MFMA k-steps per stage
   static constexpr int WBytes = BV * RowBytes;            // W rows of one stage
-  static constexpr int HBytes = kLmBM * RowBytes;         // hidden rows of one stage
+  static constexpr int HBytes = BM * RowBytes;            // hidden rows of one stage
   static constexpr int StageBytes = WBytes + HBytes;
-  static constexpr int NS = BK == 32 ? 3 : 2;             // LDS stages (ring)
   static constexpr int WLoads = WBytes / 1024 / Waves;    // direct-to-LDS loads per wave per stage
   static constexpr int HLoads = HBytes / 1024 / Waves;
   static constexpr int Loads = WLoads + HLoads;
+  static_assert(WLoads * 1024 * Waves == WBytes && HLoads * 1024 * Waves == HBytes,
+                "a stage is a whole number of wave loads per wave");
+  static_assert(BM == kLmBM, "256-row tiles");
   // 16-byte chunk c of row r of a staged tile sits at byte
   // RowBytes r + 16 (c ^ swz(r)).  A 256-byte span of LDS covers all 64
   // banks; the rows sharing one span (256 / RowBytes of them) keep their
@@ -75,12 +74,13 @@ struct LmTile {
   // of one chunk fall in 16 different 16-byte bank groups.
   static __device__ __forceinline__ int swz(int r) { return (r / (256 / RowBytes)) & (Chunks - 1); }
 };
-static_assert(kLmBM == 256 && kLmHMultiple % 64 == 0, "stage layout assumes 256-row tiles, H a multiple of 64");
-static_assert(LmTile<2, 32>::BV == kLmBV, "the workspace is sized for the 128-vocab tiles");
-static_assert(LmTile<2, 32>::NS * LmTile<2, 32>::StageBytes == 72 * 1024 &&
-              LmTile<4, 64>::NS * LmTile<4, 64>::StageBytes == 128 * 1024, "two narrow or one wide workgroup per CU");
-static_assert(LmTile<2, 32>::WLoads == 2 && LmTile<2, 32>::HLoads == 4 && LmTile<4, 64>::WLoads == 4 &&
-              LmTile<4, 64>::HLoads == 4, "loads per wave per stage");
+using TallShape = LmShape<5, 2, 2, 4, 64, 2>;     // 320 x 256: 8 waves of 160 x 64
+using NarrowShape = LmShape<2, 4, 2, 2, 32, 3>;   // 128 x 256: 4 waves of 64 x 128
+static_assert(kLmHMultiple % 64 == 0, "H is a whole number of stages of either shape");
+static_assert(NarrowShape::BV == kLmBV, "the workspace is sized for the 128-vocab tiles");
+static_assert(TallShape::NS * TallShape::StageBytes == 144 * 1024 &&
+              NarrowShape::NS * NarrowShape::StageBytes == 72 * 1024,
+              "one tall or two narrow workgroups per CU");
 
 __device__ __forceinline__ void row_owner(const LmArgs& a, int m, uint32_t& rid, uint32_t& pos) {
   // request b with q_off[b] <= m < q_off[b+1]
@@ -100,10 +100,10 @@ __device__ __forceinline__ void row_owner(const LmArgs& a, int m, uint32_t& rid,
   pos = static_cast<uint32_t>(m - a.q_off[lo] + 1);
 }
 
-template <int WV, int BK>
-__global__ __launch_bounds__((LmTile<WV, BK>::Threads)) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <typename T>
+__global__ __launch_bounds__(T::Threads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void lm_gemm(LmArgs a) {
-  using T = LmTile<WV, BK>;
+  constexpr int BK = T::BK, WV = T::WVN, TV = T::TV, TM = T::TM;
   constexpr int kNS = T::NS, kStageBytes = T::StageBytes, kWBytes = T::WBytes;
   constexpr int kRow = T::RowBytes, kChunks = T::Chunks, kRowsPerLoad = T::RowsPerLoad;
   constexpr int kWLoads = T::WLoads, kHLoads = T::HLoads, kLoadsPerWave = T::Loads;
@@ -154,15 +154,15 @@ void lm_gemm(LmArgs a) {
   int offA[T::KSteps], offB[T::KSteps];
 #pragma unroll
   for (int s = 0; s < T::KSteps; ++s) {
-    offA[s] = (64 * wv + rr) * kRow + (((2 * s + h) ^ sw) << 4);
-    offB[s] = kWBytes + (128 * wm + rr) * kRow + (((2 * s + h) ^ sw) << 4);
+    offA[s] = (32 * TV * wv + rr) * kRow + (((2 * s + h) ^ sw) << 4);
+    offB[s] = kWBytes + (32 * TM * wm + rr) * kRow + (((2 * s + h) ^ sw) << 4);
   }
 
-  f32x16 acc[2][4];
+  f32x16 acc[TV][TM];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TV; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < TM; ++j) acc[i][j] = f32x16{};
 
   const int nk = a.H / BK;
 #pragma unroll
@@ -177,53 +177,53 @@ void lm_gemm(LmArgs a) {
     const char* st = smem + (kt % kNS) * kStageBytes;
 #pragma unroll
     for (int s = 0; s < T::KSteps; ++s) {
-      bf16x8 af[2], bfr[4];
+      bf16x8 af[TV], bfr[TM];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < TV; ++t)
         af[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + offA[s] + t * 32 * kRow));
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < TM; ++t)
         bfr[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + offB[s] + t * 32 * kRow));
 #pragma unroll
-      for (int tv = 0; tv < 2; ++tv)
+      for (int tv = 0; tv < TV; ++tv)
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm) acc[tv][tm] = mfma_32x32x16(af[tv], bfr[tm], acc[tv][tm]);
+        for (int tm = 0; tm < TM; ++tm) acc[tv][tm] = mfma_32x32x16(af[tv], bfr[tm], acc[tv][tm]);
     }
   }
 
   // ---------------------------------------------------------------- epilogue
-  // acc[tv][tm][i]: vocab v0 + 64 wv + 32 tv + 8 (i/4) + 4 h + i%4,
-  //                 row    m0 + 128 wm + 32 tm + lane%32
-  // Each lane holds 32 vocab entries of one row per row tile: it stores them
+  // acc[tv][tm][i]: vocab v0 + 32 TV wv + 32 tv + 8 (i/4) + 4 h + i%4,
+  //                 row    m0 + 32 TM wm + 32 tm + lane%32
+  // Each lane holds 16 TV vocab entries of one row per row tile: it stores them
   // and folds them into the row's (max, sum of exp, best Gumbel-max
   // candidate) over this vocab tile; the WV vocab waves (wv) merge through
   // LDS (the ring is free once every wave is past the loop).
   __syncthreads();
   float4* red = reinterpret_cast<float4*>(smem);   // [wv][wm][tm][32]
   const bool vec_ok = (a.V & 3) == 0;
-  static_for<0, 4>([&](auto TM) {
-    const int m = m0 + 128 * wm + 32 * TM + rr;
+  static_for<0, TM>([&](auto TMi) {
+    const int m = m0 + 32 * TM * wm + 32 * TMi + rr;
     const bool mok = m < a.M;
     uint32_t rid = 0, pos = 0;
     if (mok) row_owner(a, m, rid, pos);
     float mx = -FLT_MAX;
-    static_for<0, 2>([&](auto TV) {
+    static_for<0, TV>([&](auto TVi) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int v = v0 + 64 * wv + 32 * TV + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (v < a.V) mx = fmaxf(mx, acc[TV][TM][i]);
+        const int v = v0 + 32 * TV * wv + 32 * TVi + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (v < a.V) mx = fmaxf(mx, acc[TVi][TMi][i]);
       }
     });
     float se = 0.f;
     Cand best{-FLT_MAX, 0x7fffffff};
     if (mok) {
       float* row = a.logits + static_cast<size_t>(m) * a.V;
-      static_for<0, 2>([&](auto TV) {
+      static_for<0, TV>([&](auto TVi) {
 #pragma unroll
         for (int ar = 0; ar < 4; ++ar) {
-          const int vb = v0 + 64 * wv + 32 * TV + 8 * ar + 4 * h;   // multiple of 4
-          const f32x4 z = {acc[TV][TM][4 * ar], acc[TV][TM][4 * ar + 1], acc[TV][TM][4 * ar + 2],
-                           acc[TV][TM][4 * ar + 3]};
+          const int vb = v0 + 32 * TV * wv + 32 * TVi + 8 * ar + 4 * h;   // multiple of 4
+          const f32x4 z = {acc[TVi][TMi][4 * ar], acc[TVi][TMi][4 * ar + 1], acc[TVi][TMi][4 * ar + 2],
+                           acc[TVi][TMi][4 * ar + 3]};
           if (vec_ok && vb + 3 < a.V) {
             *reinterpret_cast<f32x4*>(row + vb) = z;
           } else {
@@ -260,12 +260,12 @@ void lm_gemm(LmArgs a) {
       if (better(ok, oi, best.key, best.idx)) best = Cand{ok, oi};
     }
     if (wv != 0 && h == 0)
-      red[((wv * 2 + wm) * 4 + TM) * 32 + rr] = make_float4(mx, se, best.key, __int_as_float(best.idx));
+      red[((wv * T::WMN + wm) * TM + TMi) * 32 + rr] = make_float4(mx, se, best.key, __int_as_float(best.idx));
     __syncthreads();
     if (wv == 0 && h == 0 && mok) {
 #pragma unroll
       for (int o2 = 1; o2 < WV; ++o2) {
-        const float4 o = red[((o2 * 2 + wm) * 4 + TM) * 32 + rr];
+        const float4 o = red[((o2 * T::WMN + wm) * TM + TMi) * 32 + rr];
         const int oi = __float_as_int(o.w);
         const float nmx = fmaxf(mx, o.x);
         se = se * __builtin_amdgcn_exp2f((mx - nmx) * kLog2e) + o.y * __builtin_amdgcn_exp2f((o.x - nmx) * kLog2e);
@@ -305,19 +305,19 @@ __global__ __launch_bounds__(kThreads) void lm_row_reduce(LmArgs a) {
 
 }  // namespace
 
-template <int WV, int BK>
+template <typename T>
 hipError_t launch_gemm(LmArgs& b, hipStream_t s) {
-  b.n_vt = (b.V + LmTile<WV, BK>::BV - 1) / LmTile<WV, BK>::BV;
+  b.n_vt = (b.V + T::BV - 1) / T::BV;
   const int slots = (b.n_vt + 7) / 8 * b.n_mt;
-  return launch_kernel(lm_gemm<WV, BK>, dim3(slots * 8), dim3(LmTile<WV, BK>::Threads), s, b);
+  return launch_kernel(lm_gemm<T>, dim3(slots * 8), dim3(T::Threads), s, b);
 }
 
 hipError_t launch_lm_head(const LmArgs& a, hipStream_t s) {
-  // several row tiles (M > 256): 256 x 256 tiles with 64-dim stages; one
-  // row tile: 128-vocab tiles, whose 1,187 tiles at V = 151,936 spread over
-  // twice as many resident workgroups (measured ahead at M = 256)
+  // the tall tiles when they give every CU at least one tile, else the
+  // narrow ones (two workgroups per CU, 2.5x as many tiles)
   LmArgs b = a;
-  hipError_t e = a.n_mt > 1 ? launch_gemm<4, 64>(b, s) : launch_gemm<2, 32>(b, s);
+  const int64_t tall_tiles = static_cast<int64_t>((a.V + TallShape::BV - 1) / TallShape::BV) * a.n_mt;
+  hipError_t e = tall_tiles >= 256 ? launch_gemm<TallShape>(b, s) : launch_gemm<NarrowShape>(b, s);
   if (e == hipSuccess) e = launch_kernel(lm_row_reduce, dim3(b.M), dim3(kThreads), s, b);
   return e;
 }

@@ -99,7 +99,11 @@ def test_attention_mha_and_small_groups():
                                    (257, 512, 4096), (256, 64, 768), (600, 128, 1001),
                                    (1024, 64, 5000),
                                    (16, 64, 70001), (256, 64, 65600),
-                                   (16, 256, 70001), (600, 128, 65600)])
+                                   (16, 256, 70001), (600, 128, 65600),
+                                   # 320 x 256 tiles (at least 256 of them):
+                                   # ragged vocab and row tails
+                                   (600, 64, 40003), (257, 128, 82001),
+                                   (8, 64, 151936), (1024, 64, 20481)])
 def test_lm_head_shapes(M, H, V):
     cfg = C0_TINY.with_(name="lm", batch=1, draft_k=M, hidden=H, vocab=V, seed=M * 7 + V)
     inp = StepInputs(cfg)
