@@ -198,15 +198,61 @@ void lm_gemm(LmArgs a) {
   // and folds them into the row's (max, sum of exp, best Gumbel-max
   // candidate) over this vocab tile; the WV vocab waves (wv) merge through
   // LDS (the ring is free once every wave is past the loop).
+  //
+  // Full tiles (every row and vocab entry in range, 16-byte aligned rows; all
+  // but the last vocab tile) take a branch-free path that draws with the
+  // ratio form of the Gumbel-max key: with p_v = exp(z_v - max) (the terms of
+  // the sum of exp) and E_v = -ln u_v, argmax_v (z_v - ln E_v) is argmax_v
+  // p_v / E_v, tracked by comparing p_v E_best > p_best E_v, so each entry
+  // costs one logarithm instead of two; the lane's best key in log form is
+  // max + ln(p_best / E_best).  It ranks entries as the log form does up to
+  // fp32 rounding (about 1e-7 in key units).
   __syncthreads();
   float4* red = reinterpret_cast<float4*>(smem);   // [wv][wm][tm][32]
   const bool vec_ok = (a.V & 3) == 0;
+  const bool full = !a.greedy && vec_ok && v0 + T::BV <= a.V && m0 + kLmBM <= a.M;
   static_for<0, TM>([&](auto TMi) {
     const int m = m0 + 32 * TM * wm + 32 * TMi + rr;
     const bool mok = m < a.M;
     uint32_t rid = 0, pos = 0;
     if (mok) row_owner(a, m, rid, pos);
     float mx = -FLT_MAX;
+    float se = 0.f;
+    Cand best{-FLT_MAX, 0x7fffffff};
+    if (full) {
+      static_for<0, TV>([&](auto TVi) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[TVi][TMi][i]);
+      });
+      float* row = a.logits + static_cast<size_t>(m) * a.V;
+      float pb = -1.f, eb = 1.f;
+      int ib = 0x7fffffff;
+      static_for<0, TV>([&](auto TVi) {
+#pragma unroll
+        for (int ar = 0; ar < 4; ++ar) {
+          const int vb = v0 + 32 * TV * wv + 32 * TVi + 8 * ar + 4 * h;   // multiple of 4
+          const f32x4 z = {acc[TVi][TMi][4 * ar], acc[TVi][TMi][4 * ar + 1], acc[TVi][TMi][4 * ar + 2],
+                           acc[TVi][TMi][4 * ar + 3]};
+          *reinterpret_cast<f32x4*>(row + vb) = z;
+          const u32x4 w = philox4x32_10(u32x4{static_cast<uint32_t>(vb >> 2), pos, rid, kStreamDraft},
+                                        a.key0, a.key1);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float pv = __builtin_amdgcn_exp2f((z[e] - mx) * kLog2e);
+            se += pv;
+            const float u = static_cast<float>((w[e] >> 9) * 2u + 1u) * 5.9604644775390625e-8f;
+            const float ev = -kLn2 * __builtin_amdgcn_logf(u);              // -ln u > 0
+            // entries arrive in increasing order: a tie keeps the smaller index
+            if (pv * eb > pb * ev) {
+              pb = pv;
+              eb = ev;
+              ib = vb + e;
+            }
+          }
+        }
+      });
+      best = Cand{mx + kLn2 * (__builtin_amdgcn_logf(pb) - __builtin_amdgcn_logf(eb)), ib};
+    } else {
     static_for<0, TV>([&](auto TVi) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -214,8 +260,6 @@ void lm_gemm(LmArgs a) {
         if (v < a.V) mx = fmaxf(mx, acc[TVi][TMi][i]);
       }
     });
-    float se = 0.f;
-    Cand best{-FLT_MAX, 0x7fffffff};
     if (mok) {
       float* row = a.logits + static_cast<size_t>(m) * a.V;
       static_for<0, TV>([&](auto TVi) {
@@ -248,6 +292,7 @@ void lm_gemm(LmArgs a) {
           }
         }
       });
+    }
     }
     // the two halves of the wave hold the same row, other vocab entries
     {
