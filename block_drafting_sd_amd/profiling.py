@@ -3,7 +3,10 @@
 ``python -m block_drafting_sd_amd.profiling trace <run_results.db>`` prints
 the per-kernel dispatch count and average / total duration;
 ``python -m block_drafting_sd_amd.profiling pmc <run_results.db>`` prints the
-average value per dispatch of every collected counter, per kernel.
+average value per dispatch of every collected counter, per kernel;
+``python -m block_drafting_sd_amd.profiling pmcgrid <run_results.db>`` the
+same per (kernel, grid size), which separates dispatches of one kernel with
+different sizes (e.g. a calibration copy of known size from other copies).
 
 rocprofv3 writes its results as a SQLite database (``--output-format`` rocpd,
 the default); the views ``kernels`` and ``counters_collection`` hold one row
@@ -45,6 +48,26 @@ def counters(db: str):
     return out
 
 
+def counters_by_grid(db: str):
+    """{(kernel, grid size): {counter: [value per dispatch]}}."""
+    con = sqlite3.connect(db)
+    rows = con.execute("select kernel_name, grid_size, dispatch_id, counter_name, sum(value) "
+                       "from counters_collection group by dispatch_id, counter_name")
+    out = collections.defaultdict(lambda: collections.defaultdict(list))
+    for kn, grid, _, cn, v in rows:
+        out[(short_name(kn), int(grid))][cn].append(v)
+    return out
+
+
+def pmc_grid_table(db: str) -> str:
+    c = counters_by_grid(db)
+    lines = ["| kernel | grid size | counter | dispatches | avg per dispatch |", "|---|---|---|---|---|"]
+    for (k, grid), cs in sorted(c.items()):
+        for cn, vals in sorted(cs.items()):
+            lines.append(f"| `{k}` | {grid} | {cn} | {len(vals)} | {sum(vals) / len(vals):.6g} |")
+    return "\n".join(lines)
+
+
 def trace_table(db: str) -> str:
     t = kernel_times(db)
     total = sum(sum(v) for v in t.values()) or 1
@@ -65,10 +88,11 @@ def pmc_table(db: str) -> str:
 
 
 def main(argv):
-    if len(argv) != 3 or argv[1] not in ("trace", "pmc"):
+    tables = {"trace": trace_table, "pmc": pmc_table, "pmcgrid": pmc_grid_table}
+    if len(argv) != 3 or argv[1] not in tables:
         print(__doc__)
         return 2
-    print(trace_table(argv[2]) if argv[1] == "trace" else pmc_table(argv[2]))
+    print(tables[argv[1]](argv[2]))
     return 0
 
 
