@@ -295,6 +295,9 @@ def main():
                          "the rank-256 sequential correction, DeLS-Spec fusion (full prefix, "
                          "Markov local head of rank 256, alpha = beta = 0.3)")
     ap.add_argument("--greedy", action="store_true", help="temperature 0 on both sides")
+    ap.add_argument("--target-sigma", type=float, default=0.0,
+                    help="for a drafter-plus-noise target: one noise sigma for every request "
+                         "(e.g. 0.5) instead of the workload's per-request spread")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured HBM-read and MFMA ceilings (library probes, untimed) "
                          "and the library-GEMM reference of the LM head")
@@ -324,6 +327,12 @@ def main():
     sd.load()
     dev = torch.device("cuda:0")
     cfg = by_index(args.config)
+    if args.target_sigma > 0:
+        if cfg.target[0] != "drafter_plus_noise":
+            print("--target-sigma applies to drafter-plus-noise targets only", file=sys.stderr)
+            sys.exit(2)
+        sg = args.target_sigma
+        cfg = cfg.with_(name=f"{cfg.name}_sigma{sg:g}", target=("drafter_plus_noise", sg, sg))
     inp = StepInputs(cfg)
     b = inp.budgets
     t_gen = time.perf_counter()
