@@ -185,6 +185,17 @@ __device__ __forceinline__ bool locate_item(const AttnArgs& a, int block, ItemLo
   const int k = block >> 3;
   const int u = (k / a.hkv) * 8 + x;       // unit, in execution order
   L.g = k % a.hkv;
+  if (a.direct) {
+    // every request is one unit (a prefix within one split, with the draft
+    // block on it, or the block alone): the unit is the request and its
+    // single item writes its rows, so no work list or partial slot is used
+    if (u >= a.batch) return false;
+    L.b = u;
+    L.r = request_info(a, u);
+    L.sp = 0;
+    L.item = -1;
+    return L.r.kb > 0;
+  }
   // Work items beyond the partials' capacity (the prefix lengths add up to
   // more than the host bound) make the whole call invalid: nothing is
   // computed and attn_combine marks every row
@@ -664,6 +675,12 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
 
 template <int D>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
+  if (a.direct) {
+    // one item per (request, kv head), each writing its own rows
+    const dim3 grid((a.batch + 7) / 8 * 8 * a.hkv);
+    return a.rows > 64 ? launch_kernel(attn_splitk<D, kAttnStages, 4>, grid, dim3(256), s, a)
+                       : launch_kernel(attn_splitk<D, kAttnStages, 2>, grid, dim3(128), s, a);
+  }
   hipError_t e = launch_kernel(attn_worklist, dim3(1), dim3(1024), s, a);
   if (e == hipSuccess && a.max_items > 0)
     e = a.rows > 64 ? launch_kernel(attn_splitk<D, kAttnStages, 4>, dim3(attn_grid(a)), dim3(256), s, a)

@@ -7,6 +7,7 @@
 
 #include <math.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "sd_internal.h"
@@ -153,6 +154,13 @@ sd_status draft_attn_impl(const void* q, const void* k_blk, const void* v_blk, c
   a.split_tokens = L.split;
   a.max_items = static_cast<int32_t>(L.max_items);
   a.rows = L.rows;
+  {
+    // longest prefix span one request can stream: the whole page table row,
+    // or with a window its last W tokens from the page start below them
+    const int64_t span = window > 0 ? std::min<int64_t>(int64_t(window) + 15, int64_t(max_pages) * 16)
+                                    : int64_t(max_pages) * 16;
+    a.direct = span <= L.split && n_summary == 0 ? 1 : 0;
+  }
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.item_off = reinterpret_cast<int32_t*>(ws + L.off_item_off);
   a.unit_off = reinterpret_cast<int32_t*>(ws + L.off_unit_off);

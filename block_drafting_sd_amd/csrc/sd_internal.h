@@ -37,6 +37,9 @@ struct AttnArgs {
   int32_t split_tokens;   // prefix tokens per work item (multiple of 64, <= 32768)
   int32_t max_items;      // work items the partial buffers hold
   int32_t rows;           // query rows per work item: 64 (two waves) or 128 (four)
+  int32_t direct;         // 1: every request is at most one work item (its prefix span fits
+                          // one split and there is no summary), so the item of a request
+                          // writes its rows itself: no work list, no partials, no merge
   float scale_log2;       // softmax_scale * log2(e)
   int32_t* item_off;      // [batch + 1] first work item of each request
   int32_t* unit_off;      // [3][batch + 1] first unit of each request among the block
