@@ -111,17 +111,20 @@ __device__ __forceinline__ void unit_counts(const AttnArgs& a, const ReqInfo& r,
   v[0] = r.per - r.ns;
 }
 
-// Exclusive prefix sums over the requests (one workgroup): of each kind of
-// unit (the execution order) and of the work items (the partials' slots).
-// 1024 requests per round: a shuffle scan inside each wave, then the sums of
-// the preceding waves.
-__global__ __launch_bounds__(1024) void attn_worklist(AttnArgs a) {
-  __shared__ int wsum[3][16];
+// Exclusive prefix sums over the requests, by one workgroup of T threads:
+// of each kind of unit (unit_off[c (batch + 1) + b], the execution order) and
+// of the work items (item_off[b], the partials' slots), with the totals at
+// index batch.  T requests per round: a shuffle scan inside each wave, then
+// the sums of the preceding waves.  Every thread of the workgroup calls it.
+template <int T>
+__device__ void scan_units(const AttnArgs& a, int* unit_off, int* item_off) {
+  constexpr int NW = T / 64;
+  __shared__ int wsum[3][NW];
   __shared__ int carry[3];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if (tid < 3) carry[tid] = 0;
   __syncthreads();
-  for (int base = 0; base < a.batch; base += 1024) {
+  for (int base = 0; base < a.batch; base += T) {
     const int b = base + tid;
     int v[3] = {0, 0, 0};
     if (b < a.batch) unit_counts(a, request_info(a, b), v);
@@ -146,20 +149,27 @@ __global__ __launch_bounds__(1024) void attn_worklist(AttnArgs a) {
     }
     if (b < a.batch) {
 #pragma unroll
-      for (int c = 0; c < 3; ++c) a.unit_off[c * (a.batch + 1) + b] = ex[c];
-      a.item_off[b] = a.hkv * (ex[0] + ex[1] + ex[2]);
+      for (int c = 0; c < 3; ++c) unit_off[c * (a.batch + 1) + b] = ex[c];
+      item_off[b] = a.hkv * (ex[0] + ex[1] + ex[2]);
     }
     __syncthreads();   // every thread has read carry and wsum
-    if (tid == 1023)
+    if (tid == T - 1)
 #pragma unroll
       for (int c = 0; c < 3; ++c) carry[c] = ex[c] + v[c];
     __syncthreads();
   }
   if (tid == 0) {
 #pragma unroll
-    for (int c = 0; c < 3; ++c) a.unit_off[c * (a.batch + 1) + a.batch] = carry[c];
-    a.item_off[a.batch] = a.hkv * (carry[0] + carry[1] + carry[2]);
+    for (int c = 0; c < 3; ++c) unit_off[c * (a.batch + 1) + a.batch] = carry[c];
+    item_off[a.batch] = a.hkv * (carry[0] + carry[1] + carry[2]);
   }
+  __syncthreads();
+}
+
+// The work list in global memory, for batches too large for the split-K
+// workgroups to scan themselves.
+__global__ __launch_bounds__(1024) void attn_worklist(AttnArgs a) {
+  scan_units<1024>(a, a.unit_off, a.item_off);
 }
 
 // Work item of a workgroup.  A unit is one (request, split) -- a prefix split,
@@ -180,7 +190,8 @@ struct ItemLoc {
   ReqInfo r;
 };
 
-__device__ __forceinline__ bool locate_item(const AttnArgs& a, int block, ItemLoc& L) {
+__device__ __forceinline__ bool locate_item(const AttnArgs& a, int block, const int* unit_off,
+                                            const int* item_off, ItemLoc& L) {
   const int x = block & 7;
   const int k = block >> 3;
   const int u = (k / a.hkv) * 8 + x;       // unit, in execution order
@@ -199,9 +210,9 @@ __device__ __forceinline__ bool locate_item(const AttnArgs& a, int block, ItemLo
   // Work items beyond the partials' capacity (the prefix lengths add up to
   // more than the host bound) make the whole call invalid: nothing is
   // computed and attn_combine marks every row
-  if (a.item_off[a.batch] > a.max_items) return false;
-  const int total = a.item_off[a.batch];
-  const int* eo = a.unit_off;                   // block and summary units
+  if (item_off[a.batch] > a.max_items) return false;
+  const int total = item_off[a.batch];
+  const int* eo = unit_off;                     // block and summary units
   const int* fo = eo + (a.batch + 1);           // full-length prefix splits
   const int* po = fo + (a.batch + 1);           // shorter last splits
   const int ne = eo[a.batch], nf = fo[a.batch], np = po[a.batch];
@@ -220,7 +231,7 @@ __device__ __forceinline__ bool locate_item(const AttnArgs& a, int block, ItemLo
   L.b = lo;
   L.r = request_info(a, lo);
   L.sp = kind == 0 ? L.r.ns + (uu - off[lo]) : (kind == 1 ? uu - off[lo] : L.r.ns - 1);
-  L.item = a.item_off[lo] + L.g * L.r.per + L.sp;
+  L.item = item_off[lo] + L.g * L.r.per + L.sp;
   return L.item < total;
 }
 
@@ -530,7 +541,20 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   ItemLoc L;
-  if (!locate_item(a, blockIdx.x, L)) return;
+  if (!a.direct && a.batch <= kAttnLocalScan) {
+    // the workgroup scans the requests itself (no work-list launch);
+    // workgroup 0 also stores the offsets for attn_combine
+    __shared__ int s_unit_off[3 * (kAttnLocalScan + 1)];
+    __shared__ int s_item_off[kAttnLocalScan + 1];
+    scan_units<64 * W>(a, s_unit_off, s_item_off);
+    if (blockIdx.x == 0) {
+      for (int i = threadIdx.x; i < 3 * (a.batch + 1); i += 64 * W) a.unit_off[i] = s_unit_off[i];
+      for (int i = threadIdx.x; i <= a.batch; i += 64 * W) a.item_off[i] = s_item_off[i];
+    }
+    if (!locate_item(a, blockIdx.x, s_unit_off, s_item_off, L)) return;
+  } else if (!locate_item(a, blockIdx.x, a.unit_off, a.item_off, L)) {
+    return;
+  }
   const int b = L.b, g = L.g, sp = L.sp, item = L.item;
   const ReqInfo r = L.r;
   const int rows = a.group * r.kb;
@@ -681,7 +705,8 @@ hipError_t launch(const AttnArgs& a, hipStream_t s) {
     return a.rows > 64 ? launch_kernel(attn_splitk<D, kAttnStages, 4>, grid, dim3(256), s, a)
                        : launch_kernel(attn_splitk<D, kAttnStages, 2>, grid, dim3(128), s, a);
   }
-  hipError_t e = launch_kernel(attn_worklist, dim3(1), dim3(1024), s, a);
+  hipError_t e = a.batch > kAttnLocalScan ? launch_kernel(attn_worklist, dim3(1), dim3(1024), s, a)
+                                           : hipSuccess;
   if (e == hipSuccess && a.max_items > 0)
     e = a.rows > 64 ? launch_kernel(attn_splitk<D, kAttnStages, 4>, dim3(attn_grid(a)), dim3(256), s, a)
                     : launch_kernel(attn_splitk<D, kAttnStages, 2>, dim3(attn_grid(a)), dim3(128), s, a);

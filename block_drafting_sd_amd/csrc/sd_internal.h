@@ -57,6 +57,8 @@ constexpr int kAttnTile = 32;        // keys per inner tile (two 16-token pages)
 constexpr int kAttnStages = 4;       // LDS ring stages of the prefix stream
 constexpr int kAttnMaxSplitPages = 2048;   // split_tokens <= 2048 * 16
 constexpr int kAttnMaxSummary = 64;  // summary entries per KV head
+constexpr int kAttnLocalScan = 64;   // batches up to this size: each split-K workgroup
+                                     // scans the requests itself (no work-list launch)
 
 int64_t attn_max_items(int32_t batch, int32_t hkv, int64_t max_total_ctx,
                        int32_t split_tokens);
