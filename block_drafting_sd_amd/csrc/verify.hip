@@ -64,43 +64,70 @@ __global__ __launch_bounds__(kThreads) void verify_rowstats(VerifyArgs a) {
       for (int e = 0; e < 4; ++e) x[j][e] = v + e < len ? src[v + e] : -INFINITY;
     }
   }
-  Cand best{-FLT_MAX, 0x7fffffff};
+  // The first argmax is needed only at temperature 0 (greedy tests and
+  // draws); sampling needs the max alone, a cheaper reduction.
+  float mx;
+  int amax = 0;
+  if (a.greedy) {
+    Cand best{-FLT_MAX, 0x7fffffff};
 #pragma unroll
-  for (int j = 0; j < kGroups; ++j)
+    for (int j = 0; j < kGroups; ++j)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int v = lo + 4 * (threadIdx.x + kThreads * j) + e;
-      if (v < len && better(x[j][e], v, best.key, best.idx)) best = Cand{x[j][e], v};
-    }
-  best = block_best<kThreads>(best, shk, shi);
-  const float mx = best.key;
+      for (int e = 0; e < 4; ++e) {
+        const int v = lo + 4 * (threadIdx.x + kThreads * j) + e;
+        if (v < len && better(x[j][e], v, best.key, best.idx)) best = Cand{x[j][e], v};
+      }
+    best = block_best<kThreads>(best, shk, shi);
+    mx = best.key;
+    amax = best.idx;
+  } else {
+    float m = -FLT_MAX;   // entries past the row are -inf
+#pragma unroll
+    for (int j = 0; j < kGroups; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m = fmaxf(m, x[j][e]);
+    mx = block_reduce_max<kThreads>(m, sh);
+  }
   float se = 0.f;
 #pragma unroll
   for (int j = 0; j < kGroups; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) se += __builtin_amdgcn_exp2f((x[j][e] - mx) * kLog2e);
   se = block_reduce_sum<kThreads>(se, sh);
-  if (threadIdx.x == 0) a.row_part[blockIdx.x] = make_float4(mx, se, __int_as_float(best.idx), 0.f);
+  if (threadIdx.x == 0) a.row_part[blockIdx.x] = make_float4(mx, se, __int_as_float(amax), 0.f);
 }
 
-// Log-normaliser and first argmax of a row from its n chunk partials; the
-// partials are read eight at a time (clamped index, duplicates weighted zero)
-// so the loads overlap.
+// Log-normaliser of a row from its n chunk partials, and with kArgmax its
+// first argmax (temperature 0 only).  Loads are issued U at a time (clamped
+// index, duplicates weighted zero) so their latencies overlap: when sampling,
+// (max, sum) pairs 32 at a time, so at up to 32 chunks (a vocabulary of up to
+// 262,144) all of a row's partials are in flight together.
+template <bool kArgmax>
 __device__ float merge_row(const float4* part, int n, int& amax) {
-  constexpr int U = 8;
+  constexpr int U = kArgmax ? 16 : 32;
   float mx = -FLT_MAX;
   float s = 0.f;
   Cand best{-FLT_MAX, 0x7fffffff};
   for (int i0 = 0; i0 < n; i0 += U) {
     float4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = part[min(i0 + u, n - 1)];
+    for (int u = 0; u < U; ++u) {
+      const float4* pp = part + min(i0 + u, n - 1);
+      if constexpr (kArgmax) {
+        v[u] = *pp;
+      } else {
+        const float2 m2 = *reinterpret_cast<const float2*>(pp);
+        v[u] = make_float4(m2.x, m2.y, 0.f, 0.f);
+      }
+    }
     float m2 = mx;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       m2 = fmaxf(m2, v[u].x);
-      const int idx = __float_as_int(v[u].z);
-      if (i0 + u < n && better(v[u].x, idx, best.key, best.idx)) best = Cand{v[u].x, idx};
+      if constexpr (kArgmax) {
+        const int idx = __float_as_int(v[u].z);
+        if (i0 + u < n && better(v[u].x, idx, best.key, best.idx)) best = Cand{v[u].x, idx};
+      }
     }
     s *= __builtin_amdgcn_exp2f((mx - m2) * kLog2e);
 #pragma unroll
@@ -110,6 +137,10 @@ __device__ float merge_row(const float4* part, int n, int& amax) {
   }
   amax = best.idx;
   return mx + logf(s);
+}
+
+__device__ __forceinline__ float merge_row(const VerifyArgs& a, const float4* part, int& amax) {
+  return a.greedy ? merge_row<true>(part, a.n_chunks, amax) : merge_row<false>(part, a.n_chunks, amax);
 }
 
 // Shared memory of one request's decision.
@@ -149,32 +180,36 @@ __device__ void decide_request(const VerifyArgs& a, int b, bool writer, DecideSm
   for (int c0 = 0;; c0 += kDecideChunk) {
     const int n = min(kDecideChunk, nv - c0);
     const bool last = c0 + n == nv;   // this pass also holds the bonus row nv
-    // A: log-normalisers of the rows this pass touches
-    for (int i = tid; i < n + (last ? 1 : 0); i += kThreads)
-      sm.lse_p[i] = merge_row(a.row_part + static_cast<size_t>(t0 + c0 + i) * a.n_chunks, a.n_chunks,
-                              sm.amax_p[i]);
-    for (int i = tid; i < n; i += kThreads) {
-      int unused;
-      sm.lse_q[i] = a.draft_lse ? a.draft_lse[q0 + c0 + i]
-                                : merge_row(a.row_part + static_cast<size_t>(a.R + q0 + c0 + i) * a.n_chunks,
-                                            a.n_chunks, unused);
-    }
-    __syncthreads();
-
-    // B: the pass's ratio tests in parallel (eq. (1)): r_j = min(1,
-    // p_j(y_j)/q_j(y_j)); at temperature 0 both distributions are one-hot and
-    // r_j = [y_j = argmax p_j]
-    for (int i = tid; i < n; i += kThreads) {
+    // A: per position (one thread each), the log-normalisers of its rows
+    // and its ratio test (eq. (1)): r_j = min(1, p_j(y_j)/q_j(y_j)); at
+    // temperature 0 both distributions are one-hot and r_j = [y_j = argmax
+    // p_j].  The token, the row partials and the draft normaliser do not
+    // depend on one another, so their loads are issued together, and the two
+    // logits at y_j follow in a second round.  The thread after the last
+    // position takes the bonus row.
+    for (int i = tid; i < n + (last ? 1 : 0); i += kThreads) {
+      const bool test = i < n;
       const int j = c0 + i + 1;
-      const int y = clampi(a.tokens[q0 + j - 1], 0, a.V - 1);
+      const int y = test ? clampi(a.tokens[q0 + j - 1], 0, a.V - 1) : 0;
+      const float lqd = test && a.draft_lse ? a.draft_lse[q0 + j - 1] : 0.f;
+      int amax;
+      const float lse_p = merge_row(a, a.row_part + static_cast<size_t>(t0 + c0 + i) * a.n_chunks, amax);
+      sm.lse_p[i] = lse_p;
+      sm.amax_p[i] = amax;
+      if (!test) continue;
+      int unused;
+      const float lse_q = a.draft_lse ? lqd
+                                      : merge_row<false>(a.row_part + static_cast<size_t>(a.R + q0 + j - 1) * a.n_chunks,
+                                                         a.n_chunks, unused);
+      sm.lse_q[i] = lse_q;
       float r = 1.f;
       if (a.greedy) {
-        r = y == sm.amax_p[i] ? 1.f : 0.f;
+        r = y == amax ? 1.f : 0.f;
       } else {
         const int iy = a.vinv ? a.vinv[y] : y;   // y in the drafter's vocabulary
-        const float lp = a.target[static_cast<size_t>(t0 + j - 1) * a.V + y] - sm.lse_p[i];
+        const float lp = a.target[static_cast<size_t>(t0 + j - 1) * a.V + y] - lse_p;
         const float lq = iy >= 0 && iy < a.v_draft
-                             ? a.draft[static_cast<size_t>(q0 + j - 1) * a.v_draft + iy] - sm.lse_q[i]
+                             ? a.draft[static_cast<size_t>(q0 + j - 1) * a.v_draft + iy] - lse_q
                              : -INFINITY;
         if (expf(lq) > 0.f) r = fminf(1.f, expf(lp - lq));
       }
