@@ -148,7 +148,7 @@ struct DecideSmem {
   float lse_p[kDecideChunk + 1];   // the pass's rows, and the bonus row after the last one
   int amax_p[kDecideChunk + 1];
   float lse_q[kDecideChunk];
-  int ok[kDecideChunk];
+  int first_reject[kThreads / 64];   // per wave: first rejected position of the pass, or n
   int reject;                      // first rejected position (0-based), or nv
   float lse_p_dec, lse_q_dec;      // normalisers of the row the draw uses
   float4 dec;   // (accepted as int bits or -1, lse_p, lse_q, tested as int bits)
@@ -187,6 +187,7 @@ __device__ void decide_request(const VerifyArgs& a, int b, bool writer, DecideSm
     // depend on one another, so their loads are issued together, and the two
     // logits at y_j follow in a second round.  The thread after the last
     // position takes the bonus row.
+    bool rejected = false;   // position tid of this pass was rejected
     for (int i = tid; i < n + (last ? 1 : 0); i += kThreads) {
       const bool test = i < n;
       const int j = c0 + i + 1;
@@ -215,22 +216,27 @@ __device__ void decide_request(const VerifyArgs& a, int b, bool writer, DecideSm
       }
       const u32x4 w = philox4x32_10(u32x4{0u, static_cast<uint32_t>(j), rid, kStreamAccept},
                                     a.key0, a.key1);
-      sm.ok[i] = accept_from_bits(w[0]) < r;
+      rejected = !(accept_from_bits(w[0]) < r);
       if (writer && a.accept_ratio) a.accept_ratio[q0 + j - 1] = r;
+    }
+    {
+      // first rejection of each wave's positions (position i is thread i)
+      const uint64_t rj = __ballot(rejected);
+      if ((tid & 63) == 0) sm.first_reject[tid >> 6] = rj ? (tid & ~63) + __builtin_ctzll(rj) : n;
     }
     __syncthreads();
 
     // C: the first rejection ends the round; keep the normalisers of the row
     // the draw will use (the rejected one, or the bonus row)
     if (tid == 0) {
-      if (sm.reject == nv)
-        for (int i = 0; i < n; ++i)
-          if (!sm.ok[i]) {
-            sm.reject = c0 + i;
-            sm.lse_p_dec = sm.lse_p[i];
-            sm.lse_q_dec = sm.lse_q[i];
-            break;
-          }
+      int first = n;
+#pragma unroll
+      for (int w = 0; w < kThreads / 64; ++w) first = min(first, sm.first_reject[w]);
+      if (sm.reject == nv && first < n) {
+        sm.reject = c0 + first;
+        sm.lse_p_dec = sm.lse_p[first];
+        sm.lse_q_dec = sm.lse_q[first];
+      }
       if (last && sm.reject == nv) {
         sm.lse_p_dec = sm.lse_p[n];
         sm.lse_q_dec = 0.f;
@@ -298,8 +304,8 @@ __global__ __launch_bounds__(kThreads) void verify_sample(VerifyArgs a) {
   const int j = acc + 1;                      // position of the drawn token
   const float* xrow = a.target + static_cast<size_t>(t0 + acc) * a.V;
   const float* zrow = a.draft + static_cast<size_t>(q0 + acc) * a.v_draft;
-  const float lse_p = dec.y;
-  const float lse_q = dec.z;
+  const float lp2 = dec.y * kLog2e;   // log-normalisers in base-2 units
+  const float lq2 = dec.z * kLog2e;
 
   // D: Gumbel-max candidates of this vocab chunk; thread t holds entries
   // 4 (t + 256 j) + e of the chunk
@@ -343,10 +349,13 @@ __global__ __launch_bounds__(kThreads) void verify_sample(VerifyArgs a) {
         const float kp = x + gn;
         if (better(kp, v, best_p.key, best_p.idx)) best_p = Cand{kp, v};
         if (residual) {
-          const float res = expf(x - lse_p) - expf(zv[e] - lse_q);
+          // p and q by the hardware base-2 exponential of one fused
+          // multiply-add each (one rounding, as x - lse alone has)
+          const float res = __builtin_amdgcn_exp2f(fmaf(x, kLog2e, -lp2)) -
+                            __builtin_amdgcn_exp2f(fmaf(zv[e], kLog2e, -lq2));
           if (res > 0.f) {
             any_pos = 1;
-            const float kr = logf(res) + gn;
+            const float kr = kLn2 * __builtin_amdgcn_logf(res) + gn;
             if (better(kr, v, best_r.key, best_r.idx)) best_r = Cand{kr, v};
           }
         }
