@@ -481,7 +481,8 @@ def main():
                    "summary_entries": opts.n_summary, "causal_block": opts.causal_block,
                    "draft_vocab": v_draft, "markov_rank": opts.markov_rank,
                    "markov_alpha": opts.markov_alpha, "prior_beta": opts.prior_beta},
-        "roofline": {"kernel": "sd_draft_attn call: attn_worklist + attn_splitk + attn_combine",
+        "roofline": {"kernel": "sd_draft_attn call: attn_splitk + attn_combine (+ attn_worklist "
+                               "above 64 requests; attn_splitk alone when each request fits one split)",
                      "bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic() if args.path == "full" and args.config == 2
