@@ -407,14 +407,14 @@ __device__ __forceinline__ void issue_stage(const AttnArgs& a, int g, int pg0, i
     const int pg = sel ? pg1 : pg0;
     const uint16_t* src =
         a.k_cache + (static_cast<size_t>(pg) * a.hkv + g) * (D * 16) + h * 128 + slot * 8;
-    static_for<0, D / 16>([&](auto c) { dma16(src + c * 256, lds + c * 1024); });
+    static_for<0, D / 16>([&](auto c) { dma16_stream(src + c * 256, lds + c * 1024); });
   } else if (wave == 1) {
     const size_t col = (lane & 31) * 16 + 8 * h;
     const uint16_t* src0 = a.v_cache + (static_cast<size_t>(pg0) * a.hkv + g) * (D * 16) + col;
     const uint16_t* src1 = a.v_cache + (static_cast<size_t>(pg1) * a.hkv + g) * (D * 16) + col;
     static_for<0, D / 32>([&](auto m) {
-      dma16(src0 + m * 512, lds + (D / 16 + m) * 1024);
-      dma16(src1 + m * 512, lds + (D / 16 + D / 32 + m) * 1024);
+      dma16_stream(src0 + m * 512, lds + (D / 16 + m) * 1024);
+      dma16_stream(src1 + m * 512, lds + (D / 16 + D / 32 + m) * 1024);
     });
   }
 }

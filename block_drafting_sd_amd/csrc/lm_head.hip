@@ -142,7 +142,11 @@ void lm_gemm(LmArgs a) {
       constexpr bool is_w = i < kWLoads;
       const uint32_t dst = is_w ? base + (kWLoads * wave + i) * 1024
                                 : base + kWBytes + (kHLoads * wave + (i - kWLoads)) * 1024;
-      dma16(src[i] + kt * BK, dst);
+      // W is read once per vocab tile at one row tile (and by the few row
+      // tiles of one XCD otherwise): the non-temporal policy keeps it from
+      // pushing the shared hidden rows out of the caches
+      if constexpr (is_w) dma16_stream(src[i] + kt * BK, dst);
+      else dma16(src[i] + kt * BK, dst);
     });
   };
 

@@ -4,8 +4,9 @@
 // its kernels against both these and the vendor figures.
 //
 //   probe_read   1,024 workgroups (four per CU) read the buffer in
-//                contiguous 16 KiB blocks with 16-byte loads, four in flight
-//                per thread; the words are folded into one value that is
+//                contiguous 16 KiB blocks with 16-byte non-temporal loads
+//                (the policy of the kernels' own read-once streams), four in
+//                flight per thread; the words are folded into one value that is
 //                stored only if it equals a fixed key, so the loads cannot be
 //                dropped and (in practice) nothing is written.
 //   probe_mfma   every wave runs `iters` rounds of 8 independent
@@ -24,10 +25,10 @@ __global__ __launch_bounds__(256) void probe_read(const u32x4* src, size_t n16, 
   const size_t stride = static_cast<size_t>(gridDim.x) * 1024;
   uint32_t acc = 0;
   for (size_t i = static_cast<size_t>(blockIdx.x) * 1024 + threadIdx.x; i < n16; i += stride) {
-    const u32x4 a = src[i];
-    const u32x4 b = i + 256 < n16 ? src[i + 256] : a;
-    const u32x4 c = i + 512 < n16 ? src[i + 512] : a;
-    const u32x4 d = i + 768 < n16 ? src[i + 768] : a;
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    const u32x4 b = i + 256 < n16 ? __builtin_nontemporal_load(src + i + 256) : a;
+    const u32x4 c = i + 512 < n16 ? __builtin_nontemporal_load(src + i + 512) : a;
+    const u32x4 d = i + 768 < n16 ? __builtin_nontemporal_load(src + i + 768) : a;
     acc ^= a[0] ^ a[1] ^ a[2] ^ a[3] ^ b[0] ^ b[1] ^ b[2] ^ b[3];
     acc ^= c[0] ^ c[1] ^ c[2] ^ c[3] ^ d[0] ^ d[1] ^ d[2] ^ d[3];
   }

@@ -190,6 +190,19 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
       : "memory", "m0");
 }
 
+// The same load with the non-temporal cache policy, for data a call reads
+// once and never again (the paged KV stream): its lines are the first the
+// caches give up, so the stream does not push out data that is reused.
+__device__ __forceinline__ void dma16_stream(const void* src, uint32_t lds) {
+  lds = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off nt"
+      ::"v"(src), "s"(lds)
+      : "memory", "m0");
+}
+
 // LDS byte address of a pointer into a __shared__ array (wave-uniform).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane(

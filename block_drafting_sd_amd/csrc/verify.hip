@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void verify_rowstats(VerifyArgs a) {
   for (int j = 0; j < kGroups; ++j) {
     const int v = lo + 4 * (threadIdx.x + kThreads * j);
     if (vec_ok && v + 3 < len) {
-      x[j] = *reinterpret_cast<const f32x4*>(src + v);
+      x[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + v));   // read once
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[j][e] = v + e < len ? src[v + e] : -INFINITY;
