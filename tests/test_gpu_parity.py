@@ -72,6 +72,24 @@ def test_attention_many_requests():
     assert rep["ok"] and rep["rel_l2"] < 1e-2
 
 
+@pytest.mark.parametrize("batch,split", [(7, 0), (64, 64), (65, 64), (64, 0)])
+def test_attention_launch_shapes(batch, split):
+    """The call's launch shapes at their boundaries: every request within one
+    split (7 or 64 requests, automatic split: one item per request and KV
+    head, no work list, no merge), 64 requests with several splits each (the
+    split-K workgroups scan the requests themselves) and 65 (the work-list
+    kernel).  Ragged prefixes with empty ones and K_b = 0 rows."""
+    ctx = tuple((0, 17, 300, 64, 1, 250, 128)[i % 7] for i in range(batch))
+    kb = tuple((4, 1, 0, 16, 3)[i % 5] for i in range(batch))
+    inp = StepInputs(_edge_cfg(batch=batch, ctx=("list", ctx), draft_k=("list", kb),
+                               num_heads_q=8, num_heads_kv=2, head_dim=64,
+                               seed=9000 + batch + split))
+    log(f"attention launch shape B={batch} split={split}")
+    rep = compare.attention_report(gpu_attention(inp, split_tokens=split), oracle_attention(inp))
+    log(str(rep))
+    assert rep["ok"] and rep["rel_l2"] < 1e-2
+
+
 def test_attention_tiny_workload():
     inp = StepInputs(C0_TINY)
     rep = compare.attention_report(gpu_attention(inp), oracle_attention(inp))
