@@ -21,11 +21,22 @@
 //   through one L2 and one set of address translations.  With a shuffled
 //   page table this is worth a few per cent of HBM bandwidth.
 //
+// Launch shapes: when the host can see that every request is at most one item
+// per kv head (its streamable span fits one split, no summary), the item of
+// workgroup slot u is request u itself and only the split-K kernel runs (no
+// work list, no partials, no merge).  Otherwise the items are located through
+// prefix sums over the requests: computed in LDS by every split-K workgroup
+// for up to kAttnLocalScan requests, by the `attn_worklist` kernel above that.
+//
 // Prefix items stream the cache through a ring of NS LDS stages of 32 keys
 // (two 16-token pages, 128*D bytes) filled by gfx950 direct-to-LDS loads
 // (global_load_lds_dwordx4): a load writes 16 bytes per lane straight into
 // LDS without passing through registers, so NS-1 stages (NS-1 x 16 KiB at
 // D = 128) are in flight per workgroup while the current one is computed.
+// The KV loads use the non-temporal cache policy: a call reads every KV line
+// exactly once, and streaming gigabytes through the caches with the default
+// policy displaces what is reused (measured: 75% -> 85% of the HBM peak at
+// 128K context, batch 16).
 // Wave 0 fetches the stage's keys, wave 1 its values; each 1 KiB wave load is
 // laid out so that lane l of the consuming wave reads its MFMA operand at
 // byte 16 l of a 1 KiB chunk (conflict-free ds_read_b128).  The waits are
@@ -38,8 +49,9 @@
 //   O^T[D x 32 queries]     += V^T * P^T     (MFMA 32x32x16 bf16, 2 per 32 dims)
 // The key order inside a tile is permuted so that the softmax values a lane
 // holds after the first product are exactly the B operand of the second one
-// (no LDS round trip).  Both waves compute from the same stage: wave w owns
-// query rows 32w .. 32w+31 of the item's (up to) 64 rows.
+// (no LDS round trip).  All waves compute from the same stage: wave w owns
+// query rows 32w .. 32w+31 of the item's rows (two waves for up to 64 rows,
+// four for up to 128: large GQA groups).
 #include "sd_common.h"
 #include "sd_internal.h"
 

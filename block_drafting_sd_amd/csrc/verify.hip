@@ -10,12 +10,14 @@
 //   1. verify_rowstats  grid (rows x 8192-entry chunks): per chunk (max, sum
 //      exp) of every target row (and of every draft row when no draft lse is
 //      given).  Each thread issues its eight 16-byte loads at once, so the
-//      logits stream through in one pass: HBM-bound.
+//      logits stream through in one pass: HBM-bound.  The loads are
+//      non-temporal (each logit is read once here).
 //   2. verify_decide    one workgroup per request: merges the row statistics
 //      it needs, evaluates the request's ratio tests in parallel (256
-//      positions per pass) and takes the first rejection.  Only for batches of kDecideBatch requests
-//      or more: below that every sampling workgroup takes the decision itself
-//      and the launch is saved.
+//      positions per pass, one thread each, in two rounds of loads) and takes
+//      the first rejection from wave ballots.  Only for batches of
+//      kDecideBatch requests or more: below that every sampling workgroup
+//      takes the decision itself and the launch is saved.
 //   3. verify_sample    grid (requests x 2048-entry chunks): every workgroup
 //      of a request reads the decision and draws Gumbel-max candidates of its
 //      vocab chunk from the residual [p_j - q_j]_+ (and from p_j as the
