@@ -127,8 +127,13 @@ __device__ __forceinline__ void unit_counts(const AttnArgs& a, const ReqInfo& r,
 // of each kind of unit (unit_off[c (batch + 1) + b], the execution order) and
 // of the work items (item_off[b], the partials' slots), with the totals at
 // index batch.  T requests per round: a shuffle scan inside each wave, then
-// the sums of the preceding waves.  Every thread of the workgroup calls it.
-template <int T>
+// the sums of the preceding waves.  Then the order of the shorter last
+// splits, which run last: unit_off[3 (batch + 1) + r] is the request whose
+// last split has rank r, longest first (ties by request), so that the final
+// round of workgroups ends evenly (up to MaxSort requests, ranked by
+// counting; above that in request order).  Every thread of the workgroup
+// calls it.
+template <int T, int MaxSort>
 __device__ void scan_units(const AttnArgs& a, int* unit_off, int* item_off) {
   constexpr int NW = T / 64;
   __shared__ int wsum[3][NW];
@@ -176,12 +181,38 @@ __device__ void scan_units(const AttnArgs& a, int* unit_off, int* item_off) {
     item_off[a.batch] = a.hkv * (carry[0] + carry[1] + carry[2]);
   }
   __syncthreads();
+  int* perm = unit_off + 3 * (a.batch + 1);
+  const int* po = unit_off + 2 * (a.batch + 1);
+  if (a.batch <= MaxSort) {
+    __shared__ int s_len[MaxSort];   // length of b's shorter last split, or -1
+    for (int b = tid; b < a.batch; b += T) {
+      const ReqInfo r = request_info(a, b);
+      int v[3];
+      unit_counts(a, r, v);
+      s_len[b] = v[2] ? (r.n - r.a0) - (r.ns - 1) * a.split_tokens : -1;
+    }
+    __syncthreads();
+    for (int b = tid; b < a.batch; b += T) {
+      const int lb = s_len[b];
+      if (lb < 0) continue;
+      int rank = 0;
+      for (int c = 0; c < a.batch; ++c) {
+        const int lc = s_len[c];
+        rank += lc > lb || (lc == lb && c < b);
+      }
+      perm[rank] = b;
+    }
+  } else {
+    for (int b = tid; b < a.batch; b += T)
+      if (po[b + 1] > po[b]) perm[po[b]] = b;
+  }
+  __syncthreads();
 }
 
 // The work list in global memory, for batches too large for the split-K
 // workgroups to scan themselves.
 __global__ __launch_bounds__(1024) void attn_worklist(AttnArgs a) {
-  scan_units<1024>(a, a.unit_off, a.item_off);
+  scan_units<1024, kAttnSortMax>(a, a.unit_off, a.item_off);
 }
 
 // Work item of a workgroup.  A unit is one (request, split) -- a prefix split,
@@ -232,13 +263,19 @@ __device__ __forceinline__ bool locate_item(const AttnArgs& a, int block, const 
   const int kind = u < ne ? 0 : (u < ne + nf ? 1 : 2);
   const int* off = kind == 0 ? eo : (kind == 1 ? fo : po);
   const int uu = u - (kind == 0 ? 0 : (kind == 1 ? ne : ne + nf));
-  // request owning the unit: largest b with off[b] <= uu (it has a unit of
-  // this kind, since off[b + 1] > uu)
-  int lo = 0, hi = a.batch;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (off[mid] <= uu) lo = mid;
-    else hi = mid;
+  // request owning the unit: for block and full-length units the largest b
+  // with off[b] <= uu (it has a unit of this kind, since off[b + 1] > uu);
+  // the shorter last splits run in the order scan_units chose
+  int lo = 0;
+  if (kind == 2) {
+    lo = clampi(unit_off[3 * (a.batch + 1) + uu], 0, a.batch - 1);
+  } else {
+    int hi = a.batch;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (off[mid] <= uu) lo = mid;
+      else hi = mid;
+    }
   }
   L.b = lo;
   L.r = request_info(a, lo);
@@ -556,11 +593,11 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   if (!a.direct && a.batch <= kAttnLocalScan) {
     // the workgroup scans the requests itself (no work-list launch);
     // workgroup 0 also stores the offsets for attn_combine
-    __shared__ int s_unit_off[3 * (kAttnLocalScan + 1)];
+    __shared__ int s_unit_off[4 * (kAttnLocalScan + 1)];
     __shared__ int s_item_off[kAttnLocalScan + 1];
-    scan_units<64 * W>(a, s_unit_off, s_item_off);
+    scan_units<64 * W, kAttnLocalScan>(a, s_unit_off, s_item_off);
     if (blockIdx.x == 0) {
-      for (int i = threadIdx.x; i < 3 * (a.batch + 1); i += 64 * W) a.unit_off[i] = s_unit_off[i];
+      for (int i = threadIdx.x; i < 4 * (a.batch + 1); i += 64 * W) a.unit_off[i] = s_unit_off[i];
       for (int i = threadIdx.x; i <= a.batch; i += 64 * W) a.item_off[i] = s_item_off[i];
     }
     if (!locate_item(a, blockIdx.x, s_unit_off, s_item_off, L)) return;

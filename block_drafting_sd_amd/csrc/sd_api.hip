@@ -49,7 +49,7 @@ AttnLayout attn_layout(int32_t batch, int32_t group, int32_t hkv, int32_t head_d
   L.max_items = sd::attn_max_items(batch, hkv, max_total_ctx, L.split);
   L.off_item_off = 0;
   L.off_unit_off = align_up(static_cast<size_t>(batch + 1) * sizeof(int32_t));
-  L.off_lse = L.off_unit_off + align_up(3 * static_cast<size_t>(batch + 1) * sizeof(int32_t));
+  L.off_lse = L.off_unit_off + align_up(4 * static_cast<size_t>(batch + 1) * sizeof(int32_t));
   L.off_o = L.off_lse + align_up(static_cast<size_t>(L.max_items) * L.rows * sizeof(float));
   L.total = L.off_o + align_up(static_cast<size_t>(L.max_items) * L.rows * head_dim * sizeof(float));
   return L;

@@ -43,7 +43,8 @@ struct AttnArgs {
   float scale_log2;       // softmax_scale * log2(e)
   int32_t* item_off;      // [batch + 1] first work item of each request
   int32_t* unit_off;      // [3][batch + 1] first unit of each request among the block
-                          // (+ summary) units, the full-length and the last prefix splits
+                          // (+ summary) units, the full-length and the last prefix splits;
+                          // then [batch + 1]: the requests of the last splits in run order
   float* part_lse;        // [max_items][rows]       (log2 units)
   float* part_o;          // [max_items][D/4][rows][4]
 };
@@ -59,6 +60,7 @@ constexpr int kAttnMaxSplitPages = 2048;   // split_tokens <= 2048 * 16
 constexpr int kAttnMaxSummary = 64;  // summary entries per KV head
 constexpr int kAttnLocalScan = 64;   // batches up to this size: each split-K workgroup
                                      // scans the requests itself (no work-list launch)
+constexpr int kAttnSortMax = 1024;   // batches up to this size: last splits run longest first
 
 int64_t attn_max_items(int32_t batch, int32_t hkv, int64_t max_total_ctx,
                        int32_t split_tokens);
