@@ -10,7 +10,7 @@ Test infrastructure (see ``oracle/__init__``): never imported by the product.
   independently, so the block proposal factorises as the product of the
   ``q_j`` ("LongSpark", sec. 2.1, eq. (4); "DeLS-Spec": one forward pass
   followed by one sampling step).
-* Sampling: the pages only say "sample".  This build draws each token as the
+* Sampling: the pages only say "sample".  Each token is drawn here as the
   Gumbel-max ``argmax_v (z_v - log(-log u_v))`` with one Philox uniform per
   vocab entry (stream 0, position j = row - q_off[b] + 1); the smallest index
   wins a tie.  Gumbel-max yields an exact sample of ``softmax(z)``.

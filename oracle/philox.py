@@ -10,7 +10,7 @@ and the round key; the key is advanced by the two Weyl constants between
 rounds.
 
 The pages say only that draft and correction tokens are *sampled*
-("LongSpark", sec. 2.1, eqs. (1)-(2) and (4)).  This build fixes which
+("LongSpark", sec. 2.1, eqs. (1)-(2) and (4)).  Here the draws fix which
 uniform each decision consumes so that two independent implementations make
 the same draws:
 
