@@ -10,9 +10,9 @@ and the round key; the key is advanced by the two Weyl constants between
 rounds.
 
 The pages say only that draft and correction tokens are *sampled*
-("LongSpark", sec. 2.1, eqs. (1)-(2) and (4)).  Here the draws fix which
-uniform each decision consumes so that two independent implementations make
-the same draws:
+("LongSpark", sec. 2.1, eqs. (1)-(2) and (4)).  The convention below fixes
+which uniform each decision consumes, so that two independent
+implementations make the same draws:
 
 * key      = (seed mod 2^32, seed >> 32)
 * counter  = (v >> 2, j, req_id, stream); output word ``v & 3`` serves vocab
