@@ -248,7 +248,9 @@ __device__ __forceinline__ bool locate_item(const AttnArgs& a, int block, const 
     L.r = request_info(a, u);
     L.sp = 0;
     L.item = -1;
-    return L.r.kb > 0;
+    // (per is 1 whenever the host chose this shape; the test keeps an item
+    // from ever writing a partial slot that does not exist)
+    return L.r.kb > 0 && L.r.per == 1;
   }
   // Work items beyond the partials' capacity (the prefix lengths add up to
   // more than the host bound) make the whole call invalid: nothing is
