@@ -141,7 +141,12 @@ const char* sd_version(void);
  *                  split-K partials in the workspace).  If the lengths on the
  *                  device add up to more and their work items do not fit the
  *                  partials, nothing is computed and every output row of the
- *                  call is set to NaN (never left stale)
+ *                  call is set to NaN (never left stale).  When every
+ *                  request's streamable span (max_pages * 16 tokens, or the
+ *                  window plus one page) fits one split and n_summary = 0,
+ *                  each (request, KV head) is one work item that writes its
+ *                  rows directly: no partials are used and the bound plays
+ *                  no part
  *   split_tokens   prefix tokens per split-K work item; 0 lets the library
  *                  choose (a power of two in [2048, 32768] from batch,
  *                  num_heads_kv and max_total_ctx); otherwise a multiple of
