@@ -66,7 +66,6 @@ struct LmShape {
   static constexpr int Loads = WLoads + HLoads;
   static_assert(WLoads * 1024 * Waves == WBytes && HLoads * 1024 * Waves == HBytes,
                 "a stage is a whole number of wave loads per wave");
-  static_assert(BM == kLmBM, "256-row tiles");
   // 16-byte chunk c of row r of a staged tile sits at byte
   // RowBytes r + 16 (c ^ swz(r)).  A 256-byte span of LDS covers all 64
   // banks; the rows sharing one span (256 / RowBytes of them) keep their
@@ -76,8 +75,11 @@ struct LmShape {
 };
 using TallShape = LmShape<5, 2, 2, 4, 64, 2>;     // 320 x 256: 8 waves of 160 x 64
 using NarrowShape = LmShape<2, 4, 2, 2, 32, 3>;   // 128 x 256: 4 waves of 64 x 128
+using SmallShape = LmShape<2, 2, 2, 2, 64, 2>;    // 128 x 128: 4 waves of 64 x 64
 static_assert(kLmHMultiple % 64 == 0, "H is a whole number of stages of either shape");
-static_assert(NarrowShape::BV == kLmBV, "the workspace is sized for the 128-vocab tiles");
+static_assert(NarrowShape::BV == kLmBV && SmallShape::BV == kLmBV,
+              "the workspace is sized for the 128-vocab tiles");
+static_assert(SmallShape::NS * SmallShape::StageBytes == 64 * 1024, "two small workgroups per CU");
 static_assert(TallShape::NS * TallShape::StageBytes == 144 * 1024 &&
               NarrowShape::NS * NarrowShape::StageBytes == 72 * 1024,
               "one tall or two narrow workgroups per CU");
@@ -113,7 +115,7 @@ void lm_gemm(LmArgs a) {
   const int vt = (slot / a.n_mt) * 8 + xcd;
   const int mt = slot % a.n_mt;
   if (vt >= a.n_vt) return;
-  const int v0 = vt * T::BV, m0 = mt * kLmBM;
+  const int v0 = vt * T::BV, m0 = mt * T::BM;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wv = wave % WV, wm = wave / WV, h = lane >> 5;
 
@@ -214,7 +216,7 @@ void lm_gemm(LmArgs a) {
   __syncthreads();
   float4* red = reinterpret_cast<float4*>(smem);   // [wv][wm][tm][32]
   const bool vec_ok = (a.V & 3) == 0;
-  const bool full = !a.greedy && vec_ok && v0 + T::BV <= a.V && m0 + kLmBM <= a.M;
+  const bool full = !a.greedy && vec_ok && v0 + T::BV <= a.V && m0 + T::BM <= a.M;
   static_for<0, TM>([&](auto TMi) {
     const int m = m0 + 32 * TM * wm + 32 * TMi + rr;
     const bool mok = m < a.M;
@@ -357,16 +359,24 @@ __global__ __launch_bounds__(kThreads) void lm_row_reduce(LmArgs a) {
 template <typename T>
 hipError_t launch_gemm(LmArgs& b, hipStream_t s) {
   b.n_vt = (b.V + T::BV - 1) / T::BV;
+  b.n_mt = (b.M + T::BM - 1) / T::BM;
   const int slots = (b.n_vt + 7) / 8 * b.n_mt;
   return launch_kernel(lm_gemm<T>, dim3(slots * 8), dim3(T::Threads), s, b);
 }
 
 hipError_t launch_lm_head(const LmArgs& a, hipStream_t s) {
   // the tall tiles when they give every CU at least one tile, else the
-  // narrow ones (two workgroups per CU, 2.5x as many tiles)
+  // narrow ones (two workgroups per CU, 2.5x as many tiles); when even those
+  // leave CUs' second slots empty (a pruned vocabulary at 256 rows), the
+  // 128-row small tiles, twice as many again
   LmArgs b = a;
-  const int64_t tall_tiles = static_cast<int64_t>((a.V + TallShape::BV - 1) / TallShape::BV) * a.n_mt;
-  hipError_t e = tall_tiles >= 256 ? launch_gemm<TallShape>(b, s) : launch_gemm<NarrowShape>(b, s);
+  const int64_t mt = (a.M + kLmBM - 1) / kLmBM;
+  const int64_t tall_tiles = static_cast<int64_t>((a.V + TallShape::BV - 1) / TallShape::BV) * mt;
+  const int64_t narrow_tiles = static_cast<int64_t>((a.V + NarrowShape::BV - 1) / NarrowShape::BV) * mt;
+  hipError_t e;
+  if (tall_tiles >= 256) e = launch_gemm<TallShape>(b, s);
+  else if (narrow_tiles < 512 && a.M > SmallShape::BM) e = launch_gemm<SmallShape>(b, s);
+  else e = launch_gemm<NarrowShape>(b, s);
   if (e == hipSuccess) e = launch_kernel(lm_row_reduce, dim3(b.M), dim3(kThreads), s, b);
   return e;
 }
