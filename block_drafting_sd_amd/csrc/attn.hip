@@ -288,7 +288,7 @@ __device__ __forceinline__ bool locate_item(const AttnArgs& a, int block, const 
 
 // Workgroups covering every item under locate_item's mapping.
 inline int attn_grid(const AttnArgs& a) {
-  const int units = a.max_items / a.hkv;
+  const int units = a.max_units;
   return (units + 7) / 8 * 8 * a.hkv;
 }
 

@@ -151,7 +151,6 @@ sd_status draft_attn_impl(const void* q, const void* k_blk, const void* v_blk, c
   a.sum_k = n_summary > 0 ? static_cast<const uint16_t*>(summary_keys) : nullptr;
   a.sum_v = n_summary > 0 ? summary_values : nullptr;
   a.n_summary = n_summary;
-  a.split_tokens = L.split;
   a.max_items = static_cast<int32_t>(L.max_items);
   a.rows = L.rows;
   {
@@ -159,7 +158,31 @@ sd_status draft_attn_impl(const void* q, const void* k_blk, const void* v_blk, c
     // or with a window its last W tokens from the page start below them
     const int64_t span = window > 0 ? std::min<int64_t>(int64_t(window) + 15, int64_t(max_pages) * 16)
                                     : int64_t(max_pages) * 16;
-    a.direct = span <= L.split && n_summary == 0 ? 1 : 0;
+    // The automatic split is sized from the whole prefixes, which is what
+    // the workspace size sees.  A window much shorter than them would leave
+    // one item per (request, KV head) and most CUs idle, so the window is
+    // cut into k pieces of at least 512 tokens, enough for two items per CU
+    // slot (512 in all), when their items still fit the workspace.
+    a.split_tokens = L.split;
+    if (split_tokens == 0 && window > 0) {
+      const int64_t pairs = static_cast<int64_t>(batch) * num_heads_kv;
+      const int64_t k = std::min<int64_t>((512 + pairs - 1) / pairs, span / 512);
+      if (k >= 2) {
+        const int64_t s_w = ((span + k - 1) / k + 63) / 64 * 64;
+        const int64_t items = pairs * ((span + s_w - 1) / s_w + (n_summary > 0 ? 1 : 0));
+        if (s_w < L.split && items <= L.max_items) a.split_tokens = static_cast<int32_t>(s_w);
+      }
+    }
+    const int64_t split = a.split_tokens;
+    a.direct = span <= split && n_summary == 0 ? 1 : 0;
+    // Work units per request: its prefix splits (at least one unit, the
+    // block alone, for an empty prefix) and the summary unit.  The launch
+    // covers the smaller of this bound and the workspace's, so that a short
+    // window over long prefixes does not launch workgroups for work that
+    // cannot exist.
+    const int64_t per_req = std::max<int64_t>((span + split - 1) / split, 1) + (n_summary > 0 ? 1 : 0);
+    a.max_units = static_cast<int32_t>(
+        std::min<int64_t>(L.max_items / num_heads_kv, static_cast<int64_t>(batch) * per_req));
   }
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.item_off = reinterpret_cast<int32_t*>(ws + L.off_item_off);

@@ -36,6 +36,7 @@ struct AttnArgs {
   int32_t n_summary;      // 0 when there is no summary
   int32_t split_tokens;   // prefix tokens per work item (multiple of 64, <= 32768)
   int32_t max_items;      // work items the partial buffers hold
+  int32_t max_units;      // bound on the work units (request, split) of the call
   int32_t rows;           // query rows per work item: 64 (two waves) or 128 (four)
   int32_t direct;         // 1: every request is at most one work item (its prefix span fits
                           // one split and there is no summary), so the item of a request

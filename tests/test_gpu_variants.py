@@ -106,6 +106,20 @@ def test_recent_window(window):
     _check(got, _oracle_attn(inp, window=window), tag=f"window {window}")
 
 
+@pytest.mark.parametrize("window,causal", [(2048, True), (1500, False), (4096, True)])
+def test_window_automatic_split(window, causal):
+    """A long window under the automatic split: with few (request, KV head)
+    pairs the window is cut into several items of at least 512 tokens
+    (prefixes longer and shorter than the window, an empty one, ragged K_b)."""
+    inp = StepInputs(_cfg(batch=6, ctx=("list", (20000, 0, 1500, 9000, 4099, 70)),
+                          draft_k=("list", (16, 3, 16, 1, 8, 5)), num_heads_q=32,
+                          num_heads_kv=8, seed=6000 + window))
+    mask = sd.SD_MASK_CAUSAL if causal else sd.SD_MASK_NONE
+    got = _gpu_attn(inp, window=window, block_mask=mask)
+    ref = _oracle_attn(inp, window=window, block_mask="causal" if causal else "none")
+    _check(got, ref, tag=f"window {window} automatic split causal={causal}")
+
+
 @pytest.mark.parametrize("n_summary", [16, 40])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fixed_cost_context(n_summary, causal):
