@@ -3,7 +3,7 @@
 // and App. A.1, Fig. 6: the frozen target vocabulary head produces every
 // slot's base logits in parallel and each slot is sampled independently).
 //
-// lm_gemm<Shape>: one workgroup computes a BV-vocab x 256-row tile of
+// lm_gemm<Shape>: one workgroup computes a BV-vocab x BM-row tile of
 // logits^T = W * hidden^T with MFMA 32x32x16 bf16 (fp32 accumulation); each
 // wave owns a (32 TV) x (32 TM) sub-tile.  Both operands are H-contiguous.
 // They stream through a ring of LDS stages of BK hidden dims (W rows, then
@@ -11,7 +11,7 @@
 // load covers whole BK-dim row segments (16 rows x 64 bytes at BK = 32, 8
 // rows x 128 bytes at BK = 64), so global reads stay coalesced, and rows are
 // stored with a 16-byte-chunk XOR swizzle so the MFMA operand reads (32 rows,
-// one chunk) are conflict-free.  Two shapes:
+// one chunk) are conflict-free.  Three shapes:
 //   Tall   (320 x 256, 8 waves of 160 x 64, 64-dim stages, 2 x 72 KiB ring,
 //           one workgroup per CU): the fewest operand bytes per output that
 //           the registers allow (160 accumulators per lane), and at a
@@ -21,11 +21,17 @@
 //           two workgroups per CU): more, smaller tiles for launches too
 //           small to fill the CUs with the tall tiles (e.g. a 32,000-entry
 //           pruned vocabulary at 256 rows: 250 tiles against 100).
+//   Small  (128 x 128, 4 waves of 64 x 64, 64-dim stages, 2 x 32 KiB ring):
+//           twice as many tiles again, for launches whose narrow tiles
+//           would still leave the CUs' second slots empty.
 // The per-CU rate at which the operand loads arrive, not the MFMAs (the
 // LDS-to-MFMA loop alone runs at the MFMA ceiling), bounds this kernel, so
 // the tile shape that moves the fewest bytes per output wins: measured at
 // 151,936 x 4096, 0.48 -> 0.39 ms at 256 rows and 1.45 -> 1.38 ms at 1,024
-// rows against 256 x 256 tiles of 64 x 128 per wave.
+// rows against 256 x 256 tiles of 64 x 128 per wave.  The tall and narrow
+// shapes deal each wave's refill loads over the stage's k-steps instead of
+// issuing them in one burst (about 3% faster for both; the small shape,
+// with two loads per k-step, is faster with the burst).
 // Tiles are ordered so that all row tiles of one vocab tile, and a compact
 // block of vocab tiles, run together on one XCD (blockIdx % 8 picks the XCD),
 // which keeps every W and hidden slice in that XCD's L2 across row tiles.
@@ -47,9 +53,10 @@ constexpr int kThreads = 256;                       // lm_row_reduce: 4 waves
 
 // Tile shape: TV x TM MFMA tiles (32 x 32) per wave, WVN x WMN waves (vocab x
 // rows), BK hidden dims per stage, NS stages in the LDS ring.
-template <int TV_, int TM_, int WVN_, int WMN_, int BK_, int NS_>
+template <int TV_, int TM_, int WVN_, int WMN_, int BK_, int NS_, bool Spread_>
 struct LmShape {
   static constexpr int TV = TV_, TM = TM_, WVN = WVN_, WMN = WMN_, BK = BK_, NS = NS_;
+  static constexpr bool Spread = Spread_;   // stage refill dealt over the k-steps
   static constexpr int Waves = WVN * WMN;
   static constexpr int Threads = 64 * Waves;
   static constexpr int BV = 32 * TV * WVN;                // vocab rows per tile
@@ -73,9 +80,9 @@ struct LmShape {
   // of one chunk fall in 16 different 16-byte bank groups.
   static __device__ __forceinline__ int swz(int r) { return (r / (256 / RowBytes)) & (Chunks - 1); }
 };
-using TallShape = LmShape<5, 2, 2, 4, 64, 2>;     // 320 x 256: 8 waves of 160 x 64
-using NarrowShape = LmShape<2, 4, 2, 2, 32, 3>;   // 128 x 256: 4 waves of 64 x 128
-using SmallShape = LmShape<2, 2, 2, 2, 64, 2>;    // 128 x 128: 4 waves of 64 x 64
+using TallShape = LmShape<5, 2, 2, 4, 64, 2, true>;     // 320 x 256: 8 waves of 160 x 64
+using NarrowShape = LmShape<2, 4, 2, 2, 32, 3, true>;   // 128 x 256: 4 waves of 64 x 128
+using SmallShape = LmShape<2, 2, 2, 2, 64, 2, false>;   // 128 x 128: 4 waves of 64 x 64
 static_assert(kLmHMultiple % 64 == 0, "H is a whole number of stages of either shape");
 static_assert(NarrowShape::BV == kLmBV && SmallShape::BV == kLmBV,
               "the workspace is sized for the 128-vocab tiles");
@@ -138,9 +145,12 @@ void lm_gemm(LmArgs a) {
                   : a.hidden + static_cast<size_t>(min(m0 + r, a.M - 1)) * a.H + 8 * c;
   }
   const uint32_t lds_ring = lds_addr(smem);
-  auto issue = [&](int kt) {
+  // Loads of stage kt; with part >= 0 only the share of k-step `part` (the
+  // wave's loads dealt evenly over the stage's k-steps).
+  auto issue = [&](int kt, int part) {
     const uint32_t base = lds_ring + (kt % kNS) * kStageBytes;
     static_for<0, kLoadsPerWave>([&](auto i) {
+      if (part >= 0 && i * T::KSteps / kLoadsPerWave != part) return;
       constexpr bool is_w = i < kWLoads;
       const uint32_t dst = is_w ? base + (kWLoads * wave + i) * 1024
                                 : base + kWBytes + (kHLoads * wave + (i - kWLoads)) * 1024;
@@ -173,16 +183,20 @@ void lm_gemm(LmArgs a) {
   const int nk = a.H / BK;
 #pragma unroll
   for (int t = 0; t < kNS - 1; ++t)
-    if (t < nk) issue(t);
+    if (t < nk) issue(t, -1);
   for (int kt = 0; kt < nk; ++kt) {
     // stage kt has landed; issued so far: stages up to kt + kNS - 2
     wait_stage<kLoadsPerWave, kNS - 2>(nk - 1 - kt);
     stage_barrier();
-    // refill the stage every wave finished reading last iteration
-    if (kt + kNS - 1 < nk) issue(kt + kNS - 1);
+    // refill the stage every wave finished reading last iteration: in one
+    // burst, or (Spread) a share before each k-step's operand reads, so that
+    // no wave holds its MFMAs back behind a queue of load issues
+    const bool refill = kt + kNS - 1 < nk;
+    if (!T::Spread && refill) issue(kt + kNS - 1, -1);
     const char* st = smem + (kt % kNS) * kStageBytes;
 #pragma unroll
     for (int s = 0; s < T::KSteps; ++s) {
+      if (T::Spread && refill) issue(kt + kNS - 1, s);
       bf16x8 af[TV], bfr[TM];
 #pragma unroll
       for (int t = 0; t < TV; ++t)
