@@ -11,7 +11,7 @@
 // load covers whole BK-dim row segments (16 rows x 64 bytes at BK = 32, 8
 // rows x 128 bytes at BK = 64), so global reads stay coalesced, and rows are
 // stored with a 16-byte-chunk XOR swizzle so the MFMA operand reads (32 rows,
-// one chunk) are conflict-free.  Three shapes:
+// one chunk) are conflict-free.  Four shapes:
 //   Tall   (320 x 256, 8 waves of 160 x 64, 64-dim stages, 2 x 72 KiB ring,
 //           one workgroup per CU): the fewest operand bytes per output that
 //           the registers allow (160 accumulators per lane), and at a
@@ -24,6 +24,11 @@
 //   Small  (128 x 128, 4 waves of 64 x 64, 64-dim stages, 2 x 32 KiB ring):
 //           twice as many tiles again, for launches whose narrow tiles
 //           would still leave the CUs' second slots empty.
+//   Short  (320 x 64, 4 waves of 160 x 32, 64-dim stages, 3 x 48 KiB ring,
+//           one workgroup per CU): up to 64 draft rows (small decode
+//           batches), where the W stream is the whole cost and the tall
+//           tile's 256 rows would be mostly padding; two W stages in flight
+//           per CU.  0.31-0.34 -> 0.24 ms at 16-64 rows x 151,936 x 4096.
 // The per-CU rate at which the operand loads arrive, not the MFMAs (the
 // LDS-to-MFMA loop alone runs at the MFMA ceiling), bounds this kernel, so
 // the tile shape that moves the fewest bytes per output wins: measured at
@@ -50,6 +55,7 @@ namespace sd {
 namespace {
 
 constexpr int kThreads = 256;                       // lm_row_reduce: 4 waves
+constexpr int kShortMaxRows = 64;                   // draft rows up to which the short tiles serve
 
 // Tile shape: TV x TM MFMA tiles (32 x 32) per wave, WVN x WMN waves (vocab x
 // rows), BK hidden dims per stage, NS stages in the LDS ring.
@@ -83,10 +89,12 @@ struct LmShape {
 using TallShape = LmShape<5, 2, 2, 4, 64, 2, true>;     // 320 x 256: 8 waves of 160 x 64
 using NarrowShape = LmShape<2, 4, 2, 2, 32, 3, true>;   // 128 x 256: 4 waves of 64 x 128
 using SmallShape = LmShape<2, 2, 2, 2, 64, 2, false>;   // 128 x 128: 4 waves of 64 x 64
+using ShortShape = LmShape<5, 1, 2, 2, 64, 3, true>;    // 320 x 64: 4 waves of 160 x 32
 static_assert(kLmHMultiple % 64 == 0, "H is a whole number of stages of either shape");
 static_assert(NarrowShape::BV == kLmBV && SmallShape::BV == kLmBV,
               "the workspace is sized for the 128-vocab tiles");
 static_assert(SmallShape::NS * SmallShape::StageBytes == 64 * 1024, "two small workgroups per CU");
+static_assert(ShortShape::NS * ShortShape::StageBytes == 144 * 1024, "one short workgroup per CU");
 static_assert(TallShape::NS * TallShape::StageBytes == 144 * 1024 &&
               NarrowShape::NS * NarrowShape::StageBytes == 72 * 1024,
               "one tall or two narrow workgroups per CU");
@@ -379,16 +387,21 @@ hipError_t launch_gemm(LmArgs& b, hipStream_t s) {
 }
 
 hipError_t launch_lm_head(const LmArgs& a, hipStream_t s) {
-  // the tall tiles when they give every CU at least one tile, else the
-  // narrow ones (two workgroups per CU, 2.5x as many tiles); when even those
-  // leave CUs' second slots empty (a pruned vocabulary at 256 rows), the
-  // 128-row small tiles, twice as many again
+  // up to 64 rows, the 64-row short tiles when they give every CU a tile
+  // (the 256-row tall tiles would compute three quarters padding); else the
+  // tall tiles when they give every CU at least one tile, else the narrow
+  // ones (two workgroups per CU, 2.5x as many tiles); when even those leave
+  // CUs' second slots empty (a pruned vocabulary at 256 rows), the 128-row
+  // small tiles, twice as many again
   LmArgs b = a;
   const int64_t mt = (a.M + kLmBM - 1) / kLmBM;
   const int64_t tall_tiles = static_cast<int64_t>((a.V + TallShape::BV - 1) / TallShape::BV) * mt;
   const int64_t narrow_tiles = static_cast<int64_t>((a.V + NarrowShape::BV - 1) / NarrowShape::BV) * mt;
+  const int64_t short_tiles =
+      static_cast<int64_t>((a.V + ShortShape::BV - 1) / ShortShape::BV) * ((a.M + ShortShape::BM - 1) / ShortShape::BM);
   hipError_t e;
-  if (tall_tiles >= 256) e = launch_gemm<TallShape>(b, s);
+  if (a.M <= kShortMaxRows && short_tiles >= 256) e = launch_gemm<ShortShape>(b, s);
+  else if (tall_tiles >= 256) e = launch_gemm<TallShape>(b, s);
   else if (narrow_tiles < 512 && a.M > SmallShape::BM) e = launch_gemm<SmallShape>(b, s);
   else e = launch_gemm<NarrowShape>(b, s);
   if (e == hipSuccess) e = launch_kernel(lm_row_reduce, dim3(b.M), dim3(kThreads), s, b);

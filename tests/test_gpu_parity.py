@@ -121,7 +121,10 @@ def test_attention_mha_and_small_groups():
                                    # 320 x 256 tiles (at least 256 of them):
                                    # ragged vocab and row tails
                                    (600, 64, 40003), (257, 128, 82001),
-                                   (8, 64, 151936), (1024, 64, 20481)])
+                                   (8, 64, 151936), (1024, 64, 20481),
+                                   # 320 x 64 tiles (at most 64 rows, at least 256 tiles):
+                                   # full and ragged row and vocab tails
+                                   (64, 128, 90001), (33, 256, 81921)])
 def test_lm_head_shapes(M, H, V):
     cfg = C0_TINY.with_(name="lm", batch=1, draft_k=M, hidden=H, vocab=V, seed=M * 7 + V)
     inp = StepInputs(cfg)
