@@ -124,7 +124,9 @@ def test_attention_mha_and_small_groups():
                                    (8, 64, 151936), (1024, 64, 20481),
                                    # 320 x 64 tiles (at most 64 rows, at least 256 tiles):
                                    # full and ragged row and vocab tails
-                                   (64, 128, 90001), (33, 256, 81921)])
+                                   (64, 128, 90001), (33, 256, 81921),
+                                   # 320 x 128 tiles (65 to 128 rows, at least 256 tiles)
+                                   (128, 128, 90001), (100, 64, 81921)])
 def test_lm_head_shapes(M, H, V):
     cfg = C0_TINY.with_(name="lm", batch=1, draft_k=M, hidden=H, vocab=V, seed=M * 7 + V)
     inp = StepInputs(cfg)
