@@ -16,7 +16,8 @@
 //           one workgroup per CU): the fewest operand bytes per output that
 //           the registers allow (160 accumulators per lane), and at a
 //           151,936-entry vocabulary 475 vocab tiles, under two rounds over
-//           the 256 CUs.  Used whenever it yields at least one tile per CU.
+//           the 256 CUs.  Used above 128 rows whenever it yields at
+//           least one tile per CU.
 //   Narrow (128 x 256, 4 waves of 64 x 128, 32-dim stages, 3 x 24 KiB ring,
 //           two workgroups per CU): more, smaller tiles for launches too
 //           small to fill the CUs with the tall tiles (e.g. a 32,000-entry
@@ -36,10 +37,11 @@
 // LDS-to-MFMA loop alone runs at the MFMA ceiling), bounds this kernel, so
 // the tile shape that moves the fewest bytes per output wins: measured at
 // 151,936 x 4096, 0.48 -> 0.39 ms at 256 rows and 1.45 -> 1.38 ms at 1,024
-// rows against 256 x 256 tiles of 64 x 128 per wave.  The tall and narrow
-// shapes deal each wave's refill loads over the stage's k-steps instead of
-// issuing them in one burst (about 3% faster for both; the small shape,
-// with two loads per k-step, is faster with the burst).
+// rows against 256 x 256 tiles of 64 x 128 per wave.  All shapes but the
+// small one deal each wave's refill loads over the stage's k-steps instead
+// of issuing them in one burst (about 3% faster for the tall and narrow
+// tiles; the small shape, with two loads per k-step, is faster with the
+// burst).
 // Tiles are ordered so that all row tiles of one vocab tile, and a compact
 // block of vocab tiles, run together on one XCD (blockIdx % 8 picks the XCD),
 // which keeps every W and hidden slice in that XCD's L2 across row tiles.
