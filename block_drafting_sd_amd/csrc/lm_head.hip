@@ -11,7 +11,7 @@
 // load covers whole BK-dim row segments (16 rows x 64 bytes at BK = 32, 8
 // rows x 128 bytes at BK = 64), so global reads stay coalesced, and rows are
 // stored with a 16-byte-chunk XOR swizzle so the MFMA operand reads (32 rows,
-// one chunk) are conflict-free.  Five shapes:
+// one chunk) are conflict-free.  Six shapes:
 //   Tall   (320 x 256, 8 waves of 160 x 64, 64-dim stages, 2 x 72 KiB ring,
 //           one workgroup per CU): the fewest operand bytes per output that
 //           the registers allow (160 accumulators per lane), and at a
@@ -33,6 +33,11 @@
 //   Mid    (320 x 128, 4 waves of 160 x 64, 64-dim stages, 2 x 56 KiB ring,
 //           one workgroup per CU): 65-128 rows on the same grounds,
 //           0.33-0.34 -> 0.29-0.31 ms at that vocabulary.
+//   Slim   (128 x 64, 4 waves of 64 x 32, 64-dim stages, 3 x 24 KiB ring,
+//           two workgroups per CU): up to 64 rows when the short tiles would
+//           not fill the CUs (small or pruned vocabularies); at 32,000 x 4096
+//           0.10 -> 0.065 ms, and the small tiles at 65-128 rows
+//           0.12 -> 0.08 ms.
 // The per-CU rate at which the operand loads arrive, not the MFMAs (the
 // LDS-to-MFMA loop alone runs at the MFMA ceiling), bounds this kernel, so
 // the tile shape that moves the fewest bytes per output wins: measured at
@@ -97,12 +102,14 @@ using NarrowShape = LmShape<2, 4, 2, 2, 32, 3, true>;   // 128 x 256: 4 waves of
 using SmallShape = LmShape<2, 2, 2, 2, 64, 2, false>;   // 128 x 128: 4 waves of 64 x 64
 using ShortShape = LmShape<5, 1, 2, 2, 64, 3, true>;    // 320 x 64: 4 waves of 160 x 32
 using MidShape = LmShape<5, 2, 2, 2, 64, 2, true>;      // 320 x 128: 4 waves of 160 x 64
+using SlimShape = LmShape<2, 1, 2, 2, 64, 3, true>;     // 128 x 64: 4 waves of 64 x 32
 static_assert(kLmHMultiple % 64 == 0, "H is a whole number of stages of either shape");
-static_assert(NarrowShape::BV == kLmBV && SmallShape::BV == kLmBV,
+static_assert(NarrowShape::BV == kLmBV && SmallShape::BV == kLmBV && SlimShape::BV == kLmBV,
               "the workspace is sized for the 128-vocab tiles");
 static_assert(SmallShape::NS * SmallShape::StageBytes == 64 * 1024, "two small workgroups per CU");
 static_assert(ShortShape::NS * ShortShape::StageBytes == 144 * 1024, "one short workgroup per CU");
 static_assert(MidShape::NS * MidShape::StageBytes == 112 * 1024, "one mid workgroup per CU");
+static_assert(SlimShape::NS * SlimShape::StageBytes == 72 * 1024, "two slim workgroups per CU");
 static_assert(TallShape::NS * TallShape::StageBytes == 144 * 1024 &&
               NarrowShape::NS * NarrowShape::StageBytes == 72 * 1024,
               "one tall or two narrow workgroups per CU");
@@ -396,8 +403,9 @@ hipError_t launch_gemm(LmArgs& b, hipStream_t s) {
 
 hipError_t launch_lm_head(const LmArgs& a, hipStream_t s) {
   // up to 64 rows, the 64-row short tiles when they give every CU a tile
-  // (the 256-row tall tiles would compute three quarters padding), up to 128
-  // rows the 128-row mid tiles on the same condition; else the
+  // (the 256-row tall tiles would compute three quarters padding) and the
+  // 128-wide slim ones when they do not; up to 128 rows the 128-row mid
+  // tiles on the same condition, else the 128 x 128 small ones; above, the
   // tall tiles when they give every CU at least one tile, else the narrow
   // ones (two workgroups per CU, 2.5x as many tiles); when even those leave
   // CUs' second slots empty (a pruned vocabulary at 256 rows), the 128-row
@@ -408,13 +416,13 @@ hipError_t launch_lm_head(const LmArgs& a, hipStream_t s) {
   const int64_t narrow_tiles = static_cast<int64_t>((a.V + NarrowShape::BV - 1) / NarrowShape::BV) * mt;
   const int64_t short_tiles =
       static_cast<int64_t>((a.V + ShortShape::BV - 1) / ShortShape::BV) * ((a.M + ShortShape::BM - 1) / ShortShape::BM);
-  hipError_t e;
   const int64_t mid_tiles =
       static_cast<int64_t>((a.V + MidShape::BV - 1) / MidShape::BV) * ((a.M + MidShape::BM - 1) / MidShape::BM);
-  if (a.M <= kShortMaxRows && short_tiles >= 256) e = launch_gemm<ShortShape>(b, s);
-  else if (a.M <= kMidMaxRows && mid_tiles >= 256) e = launch_gemm<MidShape>(b, s);
+  hipError_t e;
+  if (a.M <= kShortMaxRows) e = short_tiles >= 256 ? launch_gemm<ShortShape>(b, s) : launch_gemm<SlimShape>(b, s);
+  else if (a.M <= kMidMaxRows) e = mid_tiles >= 256 ? launch_gemm<MidShape>(b, s) : launch_gemm<SmallShape>(b, s);
   else if (tall_tiles >= 256) e = launch_gemm<TallShape>(b, s);
-  else if (narrow_tiles < 512 && a.M > SmallShape::BM) e = launch_gemm<SmallShape>(b, s);
+  else if (narrow_tiles < 512) e = launch_gemm<SmallShape>(b, s);
   else e = launch_gemm<NarrowShape>(b, s);
   if (e == hipSuccess) e = launch_kernel(lm_row_reduce, dim3(b.M), dim3(kThreads), s, b);
   return e;

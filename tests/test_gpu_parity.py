@@ -126,7 +126,9 @@ def test_attention_mha_and_small_groups():
                                    # full and ragged row and vocab tails
                                    (64, 128, 90001), (33, 256, 81921),
                                    # 320 x 128 tiles (65 to 128 rows, at least 256 tiles)
-                                   (128, 128, 90001), (100, 64, 81921)])
+                                   (128, 128, 90001), (100, 64, 81921),
+                                   # 128 x 128 tiles at 65 to 128 rows of a smaller vocabulary
+                                   (128, 128, 32000), (100, 64, 20001)])
 def test_lm_head_shapes(M, H, V):
     cfg = C0_TINY.with_(name="lm", batch=1, draft_k=M, hidden=H, vocab=V, seed=M * 7 + V)
     inp = StepInputs(cfg)
