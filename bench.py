@@ -387,8 +387,23 @@ def main():
     if args.calibrate_copy > 0:
         copy_calibration(args.calibrate_copy)
 
+    init = None
     if opts.n_summary:
-        step.summary_init(t)       # state before the first step (untimed)
+        # state before the first step (setup, outside the timed steps); a
+        # second, warm call is timed on its own: it reads every prefix row once
+        step.summary_init(t)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step.summary_init(t)
+        e1.record()
+        torch.cuda.synchronize()
+        init_ms = e0.elapsed_time(e1)
+        init_bytes = (int(t["ctx_len_prev"].to(torch.int64).sum().item()) * cfg.num_heads_kv
+                      * cfg.head_dim * 2 * 2)
+        init = {"summary_init_ms": round(init_ms, 4), "prefix_kv_bytes": init_bytes,
+                "read_gbs": round(init_bytes / (init_ms * 1e-3) / 1e9, 1)}
+        log(f"[bench] summary initialisation {init_ms:.3f} ms ({init['read_gbs']} GB/s)")
     for i in range(args.warmup):
         step.run(t, seed + i)
     torch.cuda.synchronize()
@@ -509,6 +524,7 @@ def main():
                     "w_hbm_gbs": round(v_draft * c.hidden * 2 / (float(lm_ms.mean()) * 1e-3) / 1e9, 1),
                     "library_gemm": lib_gemm},
         "measured_peaks": peaks,
+        "setup": init,
         # secondary metric: committed tokens (accepted drafts + the correction
         # or bonus token of every request) per second of the same timed steps
         "emitted_tokens_per_s": round(emitted_total / elapsed, 1),

@@ -21,7 +21,7 @@ __all__ = ["sd_draft_attn", "sd_draft_attn_noalloc", "sd_summary_update", "sd_lm
            "sd_schedule_draft", "sd_schedule_verify", "sd_version",
            "SD_MASK_NONE", "SD_MASK_CAUSAL",
            "draft_attn_workspace_size", "lm_head_workspace_size",
-           "verify_workspace_size", "SdError", "load"]
+           "summary_workspace_size", "verify_workspace_size", "SdError", "load"]
 
 
 def _req(t: torch.Tensor, name: str, dtypes, device=None) -> torch.Tensor:
@@ -97,6 +97,12 @@ def lm_head_workspace_size(M, V) -> int:
 
 def markov_workspace_size(batch, V, max_draft_k) -> int:
     return int(load().sd_markov_workspace_size(batch, V, max_draft_k))
+
+
+def summary_workspace_size(batch, num_heads_kv, n_summary, head_dim, max_pages,
+                           page_size=16) -> int:
+    return int(load().sd_summary_workspace_size(batch, num_heads_kv, n_summary, head_dim,
+                                                max_pages, page_size))
 
 
 def verify_workspace_size(batch, total_q, total_target_rows, V) -> int:
@@ -213,10 +219,11 @@ def sd_draft_attn_noalloc(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_len
 
 def sd_summary_update(summary_queries, k_cache, v_cache, page_table, ctx_len, accepted_len,
                       summary_values, summary_lse, *, softmax_scale: Optional[float] = None,
-                      stream=None):
+                      workspace=None, stream=None):
     """Fold retained target KV rows into the context summary (in place); see
     ``sd_summary_update`` in include/sd.h.  ``accepted_len=None`` initialises
-    the summary from each request's whole prefix."""
+    the summary from each request's whole prefix (with ``workspace`` of
+    ``summary_workspace_size`` bytes, allocated here when None)."""
     lib = load()
     dev = summary_queries.device
     _req(summary_queries, "summary_queries", _BF16, dev)
@@ -238,11 +245,17 @@ def sd_summary_update(summary_queries, k_cache, v_cache, page_table, ctx_len, ac
     _need(accepted_len, batch, "accepted_len")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
+    ws, ws_bytes = None, 0
+    if accepted_len is None:
+        need = summary_workspace_size(batch, hkv, n_summary, D, max_pages, page_size)
+        if need or workspace is not None:
+            ws = _workspace(workspace, need, dev)
+            ws_bytes = ws.numel() * ws.element_size()
     st = lib.sd_summary_update(_ptr(summary_queries), _ptr(k_cache), _ptr(v_cache),
                                _ptr(page_table), _ptr(ctx_len), _ptr(accepted_len), batch,
                                num_pages, max_pages, page_size, hkv, D, n_summary,
                                float(softmax_scale), _ptr(summary_values), _ptr(summary_lse),
-                               _stream_handle(stream))
+                               _ptr(ws), ws_bytes, _stream_handle(stream))
     check("sd_summary_update", st)
     return summary_values, summary_lse
 

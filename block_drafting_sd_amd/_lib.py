@@ -37,8 +37,9 @@ SIGNATURES = {
                                      _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                      _i64, _i32, _f32, _i32, _i32, _vp, _vp, _i32,
                                      _vp, _vp]),
+    "sd_summary_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "sd_summary_update": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
-                                 _i32, _i32, _i32, _f32, _vp, _vp, _vp]),
+                                 _i32, _i32, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
     "sd_schedule_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
     "sd_schedule_draft": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32,

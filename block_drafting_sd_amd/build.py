@@ -31,12 +31,13 @@ HIP_FLAGS = [
 ]
 
 
-# Extra flags for single sources.  The attention kernel keeps its MFMA
+# Extra flags for single sources.  The attention and summary kernels keep their MFMA
 # accumulators in ordinary VGPRs: the softmax reads every score and rescales
 # the output accumulators, which would otherwise cost a copy out of (and back
 # into) the accumulation registers per tile.
 FILE_FLAGS = {
     "attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "summary.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -308,12 +308,30 @@ sd_status sd_draft_attn_noalloc(const void* q, const void* k_blk, const void* v_
                          stream);
 }
 
+// Workspace of a whole-prefix initialisation: the slices' partial states.
+static size_t summary_ws_bytes(int64_t batch, int64_t hkv, int64_t n_summary, int64_t head_dim,
+                               const sd::SummaryPlan& p) {
+  if (p.nsplit <= 1) return 0;
+  const size_t parts = static_cast<size_t>(batch * hkv * p.nsplit * n_summary);
+  return 2 * align_up(parts * sizeof(float)) + align_up(parts * head_dim * sizeof(float));
+}
+
+size_t sd_summary_workspace_size(int32_t batch, int32_t num_heads_kv, int32_t n_summary,
+                                 int32_t head_dim, int32_t max_pages, int32_t page_size) {
+  if (batch < 1 || num_heads_kv < 1 || n_summary < 1 || head_dim < 1 || max_pages < 1 ||
+      page_size != 16)
+    return 0;
+  return summary_ws_bytes(batch, num_heads_kv, n_summary, head_dim,
+                          sd::summary_plan(batch, num_heads_kv, max_pages));
+}
+
 sd_status sd_summary_update(const void* summary_queries, const void* k_cache, const void* v_cache,
                             const int32_t* page_table, const int32_t* ctx_len,
                             const int32_t* accepted_len, int32_t batch, int32_t num_pages,
                             int32_t max_pages, int32_t page_size, int32_t num_heads_kv,
                             int32_t head_dim, int32_t n_summary, float softmax_scale,
-                            float* summary_values, float* summary_lse, void* stream) {
+                            float* summary_values, float* summary_lse, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   if (!summary_queries || !k_cache || !v_cache || !page_table || !ctx_len || !summary_values ||
       !summary_lse)
     return SD_ERR_NULL;
@@ -325,8 +343,22 @@ sd_status sd_summary_update(const void* summary_queries, const void* k_cache, co
   if (static_cast<int64_t>(batch) * max_pages > (int64_t(1) << 31) - 1 ||
       static_cast<int64_t>(batch) * num_heads_kv > (int64_t(1) << 31) - 1)
     return SD_ERR_SHAPE;
-  if (!aligned16(k_cache) || !aligned16(v_cache)) return SD_ERR_SHAPE;
-  sd::SummaryArgs a;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(summary_queries))
+    return SD_ERR_SHAPE;
+  sd::SummaryPlan plan{1, static_cast<int64_t>(max_pages) * page_size};
+  if (!accepted_len) plan = sd::summary_plan(batch, num_heads_kv, max_pages);
+  if (static_cast<int64_t>(batch) * num_heads_kv * plan.nsplit > (int64_t(1) << 31) - 1)
+    return SD_ERR_SHAPE;
+  sd::SummaryArgs a{};
+  if (plan.nsplit > 1) {
+    const size_t need = summary_ws_bytes(batch, num_heads_kv, n_summary, head_dim, plan);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SD_ERR_WORKSPACE;
+    const size_t parts = static_cast<size_t>(batch) * num_heads_kv * plan.nsplit * n_summary;
+    char* w = static_cast<char*>(workspace);
+    a.part_m = reinterpret_cast<float*>(w);
+    a.part_l = reinterpret_cast<float*>(w + align_up(parts * sizeof(float)));
+    a.part_o = reinterpret_cast<float*>(w + 2 * align_up(parts * sizeof(float)));
+  }
   a.u = static_cast<const uint16_t*>(summary_queries);
   a.k_cache = static_cast<const uint16_t*>(k_cache);
   a.v_cache = static_cast<const uint16_t*>(v_cache);
@@ -340,8 +372,11 @@ sd_status sd_summary_update(const void* summary_queries, const void* k_cache, co
   a.n_summary = n_summary;
   a.num_pages = num_pages;
   a.max_pages = max_pages;
+  a.head_dim = head_dim;
+  a.nsplit = static_cast<int32_t>(plan.nsplit);
+  a.split_tokens = static_cast<int32_t>(plan.split_tokens);
   a.scale = softmax_scale;
-  return from_hip(sd::launch_summary(a, head_dim, static_cast<hipStream_t>(stream)));
+  return from_hip(sd::launch_summary(a, static_cast<hipStream_t>(stream)));
 }
 
 size_t sd_schedule_workspace_size(int32_t n, int32_t r, int32_t max_rows, int32_t m) {

@@ -78,13 +78,29 @@ struct SummaryArgs {
   const int32_t* accepted;    // [batch], or null to initialise from the prefix
   float* z;                   // [batch][hkv][n_summary][D]
   float* c;                   // [batch][hkv][n_summary]
-  int32_t batch, hkv, n_summary, num_pages, max_pages;
+  // slices of a whole-prefix initialisation (nsplit > 1): partial states
+  // [batch * hkv][nsplit][n_summary] (max in base 2, sum) and
+  // [batch * hkv][nsplit][n_summary][D] (unnormalised values), in the workspace
+  float* part_m;
+  float* part_l;
+  float* part_o;
+  int32_t batch, hkv, n_summary, num_pages, max_pages, head_dim;
+  int32_t nsplit, split_tokens;   // nsplit = 1: one wave per (request, KV head)
   float scale;
 };
 
-constexpr int kSummaryMax = 64;   // summary entries per KV head
+constexpr int kSummaryMax = 64;            // summary entries per KV head
+constexpr int kSummaryInitWaves = 8192;    // wavefronts an initialisation aims for
+constexpr int kSummaryMinSplit = 512;      // fewest tokens per slice
 
-hipError_t launch_summary(const SummaryArgs& a, int head_dim, hipStream_t s);
+struct SummaryPlan {
+  int64_t nsplit, split_tokens;
+};
+// Slices of a whole-prefix initialisation; folds always use one.
+SummaryPlan summary_plan(int64_t batch, int64_t hkv, int64_t max_pages);
+
+// Launches summary_rows (and summary_merge when the prefix is sliced).
+hipError_t launch_summary(const SummaryArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------- scheduling
 struct SchedGemmArgs {        // c = a1 b1^T (+ a2 b2^T) (+ bias, SiLU)

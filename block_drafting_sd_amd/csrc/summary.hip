@@ -11,16 +11,28 @@
 // eq. (11), c'' = log(e^c + e^c'), Z'' = e^(c - c'') Z + e^(c' - c'') Z'.
 // An empty set of new rows leaves the state as it is.
 //
-// summary_fold: one workgroup (4 waves) per (request, KV head).  The new rows
-// are read in place through the page table in tiles of 64: the tile's page
-// ids first, then every key chunk and every 8-token value chunk as
-// independent 16-byte loads.  Lane l of every wave owns row l of the tile;
-// wave w owns the summary queries w, w + 4, ...: its scores are dot products
-// of the lane's key row (read once per 8 dims) with each query (a broadcast
-// read), the online softmax of a query is a wave reduction, and the weighted
-// values are summed per (query, dim) entry with independent accumulators.
-// Everything is fp32.  A step folds at most K + 1 rows (one tile);
-// initialising from a whole prefix is the same loop over all of its tiles.
+// summary_rows: one wavefront per (request, KV head, slice of rows).  The
+// rows are walked in 32-token tiles (aligned to 32 tokens; rows outside the
+// slice are masked), read in place through the page table with 16-byte
+// non-temporal loads straight into MFMA operands; the next tile's loads are
+// in flight while the current one is computed.  Per tile and group of 16
+// summary queries:
+//   * scores^T (32 tokens x 16 queries) = K U^T as two 16x16x32 bf16 MFMA
+//     chains over the head dim; the A operand of chain h holds the tokens
+//     8 (r / 4) + 4 h + r % 4 for row r, so that each lane's eight scores are
+//     the tokens 8 (lane / 16) + [0, 8) of its query (lane % 16);
+//   * an online softmax in base 2 (running max per query over the four
+//     lanes of a column, sums kept per lane until the end);
+//   * O (16 queries x D) += P V with P as the A operand straight from the
+//     scores' registers and V's 16-byte loads (8 consecutive tokens of one
+//     dim) as B.  P enters as a bf16 pair hi + lo (hi = bf16(p),
+//     lo = bf16(p - hi)), two MFMAs per product, so the weights keep
+//     ~2^-18 relative error; every sum is fp32.
+// A fold (one slice: the new rows) merges its result into the stored state
+// with eq. (11).  Initialising from a whole prefix splits the prefix into
+// slices whose partial states (max, sum, unnormalised O) go to the
+// workspace, and summary_merge combines them per (request, KV head) with the
+// same merge rule.
 #include "sd_common.h"
 #include "sd_internal.h"
 
@@ -29,230 +41,318 @@
 namespace sd {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr int kRows = 64;                         // rows per tile = lanes
+constexpr int kTile = 32;        // tokens per wave step
+constexpr int kMergeThreads = 256;
 
-// D: head dim; SMAX: the most summary entries this instance handles (16, or
-// kSummaryMax), which sizes the per-wave query registers and accumulators.
-template <int D, int SMAX>
-__global__ __launch_bounds__(kThreads) void summary_fold(SummaryArgs a) {
-  constexpr int kQPerWave = SMAX / kWaves;        // summary queries per wave (max)
-  constexpr int KP = D + 8;                       // key row pitch (bf16): spreads banks
-  __shared__ __attribute__((aligned(16))) float s_u[SMAX * D];          // queries [q][d]
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[kRows * KP];     // keys [row][d]
-  __shared__ uint16_t s_v[kRows * D];                                   // values [row][d]
-  __shared__ float s_p[SMAX * kRows];                                   // weights [q][row]
-  __shared__ float s_alpha[SMAX];
-  __shared__ int s_pg[kRows];
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
-  const int b = blockIdx.x / a.hkv;
-  const int g = blockIdx.x % a.hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ __forceinline__ u32x4 load_nt(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+template <int D>
+struct Tile {
+  u32x4 k[2][D / 32];   // score chain h, k-step over the head dim
+  u32x4 v[D / 16];      // value columns 16 nb + (lane % 16)
+};
+
+// D: head dim; QG: groups of 16 summary queries (S <= 16 QG).
+template <int D, int QG>
+__global__ __launch_bounds__(64) void summary_rows(SummaryArgs a) {
+  constexpr int KS = D / 32, NB = D / 16;
+  const int pair = blockIdx.x / a.nsplit, split = blockIdx.x % a.nsplit;
+  const int b = pair / a.hkv, g = pair % a.hkv;
+  const int lane = threadIdx.x, col = lane & 15, grp = lane >> 4;
   const int S = a.n_summary;
   const int n_max = a.max_pages * 16;
   const int n = clampi(a.ctx_len[b], 0, n_max);
-  int r0, r1;   // rows [r0, r1) to fold
+  int lo, hi;   // rows [lo, hi) of this wave
   if (a.accepted) {
-    r0 = n;
-    r1 = min(n_max, n + clampi(a.accepted[b], 0, n_max) + 1);
+    lo = n;
+    hi = min(n_max, n + clampi(a.accepted[b], 0, n_max) + 1);
   } else {
-    r0 = 0;
-    r1 = n;
+    lo = 0;
+    hi = n;
   }
-  float* zs = a.z + (static_cast<size_t>(b) * a.hkv + g) * S * D;
-  float* cs = a.c + (static_cast<size_t>(b) * a.hkv + g) * S;
-  if (r1 <= r0) {
-    if (!a.accepted) {   // initialising from an empty prefix: the empty state
-      for (int i = tid; i < S; i += kThreads) cs[i] = -INFINITY;
-      for (int i = tid; i < S * D; i += kThreads) zs[i] = 0.f;
+  if (a.nsplit > 1) {
+    lo = max(lo, split * a.split_tokens);
+    hi = min(hi, (split + 1) * a.split_tokens);
+  }
+
+  // summary queries: B operand of the score products (query 16 qg + col)
+  bf16x8 uq[QG][KS];
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    const int q = 16 * qg + col;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      uq[qg][ks] = q < S ? load_bf16x8(a.u + (static_cast<size_t>(g) * S + q) * D + 32 * ks + 8 * grp)
+                         : zero_bf16x8();
+  }
+  f32x4 o[QG][NB];
+  float m[QG], l[QG];
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    m[qg] = -INFINITY;
+    l[qg] = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) o[qg][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float sl2 = a.scale * kLog2e;
+  const int* pt = a.page_table + static_cast<size_t>(b) * a.max_pages;
+  // the lane's key tokens (chain h) lie in tile page col / 8, its value
+  // tokens 8 grp .. 8 grp + 7 in tile page grp / 2
+  auto pages = [&](int t0, int& pk, int& pv) {
+    pk = clampi(pt[min((t0 >> 4) + (col >> 3), a.max_pages - 1)], 0, a.num_pages - 1);
+    pv = clampi(pt[min((t0 >> 4) + (grp >> 1), a.max_pages - 1)], 0, a.num_pages - 1);
+  };
+  auto load = [&](int pk, int pv, Tile<D>& r) {
+    const uint16_t* kb = a.k_cache + (static_cast<size_t>(pk) * a.hkv + g) * (D / 8) * 128;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int tok = (8 * (col >> 2) + 4 * h + (col & 3)) & 15;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) r.k[h][ks] = load_nt(kb + (4 * ks + grp) * 128 + tok * 8);
+    }
+    const uint16_t* vb = a.v_cache + (static_cast<size_t>(pv) * a.hkv + g) * D * 16 + ((8 * grp) & 15);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) r.v[nb] = load_nt(vb + (16 * nb + col) * 16);
+  };
+  auto compute = [&](int t0, const Tile<D>& r) {
+    const bool partial = t0 < lo || t0 + kTile > hi;       // wave-uniform
+    uint32_t keep = 0xffu;                                 // bit j: token t0 + 8 grp + j is in range
+    if (partial) {
+      keep = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int t = t0 + 8 * grp + j;
+        keep |= (t >= lo && t < hi) ? 1u << j : 0u;
+      }
+    }
+    bf16x8 vv[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      u32x4 w = r.v[nb];
+      if (partial) {   // rows outside the range may hold anything, even NaN
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] &= ((keep >> (2 * e)) & 1u ? 0x0000ffffu : 0u) | ((keep >> (2 * e + 1)) & 1u ? 0xffff0000u : 0u);
+      }
+      vv[nb] = __builtin_bit_cast(bf16x8, w);
+    }
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) {
+      f32x4 s[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) s[h] = mfma16(__builtin_bit_cast(bf16x8, r.k[h][ks]), uq[qg][ks], s[h]);
+      }
+      float x[8];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        x[j] = (keep >> j) & 1u ? s[j >> 2][j & 3] * sl2 : -INFINITY;
+        mt = fmaxf(mt, x[j]);
+      }
+      mt = fmaxf(mt, xor_shuffle(mt, 16));
+      mt = fmaxf(mt, xor_shuffle(mt, 32));
+      const float mn = fmaxf(m[qg], mt);                 // finite: every tile holds a row in range
+      const float al = exp2f(m[qg] - mn);                 // 0 on the first tile
+      float ls = 0.f;
+      bf16x8 ph, pl;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p = exp2f(x[j] - mn);
+        ls += p;
+        ph[j] = static_cast<__bf16>(p);
+        pl[j] = static_cast<__bf16>(p - static_cast<float>(ph[j]));
+      }
+      l[qg] = l[qg] * al + ls;
+      m[qg] = mn;
+      // row q = 16 qg + 4 grp + i of O takes the factor of column 4 grp + i
+      float ar[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ar[i] = __shfl(al, 4 * grp + i, 64);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[qg][nb][i] *= ar[i];
+        o[qg][nb] = mfma16(ph, vv[nb], o[qg][nb]);
+        o[qg][nb] = mfma16(pl, vv[nb], o[qg][nb]);
+      }
+    }
+  };
+
+  if (hi > lo) {
+    // tiles first + 32 i, i < nt, in two register sets in turn; the page ids
+    // run two tiles ahead of the loads that use them.  Inside the loop every
+    // load is unconditional (a conditional one would make the compiler copy
+    // the registers it fills, waiting for them at once); the last one or two
+    // tiles are computed after it.
+    const int first = lo & ~(kTile - 1);
+    const int nt = (hi - first + kTile - 1) / kTile;
+    int pka, pva, pkb, pvb;
+    pages(first, pka, pva);
+    pages(first + kTile, pkb, pvb);
+    Tile<D> ra, rb;
+    load(pka, pva, ra);
+    int i = 0;
+    for (; i + 2 < nt; i += 2) {
+      pages(first + (i + 2) * kTile, pka, pva);
+      load(pkb, pvb, rb);
+      compute(first + i * kTile, ra);
+      pages(first + (i + 3) * kTile, pkb, pvb);
+      load(pka, pva, ra);
+      compute(first + (i + 1) * kTile, rb);
+    }
+    if (i + 1 < nt) {
+      load(pkb, pvb, rb);
+      compute(first + i * kTile, ra);
+      compute(first + (i + 1) * kTile, rb);
+    } else {
+      compute(first + i * kTile, ra);
+    }
+  }
+  // per-query sums over the four lanes of a column
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    l[qg] += xor_shuffle(l[qg], 16);
+    l[qg] += xor_shuffle(l[qg], 32);
+  }
+
+  if (a.nsplit > 1) {
+    // partial state of the slice: max (base 2), sum, unnormalised O
+    const size_t base = static_cast<size_t>(blockIdx.x) * S;
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) {
+      const int q = 16 * qg + col;
+      if (grp == 0 && q < S) {
+        a.part_m[base + q] = m[qg];
+        a.part_l[base + q] = l[qg];
+      }
+      if (hi > lo) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int qi = 16 * qg + 4 * grp + i;
+          if (qi < S) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) a.part_o[(base + qi) * D + 16 * nb + col] = o[qg][nb][i];
+          }
+        }
+      }
     }
     return;
   }
 
-  const uint16_t* uq = a.u + static_cast<size_t>(g) * S * D;
-  for (int i = tid; i < S * D; i += kThreads) s_u[i] = __uint_as_float(static_cast<uint32_t>(uq[i]) << 16);
-  // running max and sum of the wave's queries (wave-uniform)
-  float m_run[kQPerWave], l_run[kQPerWave];
+  // one slice: merge with the stored state (eq. (11)); initialisation replaces it
+  float* zs = a.z + static_cast<size_t>(pair) * S * D;
+  float* cs = a.c + static_cast<size_t>(pair) * S;
 #pragma unroll
-  for (int j = 0; j < kQPerWave; ++j) {
-    m_run[j] = -INFINITY;
-    l_run[j] = 0.f;
-  }
-  // weighted values: thread t owns entries t, t + 256, ... of [q][d]
-  static_assert(kThreads % D == 0, "a thread's entries share one dim");
-  constexpr int kOwn = SMAX * D / kThreads;
-  float acc[kOwn];
+  for (int qg = 0; qg < QG; ++qg) {
 #pragma unroll
-  for (int e = 0; e < kOwn; ++e) acc[e] = 0.f;
-  const int* pt = a.page_table + static_cast<size_t>(b) * a.max_pages;
-
-  for (int t0 = r0; t0 < r1; t0 += kRows) {
-    const int rows = min(kRows, r1 - t0);
-    __syncthreads();   // the previous tile's readers are done
-    if (tid < kRows) s_pg[tid] = tid < rows ? clampi(pt[(t0 + tid) >> 4], 0, a.num_pages - 1) : 0;
-    __syncthreads();
-    // keys: one 16-byte chunk (8 dims) per (row, chunk)
-    constexpr int kKeyLoads = kRows * (D / 8) / kThreads;
-    u32x4 kv[kKeyLoads];
-#pragma unroll
-    for (int j = 0; j < kKeyLoads; ++j) {
-      const int i = tid + kThreads * j;
-      const int rr = i % kRows, c = i / kRows;
-      kv[j] = u32x4{0u, 0u, 0u, 0u};
-      if (rr < rows)
-        kv[j] = *reinterpret_cast<const u32x4*>(
-            a.k_cache + ((static_cast<size_t>(s_pg[rr]) * a.hkv + g) * (D / 8) + c) * 128 + ((t0 + rr) & 15) * 8);
-    }
-    // values: one 16-byte chunk = 8 consecutive tokens (8-aligned, so inside
-    // one page) of one dim; chunk ch covers tokens 8 ch .. 8 ch + 7
-    const int ch0 = t0 >> 3;
-    const int nch = ((t0 + rows - 1) >> 3) - ch0 + 1;           // <= kRows / 8 + 1
-    constexpr int kValLoads = (kRows / 8 + 1) * D / kThreads + 1;
-    u32x4 vv[kValLoads];
-#pragma unroll
-    for (int j = 0; j < kValLoads; ++j) {
-      const int i = tid + kThreads * j;
-      const int cj = i / D, d = i % D;
-      vv[j] = u32x4{0u, 0u, 0u, 0u};
-      if (cj < nch) {
-        const int first = max((ch0 + cj) * 8, t0);                // a row of this tile in the chunk's page
-        vv[j] = *reinterpret_cast<const u32x4*>(
-            a.v_cache + ((static_cast<size_t>(s_pg[first - t0]) * a.hkv + g) * D + d) * 16 + ((ch0 + cj) * 8 & 15));
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kKeyLoads; ++j) {
-      const int i = tid + kThreads * j;
-      const int rr = i % kRows, c = i / kRows;
-      *reinterpret_cast<u32x4*>(s_k + rr * KP + 8 * c) = kv[j];
-    }
-#pragma unroll
-    for (int j = 0; j < kValLoads; ++j) {
-      const int i = tid + kThreads * j;
-      const int cj = i / D, d = i % D;
-      if (cj < nch) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int rr = (ch0 + cj) * 8 + e - t0;
-          if (rr >= 0 && rr < rows) s_v[rr * D + d] = static_cast<uint16_t>(vv[j][e / 2] >> (16 * (e & 1)));
-        }
-      }
-    }
-    for (int i = tid; i < (kRows - rows) * D; i += kThreads) s_v[rows * D + i] = 0;
-    __syncthreads();
-
-    // scores of the wave's queries against row `lane`
-    float sc[kQPerWave];
-#pragma unroll
-    for (int j = 0; j < kQPerWave; ++j) sc[j] = 0.f;
-#pragma unroll 2
-    for (int c = 0; c < D / 8; ++c) {
-      const u32x4 kc = *reinterpret_cast<const u32x4*>(s_k + lane * KP + 8 * c);
-      float kf[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kf[e] = __uint_as_float((e & 1) ? (kc[e / 2] & 0xffff0000u) : (kc[e / 2] << 16));
-#pragma unroll
-      for (int j = 0; j < kQPerWave; ++j) {
-        const int q = wave + kWaves * j;
-        if (q < S) {                                     // wave-uniform
-          const float4 u0 = *reinterpret_cast<const float4*>(s_u + q * D + 8 * c);
-          const float4 u1 = *reinterpret_cast<const float4*>(s_u + q * D + 8 * c + 4);
-          sc[j] += u0.x * kf[0] + u0.y * kf[1] + u0.z * kf[2] + u0.w * kf[3] + u1.x * kf[4] + u1.y * kf[5] +
-                   u1.z * kf[6] + u1.w * kf[7];
-        }
-      }
-    }
-    // online softmax of each query over the tile (a wave reduction)
-#pragma unroll
-    for (int j = 0; j < kQPerWave; ++j) {
-      const int q = wave + kWaves * j;
-      if (q < S) {                                       // wave-uniform
-        const float s = lane < rows ? sc[j] * a.scale : -INFINITY;
-        float mx = s;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-        const float mnew = fmaxf(m_run[j], mx);
-        const float w = lane < rows ? expf(s - mnew) : 0.f;
-        float sum = w;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) sum += __shfl_xor(sum, o, 64);
-        const float alpha = expf(m_run[j] - mnew);       // 0 on the first tile (m_run = -inf)
-        l_run[j] = l_run[j] * alpha + sum;
-        m_run[j] = mnew;
-        s_p[q * kRows + lane] = w;
-        if (lane == 0) s_alpha[q] = alpha;
-      }
-    }
-    __syncthreads();
-    // entry e of this thread is (query (tid + 256 e) / D, dim tid % D): one
-    // value read per row serves all of them
-#pragma unroll
-    for (int e = 0; e < kOwn; ++e) {
-      const int idx = tid + kThreads * e;
-      if (idx < S * D) acc[e] *= s_alpha[idx / D];
-    }
-    for (int k = 0; k < rows; ++k) {
-      const float vk = __uint_as_float(static_cast<uint32_t>(s_v[k * D + tid % D]) << 16);
-#pragma unroll
-      for (int e = 0; e < kOwn; ++e) {
-        const int idx = tid + kThreads * e;
-        if (idx < S * D) acc[e] += s_p[(idx / D) * kRows + k] * vk;
-      }
-    }
-  }
-  // publish each query's running max and sum (s_alpha and s_p are free)
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kQPerWave; ++j) {
-    const int q = wave + kWaves * j;
-    if (q < S && lane == 0) {
-      s_alpha[q] = m_run[j];
-      s_p[q] = l_run[j];
-    }
-  }
-  __syncthreads();
-
-  // merge with the stored state (eq. (11)); initialisation replaces it
-#pragma unroll
-  for (int e = 0; e < kOwn; ++e) {
-    const int idx = tid + kThreads * e;
-    if (idx < S * D) {
-      const int q = idx / D;
-      const float c_new = s_alpha[q] + logf(s_p[q]);
-      const float z_new = acc[e] / s_p[q];
+    for (int i = 0; i < 4; ++i) {
+      const int q = 16 * qg + 4 * grp + i;
+      const float mq = __shfl(m[qg], 4 * grp + i, 64);
+      const float lq = __shfl(l[qg], 4 * grp + i, 64);
+      if (q >= S) continue;
+      const float c_new = lq > 0.f ? (mq + log2f(lq)) * kLn2 : -INFINITY;
       const float c_old = a.accepted ? cs[q] : -INFINITY;
-      if (c_old == -INFINITY) {
-        zs[idx] = z_new;
+      float* zq = zs + static_cast<size_t>(q) * D;
+      if (c_new == -INFINITY) {
+        if (!a.accepted) {   // empty prefix: the empty state
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) zq[16 * nb + col] = 0.f;
+        }
+      } else if (c_old == -INFINITY) {
+        const float inv = 1.f / lq;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) zq[16 * nb + col] = o[qg][nb][i] * inv;
       } else {
         const float mx = fmaxf(c_old, c_new);
         const float c = mx + logf(expf(c_old - mx) + expf(c_new - mx));
-        zs[idx] = expf(c_old - c) * zs[idx] + expf(c_new - c) * z_new;
+        const float wo = expf(c_old - c), wn = expf(c_new - c) / lq;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) zq[16 * nb + col] = wo * zq[16 * nb + col] + wn * o[qg][nb][i];
       }
-    }
-  }
-  __syncthreads();   // every thread has read cs[] before it is overwritten
-  for (int q = tid; q < S; q += kThreads) {
-    const float c_new = s_alpha[q] + logf(s_p[q]);
-    const float c_old = a.accepted ? cs[q] : -INFINITY;
-    if (c_old == -INFINITY) {
-      cs[q] = c_new;
-    } else {
-      const float mx = fmaxf(c_old, c_new);
-      cs[q] = mx + logf(expf(c_old - mx) + expf(c_new - mx));
+      if (col == 0) {
+        float c = c_old;
+        if (c_new != -INFINITY) {
+          if (c_old == -INFINITY) {
+            c = c_new;
+          } else {
+            const float mx = fmaxf(c_old, c_new);
+            c = mx + logf(expf(c_old - mx) + expf(c_new - mx));
+          }
+        }
+        cs[q] = a.accepted ? c : c_new;
+      }
     }
   }
 }
 
+// Combines the slices of a whole-prefix initialisation: entry (q, d) of a
+// (request, KV head) is sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s over
+// the non-empty slices s, M = max m_s; c = ln 2 (M + log2 of that sum).
+__global__ __launch_bounds__(kMergeThreads) void summary_merge(SummaryArgs a) {
+  const int pair = blockIdx.x, S = a.n_summary, D = a.head_dim;
+  const int e = blockIdx.y * kMergeThreads + threadIdx.x;
+  if (e >= S * D) return;
+  const int q = e / D, d = e % D;
+  const size_t base = static_cast<size_t>(pair) * a.nsplit;
+  float M = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s) {
+    const size_t i = (base + s) * S + q;
+    if (a.part_l[i] > 0.f) M = fmaxf(M, a.part_m[i]);
+  }
+  float L = 0.f, O = 0.f;
+  for (int s = 0; s < a.nsplit; ++s) {
+    const size_t i = (base + s) * S + q;
+    const float ls = a.part_l[i];
+    if (ls > 0.f) {
+      const float w = exp2f(a.part_m[i] - M);
+      L += ls * w;
+      O += a.part_o[i * D + d] * w;
+    }
+  }
+  a.z[(static_cast<size_t>(pair) * S + q) * D + d] = L > 0.f ? O / L : 0.f;
+  if (d == 0) a.c[static_cast<size_t>(pair) * S + q] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
+template <int D>
+hipError_t launch_rows(const SummaryArgs& a, dim3 grid, hipStream_t s) {
+  const dim3 block(64);
+  if (a.n_summary <= 16) return launch_kernel(summary_rows<D, 1>, grid, block, s, a);
+  if (a.n_summary <= 32) return launch_kernel(summary_rows<D, 2>, grid, block, s, a);
+  return launch_kernel(summary_rows<D, 4>, grid, block, s, a);
+}
+
 }  // namespace
 
-hipError_t launch_summary(const SummaryArgs& a, int head_dim, hipStream_t s) {
-  const dim3 grid(a.batch * a.hkv), block(kThreads);
-  if (a.n_summary <= 16)
-    return head_dim == 64 ? launch_kernel(summary_fold<64, 16>, grid, block, s, a)
-                          : launch_kernel(summary_fold<128, 16>, grid, block, s, a);
-  return head_dim == 64 ? launch_kernel(summary_fold<64, kSummaryMax>, grid, block, s, a)
-                        : launch_kernel(summary_fold<128, kSummaryMax>, grid, block, s, a);
+SummaryPlan summary_plan(int64_t batch, int64_t hkv, int64_t max_pages) {
+  // about 8,192 wavefronts (three rounds of the chip's wave slots at the
+  // operand registers these kernels hold), slices of at least 512 tokens
+  const int64_t pairs = batch * hkv, n_max = max_pages * 16;
+  const int64_t want = (kSummaryInitWaves + pairs - 1) / pairs;
+  int64_t tok = (n_max + want - 1) / want;
+  tok = ((tok + kTile - 1) / kTile) * kTile;
+  if (tok < kSummaryMinSplit) tok = kSummaryMinSplit;
+  SummaryPlan p;
+  p.nsplit = (n_max + tok - 1) / tok;
+  p.split_tokens = p.nsplit > 1 ? tok : n_max;
+  return p;
+}
+
+hipError_t launch_summary(const SummaryArgs& a, hipStream_t s) {
+  const int head_dim = a.head_dim;
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.batch) * a.hkv * a.nsplit));
+  hipError_t e = head_dim == 64 ? launch_rows<64>(a, grid, s) : launch_rows<128>(a, grid, s);
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  const dim3 mgrid(a.batch * a.hkv, (a.n_summary * head_dim + kMergeThreads - 1) / kMergeThreads);
+  return launch_kernel(summary_merge, mgrid, dim3(kMergeThreads), s, a);
 }
 
 }  // namespace sd

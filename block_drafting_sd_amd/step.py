@@ -24,7 +24,7 @@ import torch
 from . import (SD_MASK_CAUSAL, SD_MASK_NONE, draft_attn_workspace_size,
                lm_head_workspace_size, markov_workspace_size, sd_draft_attn,
                sd_lm_head_probs, sd_markov_sample, sd_summary_update, sd_verify,
-               verify_workspace_size)
+               summary_workspace_size, verify_workspace_size)
 
 
 @dataclass
@@ -82,6 +82,7 @@ class DraftVerifyStep:
         self.accepted = torch.empty(s.batch, dtype=torch.int32, device=dev)
         self.next_token = torch.empty(s.batch, dtype=torch.int32, device=dev)
         self.ratio = torch.empty(s.total_q, dtype=torch.float32, device=dev)
+        self.ws_summary = None
         u8 = dict(dtype=torch.uint8, device=dev)
         self.ws_attn = torch.empty(max(256, draft_attn_workspace_size(
             s.batch, s.num_heads_q, s.num_heads_kv, s.head_dim, s.max_draft_k, s.max_total_ctx,
@@ -98,10 +99,16 @@ class DraftVerifyStep:
             s.batch, s.total_q, s.total_target_rows, s.vocab)), **u8)
 
     def summary_init(self, t: Dict[str, torch.Tensor], stream=None):
-        """Summary of every request's prefix before the step's new rows."""
+        """Summary of every request's prefix before the step's new rows (its
+        workspace is allocated on the first call)."""
+        if self.ws_summary is None:
+            s = self.shape
+            need = summary_workspace_size(s.batch, s.num_heads_kv, self.options.n_summary,
+                                          s.head_dim, t["page_table"].shape[1])
+            self.ws_summary = torch.empty(max(256, need), dtype=torch.uint8, device=self.device)
         return sd_summary_update(t["summary_keys"], t["k_cache"], t["v_cache"], t["page_table"],
                                  t["ctx_len_prev"], None, self.summary_values, self.summary_lse,
-                                 stream=stream)
+                                 workspace=self.ws_summary, stream=stream)
 
     def attention(self, t: Dict[str, torch.Tensor], stream=None):
         s, o = self.shape, self.options

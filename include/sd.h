@@ -5,7 +5,8 @@
  * The step has three parts, one entry point each:
  *   sd_draft_attn     draft-block attention over the target's paged KV cache
  *                     (whole prefix, or recent window + context summary)
- *   sd_summary_update fold newly retained target KV rows into the summary
+ *   sd_summary_update summarise whole prefixes, or fold newly retained target
+ *                     KV rows into the summary
  *   sd_schedule_draft  pre-draft estimation, joint draft / verify schedule
  *   sd_schedule_verify post-draft estimation, verification budget split
  *   sd_lm_head_probs  drafter LM head, softmax statistics, draft sampling
@@ -235,10 +236,13 @@ sd_status sd_draft_attn_noalloc(const void* q, const void* k_blk, const void* v_
  *     committed token and the a_b accepted drafts, which the target's
  *     verification pass has already written to the cache) into the stored
  *     state; a stored c = -inf is the empty state.
- * Arithmetic is fp32 (online softmax over the new rows, then the merge).
+ * Arithmetic is fp32 (scores and weighted sums accumulate in fp32; the
+ * softmax weights enter the value sums as a bf16 pair hi + lo, ~2^-18
+ * relative), then the merge.
  *
  * Arguments
- *   summary_queries bf16 [Hkv, n_summary, D]  U (fixed, shared by requests)
+ *   summary_queries bf16 [Hkv, n_summary, D]  U (fixed, shared by requests),
+ *                   16-byte aligned
  *   k_cache, v_cache, page_table, num_pages, max_pages, page_size
  *                   as for sd_draft_attn (rows are read in place)
  *   ctx_len         int32 [batch]  N_b before the new rows
@@ -247,8 +251,18 @@ sd_status sd_draft_attn_noalloc(const void* q, const void* k_blk, const void* v_
  *   softmax_scale   > 0, usually 1/sqrt(head_dim)
  *   summary_values  fp32 [batch, Hkv, n_summary, D]  Z, updated in place
  *   summary_lse     fp32 [batch, Hkv, n_summary]     c, updated in place
- * No workspace.  One workgroup per (request, KV head).
+ *   workspace       initialisation (accepted_len == NULL) only: at least
+ *                   sd_summary_workspace_size(...) bytes (NULL allowed when
+ *                   that size is 0); folds ignore it
+ * Work: one wavefront per (request, KV head) for a fold; an initialisation
+ * slices every prefix (about 8,192 wavefronts, slices of >= 512 tokens,
+ * sized from max_pages) and merges the slices' states in a second kernel.
+ * Errors: SD_ERR_NULL, SD_ERR_SHAPE (as listed above, unaligned pointers),
+ * SD_ERR_WORKSPACE (initialisation with a missing or short workspace),
+ * SD_ERR_LAUNCH.
  * ------------------------------------------------------------------------ */
+size_t sd_summary_workspace_size(int32_t batch, int32_t num_heads_kv, int32_t n_summary,
+                                 int32_t head_dim, int32_t max_pages, int32_t page_size);
 sd_status sd_summary_update(const void* summary_queries, const void* k_cache,
                             const void* v_cache, const int32_t* page_table,
                             const int32_t* ctx_len, const int32_t* accepted_len,
@@ -256,7 +270,8 @@ sd_status sd_summary_update(const void* summary_queries, const void* k_cache,
                             int32_t page_size, int32_t num_heads_kv,
                             int32_t head_dim, int32_t n_summary,
                             float softmax_scale, float* summary_values,
-                            float* summary_lse, void* stream);
+                            float* summary_lse, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * sd_schedule_draft -- pre-draft estimation and the joint draft /

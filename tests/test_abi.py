@@ -140,21 +140,40 @@ def test_noalloc_rejects_before_any_device_call(lib):
 def _sum(lib, **kw):
     a = dict(u=FAKE, k_cache=FAKE, v_cache=FAKE, page_table=FAKE, ctx_len=FAKE, acc=FAKE,
              batch=2, num_pages=10, max_pages=5, page_size=16, hkv=2, d=128, n_sum=16,
-             scale=0.088, z=FAKE, c=FAKE)
+             scale=0.088, z=FAKE, c=FAKE, ws=FAKE, ws_bytes=1 << 40)
     a.update(kw)
     return lib.sd_summary_update(a["u"], a["k_cache"], a["v_cache"], a["page_table"],
                                  a["ctx_len"], a["acc"], a["batch"], a["num_pages"],
                                  a["max_pages"], a["page_size"], a["hkv"], a["d"], a["n_sum"],
-                                 a["scale"], a["z"], a["c"], None)
+                                 a["scale"], a["z"], a["c"], a["ws"], a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(u=None), 1), (dict(z=None), 1), (dict(c=None), 1), (dict(ctx_len=None), 1),
     (dict(batch=0), 2), (dict(d=96), 2), (dict(n_sum=0), 2), (dict(n_sum=65), 2),
-    (dict(page_size=8), 2), (dict(scale=-1.0), 2), (dict(k_cache=ODD), 2),
+    (dict(page_size=8), 2), (dict(scale=-1.0), 2), (dict(k_cache=ODD), 2), (dict(u=ODD), 2),
+    # an initialisation over 4,096-page rows is sliced and needs the workspace
+    (dict(acc=None, max_pages=4096, ws=None), 3), (dict(acc=None, max_pages=4096, ws_bytes=16), 3),
+    (dict(acc=None, max_pages=4096, ws=ODD), 3),
 ])
 def test_summary_update_validation(lib, kw, status):
     assert _sum(lib, **kw) == status
+
+
+def test_summary_workspace_size(lib):
+    """A fold needs no workspace; an initialisation is cut into slices of at
+    least 512 tokens, aiming at 8,192 wavefronts, each slice keeping a
+    (max, sum, S x D values) partial state in fp32."""
+    size = lib.sd_summary_workspace_size
+    assert size(2, 2, 16, 128, 5, 16) == 0          # 80 tokens: one slice
+    assert size(2, 2, 16, 128, 32, 16) == 0         # 512 tokens: one slice
+    # 16 requests x 8 KV heads over 131,072 tokens: 64 slices of 2,048 tokens
+    parts = 16 * 8 * 64 * 16
+    assert size(16, 8, 16, 128, 8192, 16) == 2 * parts * 4 + parts * 128 * 4
+    # 4 pairs over 65,536 tokens: slices of 512 tokens, 128 of them
+    parts = 4 * 128 * 16
+    assert size(2, 2, 16, 128, 4096, 16) == 2 * parts * 4 + parts * 128 * 4
+    assert size(0, 2, 16, 128, 4096, 16) == 0 and size(2, 2, 16, 128, 4096, 8) == 0
 
 
 def _lm(lib, **kw):

@@ -158,7 +158,8 @@ def _check_summary(z, c, Zr, Cr, tag):
     assert dz <= Z_ATOL and (dc.size == 0 or dc.max() <= C_RTOL)
 
 
-@pytest.mark.parametrize("head_dim,n_summary", [(128, 16), (64, 64), (128, 40), (64, 5)])
+@pytest.mark.parametrize("head_dim,n_summary", [(128, 16), (64, 64), (128, 40), (64, 5), (128, 64),
+                                                (64, 17)])
 def test_summary_init_then_fold(head_dim, n_summary):
     # every round appends a_b + 1 >= 1 rows; the first request starts empty
     inp = StepInputs(_cfg(head_dim=head_dim, batch=5, ctx=("list", (1, 2, 37, 160, 1000)),
@@ -183,6 +184,40 @@ def test_summary_init_then_fold(head_dim, n_summary):
     Zf, Cf = osum.summary_init(u, inp.k_cache, inp.v_cache, inp.page_table,
                                b.ctx_len.astype(np.int32), hkv, scale)
     _check_summary(z, c, Zf, Cf, "fold == summary of all rows")
+
+
+@pytest.mark.parametrize("head_dim,n_summary", [(128, 16), (64, 33)])
+def test_summary_init_sliced_ragged(head_dim, n_summary):
+    """Initialisation over many slices: ragged prefixes (empty, shorter than a
+    slice, ending inside a tile and inside a page, spanning dozens of
+    slices), every slice's partial state merged by the second kernel."""
+    ctx = (1, 5000, 12345, 511, 513, 31)
+    inp = StepInputs(_cfg(head_dim=head_dim, batch=len(ctx), ctx=("list", ctx),
+                          draft_k=("list", (1,) * len(ctx)), seed=6262))
+    b = inp.budgets
+    u = inp.summary_queries(n_summary)
+    hkv = inp.cfg.num_heads_kv
+    max_pages = inp.page_table.shape[1]
+    ws = sd.summary_workspace_size(len(ctx), hkv, n_summary, head_dim, max_pages)
+    log(f"sliced init: {max_pages} pages per row, workspace {ws} bytes")
+    assert ws > 0
+    n0 = b.ctx_len.astype(np.int32)
+    n0[0] = 0                                   # an empty prefix
+    Z0, C0 = osum.summary_init(u, inp.k_cache, inp.v_cache, inp.page_table, n0, hkv,
+                               inp.softmax_scale)
+    z, c = _gpu_summary(inp, u, n0)
+    _check_summary(z, c, Z0, C0, f"sliced init D={head_dim} S={n_summary}")
+    # folds that start inside a 32-token tile and end in the next one, or
+    # start on a tile or page boundary
+    acc = np.array([0, 40, 3, 30, 0, 20], np.int32)
+    old = (b.ctx_len - acc - 1).astype(np.int32)
+    z, c = _gpu_summary(inp, u, old)
+    Zs = z.cpu().numpy().astype(np.float64)
+    Cs = c.cpu().numpy().astype(np.float64)
+    Z1, C1 = osum.summary_update(u, inp.k_cache, inp.v_cache, inp.page_table, old, acc, Zs, Cs,
+                                 hkv, inp.softmax_scale)
+    z, c = _gpu_summary(inp, u, old, acc, state=(z, c))
+    _check_summary(z, c, Z1, C1, f"fold across tiles D={head_dim} S={n_summary}")
 
 
 def test_summary_then_attention_chain():
