@@ -313,7 +313,7 @@ static size_t summary_ws_bytes(int64_t batch, int64_t hkv, int64_t n_summary, in
                                const sd::SummaryPlan& p) {
   if (p.nsplit <= 1) return 0;
   const size_t parts = static_cast<size_t>(batch * hkv * p.nsplit * n_summary);
-  return 2 * align_up(parts * sizeof(float)) + align_up(parts * head_dim * sizeof(float));
+  return align_up(parts * 2 * sizeof(float)) + align_up(parts * head_dim * sizeof(float));
 }
 
 size_t sd_summary_workspace_size(int32_t batch, int32_t num_heads_kv, int32_t n_summary,
@@ -355,9 +355,8 @@ sd_status sd_summary_update(const void* summary_queries, const void* k_cache, co
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SD_ERR_WORKSPACE;
     const size_t parts = static_cast<size_t>(batch) * num_heads_kv * plan.nsplit * n_summary;
     char* w = static_cast<char*>(workspace);
-    a.part_m = reinterpret_cast<float*>(w);
-    a.part_l = reinterpret_cast<float*>(w + align_up(parts * sizeof(float)));
-    a.part_o = reinterpret_cast<float*>(w + 2 * align_up(parts * sizeof(float)));
+    a.part_ml = reinterpret_cast<float2*>(w);
+    a.part_o = reinterpret_cast<float*>(w + align_up(parts * 2 * sizeof(float)));
   }
   a.u = static_cast<const uint16_t*>(summary_queries);
   a.k_cache = static_cast<const uint16_t*>(k_cache);

@@ -81,8 +81,7 @@ struct SummaryArgs {
   // slices of a whole-prefix initialisation (nsplit > 1): partial states
   // [batch * hkv][nsplit][n_summary] (max in base 2, sum) and
   // [batch * hkv][nsplit][n_summary][D] (unnormalised values), in the workspace
-  float* part_m;
-  float* part_l;
+  float2* part_ml;
   float* part_o;
   int32_t batch, hkv, n_summary, num_pages, max_pages, head_dim;
   int32_t nsplit, split_tokens;   // nsplit = 1: one wave per (request, KV head)

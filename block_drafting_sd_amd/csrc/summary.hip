@@ -230,10 +230,7 @@ __global__ __launch_bounds__(64) void summary_rows(SummaryArgs a) {
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
       const int q = 16 * qg + col;
-      if (grp == 0 && q < S) {
-        a.part_m[base + q] = m[qg];
-        a.part_l[base + q] = l[qg];
-      }
+      if (grp == 0 && q < S) a.part_ml[base + q] = make_float2(m[qg], l[qg]);
       if (hi > lo) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -295,27 +292,38 @@ __global__ __launch_bounds__(64) void summary_rows(SummaryArgs a) {
 }
 
 // Combines the slices of a whole-prefix initialisation: entry (q, d) of a
-// (request, KV head) is sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s over
-// the non-empty slices s, M = max m_s; c = ln 2 (M + log2 of that sum).
+// (request, KV head) is sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over
+// the non-empty slices s, M = max m_s (base 2); c = ln 2 (M + log2 of the
+// denominator).
 __global__ __launch_bounds__(kMergeThreads) void summary_merge(SummaryArgs a) {
   const int pair = blockIdx.x, S = a.n_summary, D = a.head_dim;
   const int e = blockIdx.y * kMergeThreads + threadIdx.x;
   if (e >= S * D) return;
   const int q = e / D, d = e % D;
   const size_t base = static_cast<size_t>(pair) * a.nsplit;
-  float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const size_t i = (base + s) * S + q;
-    if (a.part_l[i] > 0.f) M = fmaxf(M, a.part_m[i]);
-  }
-  float L = 0.f, O = 0.f;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const size_t i = (base + s) * S + q;
-    const float ls = a.part_l[i];
-    if (ls > 0.f) {
-      const float w = exp2f(a.part_m[i] - M);
-      L += ls * w;
-      O += a.part_o[i * D + d] * w;
+  // one pass with a running maximum over groups of 16 slices whose loads go
+  // out together (clamped index; an empty slice's values are never written
+  // and are dropped by a select)
+  constexpr int U = 16;
+  float M = -INFINITY, L = 0.f, O = 0.f;
+  for (int s0 = 0; s0 < a.nsplit; s0 += U) {
+    float2 ml[U];
+    float os[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t i = (base + min(s0 + u, a.nsplit - 1)) * S + q;
+      ml[u] = a.part_ml[i];
+      os[u] = a.part_o[i * D + d];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool live = s0 + u < a.nsplit && ml[u].y > 0.f;
+      const float mn = live ? fmaxf(M, ml[u].x) : M;
+      const float r = mn == M ? 1.f : exp2f(M - mn);    // M = -inf: 0
+      const float w = live ? exp2f(ml[u].x - mn) : 0.f;
+      L = L * r + (live ? ml[u].y * w : 0.f);
+      O = O * r + (live ? os[u] * w : 0.f);
+      M = mn;
     }
   }
   a.z[(static_cast<size_t>(pair) * S + q) * D + d] = L > 0.f ? O / L : 0.f;
