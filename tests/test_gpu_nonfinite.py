@@ -1,4 +1,5 @@
-"""GPU parity with non-finite values in cache slots that no query attends.
+"""GPU parity with non-finite values in cache slots that no query attends
+(and that the context summary does not cover).
 
 The target's cache is read in place ("H-Spec", sec. 3.3.2), so the slots of a
 request's last page past its N_b tokens hold whatever the target last wrote
@@ -7,13 +8,15 @@ window the slots of the window's first page before N_b - W are outside the
 attended range.  Their weights are zero, and the output must not depend on
 them at all: these tests fill every such slot of both caches with NaN and
 +-infinity bf16 patterns and compare with the oracle, which never reads them.
+The summary walks 32-token tiles, so its first and last tiles hold rows
+outside the range it summarises; those are poisoned too.
 """
 import numpy as np
 import pytest
 import torch
 
 import block_drafting_sd_amd as sd
-from oracle import attention as oa, compare
+from oracle import attention as oa, compare, summary as osum
 from synth import StepInputs, device as sdev
 from synth.configs import C1_32K, C2_128K
 
@@ -112,3 +115,66 @@ def test_nonfinite_qwen_shapes():
     got, ref, hit = _run(inp)
     assert hit > 0
     _check(got, ref, f"nonfinite qwen slots={hit}")
+
+
+def _poison_rows(t, inp, b, t0, t1):
+    """Overwrite token rows [t0, t1) of request b in both caches."""
+    kc = t["k_cache"].view(torch.int16)
+    vc = t["v_cache"].view(torch.int16)
+    for tok in range(t0, t1):
+        page, slot = int(inp.page_table[b, tok // 16]), tok % 16
+        pk = torch.from_numpy(np.resize(POISON, kc[page, :, :, slot, :].numel()).view(np.int16)
+                              .copy()).to(DEV)
+        kc[page, :, :, slot, :] = pk.view(kc[page, :, :, slot, :].shape)
+        pv = torch.from_numpy(np.resize(POISON[::-1], vc[page, :, :, slot].numel()).view(np.int16)
+                              .copy()).to(DEV)
+        vc[page, :, :, slot] = pv.view(vc[page, :, :, slot].shape)
+    return t1 - t0
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_nonfinite_summary(head_dim):
+    """Initialisation with every slot past N_b poisoned, then a fold of
+    a_b + 1 rows starting inside a 32-token tile whose earlier rows (already
+    summarised) are poisoned as well."""
+    inp = StepInputs(_edge(head_dim=head_dim, ctx=("list", (1, 37, 160, 1000, 77)),
+                           draft_k=("list", (16, 16, 16, 16, 16))))
+    t = sdev.attention_tensors(inp, DEV)
+    b = inp.budgets
+    n = b.ctx_len.astype(np.int32)
+    acc = np.array([0, 5, 16, 9, 30], np.int32)
+    old = (n - acc - 1).astype(np.int32)
+    u = inp.summary_queries(16)
+    hkv, D, B = inp.cfg.num_heads_kv, head_dim, len(n)
+    hit = _poison(t, inp)
+    assert hit > 0
+    args = (sdev.bf16(u, DEV), t["k_cache"], t["v_cache"], t["page_table"])
+    # initialisation over the whole prefixes: the slots past N_b are poisoned
+    z = torch.full((B, hkv, 16, D), float("nan"), device=DEV)
+    c = torch.full((B, hkv, 16), float("nan"), device=DEV)
+    sd.sd_summary_update(*args, sdev.i32(n, DEV), None, z, c)
+    torch.cuda.synchronize()
+    Zr, Cr = osum.summary_init(u, inp.k_cache, inp.v_cache, inp.page_table, n, hkv,
+                               inp.softmax_scale)
+    zg, cg = z.cpu().numpy().astype(np.float64), c.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(zg)) and np.all(np.isfinite(cg))
+    dz, dc = np.abs(zg - Zr).max(), (np.abs(cg - Cr) / np.maximum(1, np.abs(Cr))).max()
+    log(f"nonfinite summary init D={head_dim} slots={hit}: Z max-abs {dz:.3g}, c max-rel {dc:.3g}")
+    assert dz <= 1e-4 and dc <= 1e-4
+    # the state before the new rows, then poison the rows of the fold's first
+    # tile that come before it, and fold
+    sd.sd_summary_update(*args, sdev.i32(old, DEV), None, z, c)
+    torch.cuda.synchronize()
+    Zs, Cs = z.cpu().numpy().astype(np.float64), c.cpu().numpy().astype(np.float64)
+    hit2 = sum(_poison_rows(t, inp, r, int(old[r]) & ~31, int(old[r])) for r in range(B))
+    torch.cuda.synchronize()
+    assert hit2 > 0
+    sd.sd_summary_update(*args, sdev.i32(old, DEV), sdev.i32(acc, DEV), z, c)
+    torch.cuda.synchronize()
+    Z1, C1 = osum.summary_update(u, inp.k_cache, inp.v_cache, inp.page_table, old, acc, Zs, Cs,
+                                 hkv, inp.softmax_scale)
+    zg, cg = z.cpu().numpy().astype(np.float64), c.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(zg)) and np.all(np.isfinite(cg))
+    dz, dc = np.abs(zg - Z1).max(), (np.abs(cg - C1) / np.maximum(1, np.abs(C1))).max()
+    log(f"nonfinite summary fold D={head_dim} slots={hit2}: Z max-abs {dz:.3g}, c max-rel {dc:.3g}")
+    assert dz <= 1e-4 and dc <= 1e-4
