@@ -341,8 +341,9 @@ hipError_t launch_rows(const SummaryArgs& a, dim3 grid, hipStream_t s) {
 }  // namespace
 
 SummaryPlan summary_plan(int64_t batch, int64_t hkv, int64_t max_pages) {
-  // about 8,192 wavefronts (three rounds of the chip's wave slots at the
-  // operand registers these kernels hold), slices of at least 512 tokens
+  // about 8,192 wavefronts (four rounds of the chip's 2,048 wave slots at
+  // two waves per SIMD, the register budget of the 16-entry kernels), slices
+  // of at least 512 tokens
   const int64_t pairs = batch * hkv, n_max = max_pages * 16;
   const int64_t want = (kSummaryInitWaves + pairs - 1) / pairs;
   int64_t tok = (n_max + want - 1) / want;
