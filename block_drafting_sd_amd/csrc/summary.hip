@@ -58,8 +58,10 @@ struct Tile {
   u32x4 v[D / 16];      // value columns 16 nb + (lane % 16)
 };
 
-// D: head dim; QG: groups of 16 summary queries (S <= 16 QG).
-template <int D, int QG>
+// D: head dim; QG: groups of 16 summary queries (S <= 16 QG); FOLD: a fold
+// (a.accepted given), whose stored state is loaded at the start (one group
+// of queries) so that its latency overlaps the page-id and row loads.
+template <int D, int QG, bool FOLD>
 __global__ __launch_bounds__(64) void summary_rows(SummaryArgs a) {
   constexpr int KS = D / 32, NB = D / 16;
   const int pair = blockIdx.x / a.nsplit, split = blockIdx.x % a.nsplit;
@@ -69,7 +71,7 @@ __global__ __launch_bounds__(64) void summary_rows(SummaryArgs a) {
   const int n_max = a.max_pages * 16;
   const int n = clampi(a.ctx_len[b], 0, n_max);
   int lo, hi;   // rows [lo, hi) of this wave
-  if (a.accepted) {
+  if constexpr (FOLD) {
     lo = n;
     hi = min(n_max, n + clampi(a.accepted[b], 0, n_max) + 1);
   } else {
@@ -79,6 +81,21 @@ __global__ __launch_bounds__(64) void summary_rows(SummaryArgs a) {
   if (a.nsplit > 1) {
     lo = max(lo, split * a.split_tokens);
     hi = min(hi, (split + 1) * a.split_tokens);
+  }
+
+  // a fold's stored state for the entries this lane merges (below)
+  constexpr bool kEarly = FOLD && QG == 1;
+  float c_pre[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  float z_pre[kEarly ? 4 : 1][kEarly ? NB : 1];
+  if constexpr (kEarly) {
+    const float* zs = a.z + static_cast<size_t>(pair) * S * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = 4 * grp + i;
+      c_pre[i] = q < S ? a.c[static_cast<size_t>(pair) * S + q] : 0.f;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) z_pre[i][nb] = q < S ? zs[static_cast<size_t>(q) * D + 16 * nb + col] : 0.f;
+    }
   }
 
   // summary queries: B operand of the score products (query 16 qg + col)
@@ -257,10 +274,12 @@ __global__ __launch_bounds__(64) void summary_rows(SummaryArgs a) {
       const float lq = __shfl(l[qg], 4 * grp + i, 64);
       if (q >= S) continue;
       const float c_new = lq > 0.f ? (mq + log2f(lq)) * kLn2 : -INFINITY;
-      const float c_old = a.accepted ? cs[q] : -INFINITY;
+      float c_old = -INFINITY;
+      if constexpr (kEarly) c_old = c_pre[i];
+      else if constexpr (FOLD) c_old = cs[q];
       float* zq = zs + static_cast<size_t>(q) * D;
       if (c_new == -INFINITY) {
-        if (!a.accepted) {   // empty prefix: the empty state
+        if (!FOLD) {   // empty prefix: the empty state
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) zq[16 * nb + col] = 0.f;
         }
@@ -273,7 +292,12 @@ __global__ __launch_bounds__(64) void summary_rows(SummaryArgs a) {
         const float c = mx + logf(expf(c_old - mx) + expf(c_new - mx));
         const float wo = expf(c_old - c), wn = expf(c_new - c) / lq;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) zq[16 * nb + col] = wo * zq[16 * nb + col] + wn * o[qg][nb][i];
+        for (int nb = 0; nb < NB; ++nb) {
+          float z_old;
+          if constexpr (kEarly) z_old = z_pre[i][nb];
+          else z_old = zq[16 * nb + col];
+          zq[16 * nb + col] = wo * z_old + wn * o[qg][nb][i];
+        }
       }
       if (col == 0) {
         float c = c_old;
@@ -285,7 +309,7 @@ __global__ __launch_bounds__(64) void summary_rows(SummaryArgs a) {
             c = mx + logf(expf(c_old - mx) + expf(c_new - mx));
           }
         }
-        cs[q] = a.accepted ? c : c_new;
+        cs[q] = FOLD ? c : c_new;
       }
     }
   }
@@ -330,12 +354,12 @@ __global__ __launch_bounds__(kMergeThreads) void summary_merge(SummaryArgs a) {
   if (d == 0) a.c[static_cast<size_t>(pair) * S + q] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
-template <int D>
+template <int D, bool FOLD>
 hipError_t launch_rows(const SummaryArgs& a, dim3 grid, hipStream_t s) {
   const dim3 block(64);
-  if (a.n_summary <= 16) return launch_kernel(summary_rows<D, 1>, grid, block, s, a);
-  if (a.n_summary <= 32) return launch_kernel(summary_rows<D, 2>, grid, block, s, a);
-  return launch_kernel(summary_rows<D, 4>, grid, block, s, a);
+  if (a.n_summary <= 16) return launch_kernel(summary_rows<D, 1, FOLD>, grid, block, s, a);
+  if (a.n_summary <= 32) return launch_kernel(summary_rows<D, 2, FOLD>, grid, block, s, a);
+  return launch_kernel(summary_rows<D, 4, FOLD>, grid, block, s, a);
 }
 
 }  // namespace
@@ -358,7 +382,11 @@ SummaryPlan summary_plan(int64_t batch, int64_t hkv, int64_t max_pages) {
 hipError_t launch_summary(const SummaryArgs& a, hipStream_t s) {
   const int head_dim = a.head_dim;
   const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.batch) * a.hkv * a.nsplit));
-  hipError_t e = head_dim == 64 ? launch_rows<64>(a, grid, s) : launch_rows<128>(a, grid, s);
+  hipError_t e;
+  if (a.accepted)
+    e = head_dim == 64 ? launch_rows<64, true>(a, grid, s) : launch_rows<128, true>(a, grid, s);
+  else
+    e = head_dim == 64 ? launch_rows<64, false>(a, grid, s) : launch_rows<128, false>(a, grid, s);
   if (e != hipSuccess || a.nsplit == 1) return e;
   const dim3 mgrid(a.batch * a.hkv, (a.n_summary * head_dim + kMergeThreads - 1) / kMergeThreads);
   return launch_kernel(summary_merge, mgrid, dim3(kMergeThreads), s, a);
