@@ -6,8 +6,10 @@ launches on the caller's stream, so a serving loop can capture a whole
 draft-and-verify step once and replay it.  Each replay here follows eager work
 on the same buffers (the step run eagerly with another seed, which overwrites
 every output) and a synchronisation, and must reproduce the eager outputs of
-the captured seed bit for bit.  The variants are the stateless ones: the
-summary fold updates its state in place, so its replays differ by design.
+the captured seed bit for bit.  The fixed-cost path also folds the accepted
+rows into its summary state in place, so that state is reset from a saved
+copy before every eager run and every replay, and the folded state is
+compared too.
 """
 import numpy as np
 import pytest
@@ -34,6 +36,7 @@ def _setup(path):
         "full": StepOptions(),
         "hspec_greedy": StepOptions(causal_block=True, window=512, draft_vocab=1000, greedy=True),
         "fusion": StepOptions(markov_rank=64, markov_alpha=0.3, prior_beta=0.3),
+        "fixed": StepOptions(window=256, n_summary=16),
     }[path]
     t = {}
     t.update(sdev.attention_tensors(inp, DEV))
@@ -52,22 +55,45 @@ def _setup(path):
     if opts.prior_beta:
         t["vocab_bias"] = sd.sd_log_prior_bias(torch.from_numpy(inp.unigram_counts()).to(DEV),
                                                lam=1.0, scale=-opts.prior_beta)
+    if opts.n_summary:
+        # the last K_max + 1 rows of each prefix stand in for the new rows
+        t["summary_keys"] = sdev.bf16(inp.summary_queries(opts.n_summary), DEV)
+        t["ctx_len_prev"] = sdev.i32(np.maximum(b.ctx_len - (int(b.draft_k.max()) + 1), 0), DEV)
     shape = StepShape(batch=cfg.batch, total_q=inp.total_q, total_target_rows=inp.total_target_rows,
                       num_heads_q=cfg.num_heads_q, num_heads_kv=cfg.num_heads_kv,
                       head_dim=cfg.head_dim, hidden=cfg.hidden, vocab=cfg.vocab,
                       max_total_ctx=inp.max_total_ctx, max_draft_k=int(b.draft_k.max()))
-    return DraftVerifyStep(shape, DEV, opts), t, inp.philox_seed
+    step = DraftVerifyStep(shape, DEV, opts)
+    if opts.n_summary:
+        step.summary_init(t)
+    return step, t, inp.philox_seed
 
 
 def _snapshot(out):
     return {k: v.clone() for k, v in out.items()}
 
 
-@pytest.mark.parametrize("path", ["full", "hspec_greedy", "fusion"])
+@pytest.mark.parametrize("path", ["full", "hspec_greedy", "fusion", "fixed"])
 def test_step_graph_replays_match_eager(path):
     step, t, seed = _setup(path)
-    ref = _snapshot(step.run(t, seed))
-    other = _snapshot(step.run(t, seed + 1))
+    stateful = step.options.n_summary > 0
+    saved = (step.summary_values.clone(), step.summary_lse.clone()) if stateful else None
+
+    def reset():
+        if stateful:
+            step.summary_values.copy_(saved[0])
+            step.summary_lse.copy_(saved[1])
+
+    def outputs(out):
+        d = dict(out)
+        if stateful:
+            d.update(summary_values=step.summary_values, summary_lse=step.summary_lse)
+        return d
+
+    reset()
+    ref = _snapshot(outputs(step.run(t, seed)))
+    reset()
+    other = _snapshot(outputs(step.run(t, seed + 1)))
     torch.cuda.synchronize()
     # the other seed must change what the replays have to restore
     assert not torch.equal(ref["logits"], other["logits"]) or not torch.equal(ref["tokens"],
@@ -76,17 +102,21 @@ def test_step_graph_replays_match_eager(path):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
+        reset()
         step.run(t, seed)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        outs = step.run(t, seed)
+        outs = outputs(step.run(t, seed))
     torch.cuda.synchronize()
     for rep in range(3):
+        reset()
         step.run(t, seed + 1 + rep)                 # eager work on the same buffers
         x = torch.randn(256, 256, device=DEV)
         (x @ x).sum().item()                        # unrelated eager work, then a sync
+        torch.cuda.synchronize()
+        reset()
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
