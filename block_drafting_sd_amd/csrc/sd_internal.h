@@ -89,7 +89,7 @@ struct SummaryArgs {
 };
 
 constexpr int kSummaryMax = 64;            // summary entries per KV head
-constexpr int kSummaryInitWaves = 8192;    // wavefronts an initialisation aims for
+constexpr int kSummaryInitWaves = 1024;    // wavefronts an initialisation aims for
 constexpr int kSummaryMinSplit = 512;      // fewest tokens per slice
 
 struct SummaryPlan {

@@ -365,9 +365,10 @@ hipError_t launch_rows(const SummaryArgs& a, dim3 grid, hipStream_t s) {
 }  // namespace
 
 SummaryPlan summary_plan(int64_t batch, int64_t hkv, int64_t max_pages) {
-  // about 8,192 wavefronts (four rounds of the chip's 2,048 wave slots at
-  // two waves per SIMD, the register budget of the 16-entry kernels), slices
-  // of at least 512 tokens
+  // about 1,024 wavefronts (one per SIMD) in slices of at least 512 tokens:
+  // at 16 x 131,072-token prefixes 8,192 / 4,096 / 2,048 / 1,024 / 768 / 512
+  // wavefronts took 1.44 / 1.35 / 1.30 / 1.26 / 1.24 / 1.25 ms (fewer
+  // wavefronts: fewer partials to write and merge, less per-wave start-up)
   const int64_t pairs = batch * hkv, n_max = max_pages * 16;
   const int64_t want = (kSummaryInitWaves + pairs - 1) / pairs;
   int64_t tok = (n_max + want - 1) / want;

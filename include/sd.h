@@ -255,8 +255,9 @@ sd_status sd_draft_attn_noalloc(const void* q, const void* k_blk, const void* v_
  *                   sd_summary_workspace_size(...) bytes (NULL allowed when
  *                   that size is 0); folds ignore it
  * Work: one wavefront per (request, KV head) for a fold; an initialisation
- * slices every prefix (about 8,192 wavefronts, slices of >= 512 tokens,
- * sized from max_pages) and merges the slices' states in a second kernel.
+ * slices every prefix (about 1,024 wavefronts, slices of >= 512 tokens,
+ * sized from max_pages; none when there are 1,024 or more (request, KV head)
+ * pairs) and merges the slices' states in a second kernel.
  * Errors: SD_ERR_NULL, SD_ERR_SHAPE (as listed above, unaligned pointers),
  * SD_ERR_WORKSPACE (initialisation with a missing or short workspace),
  * SD_ERR_LAUNCH.

@@ -162,17 +162,19 @@ def test_summary_update_validation(lib, kw, status):
 
 def test_summary_workspace_size(lib):
     """A fold needs no workspace; an initialisation is cut into slices of at
-    least 512 tokens, aiming at 8,192 wavefronts, each slice keeping a
+    least 512 tokens, aiming at 1,024 wavefronts, each slice keeping a
     (max, sum, S x D values) partial state in fp32."""
     size = lib.sd_summary_workspace_size
     assert size(2, 2, 16, 128, 5, 16) == 0          # 80 tokens: one slice
     assert size(2, 2, 16, 128, 32, 16) == 0         # 512 tokens: one slice
-    # 16 requests x 8 KV heads over 131,072 tokens: 64 slices of 2,048 tokens
-    parts = 16 * 8 * 64 * 16
+    # 16 requests x 8 KV heads over 131,072 tokens: 8 slices of 16,384 tokens
+    parts = 16 * 8 * 8 * 16
     assert size(16, 8, 16, 128, 8192, 16) == 2 * parts * 4 + parts * 128 * 4
     # 4 pairs over 65,536 tokens: slices of 512 tokens, 128 of them
     parts = 4 * 128 * 16
     assert size(2, 2, 16, 128, 4096, 16) == 2 * parts * 4 + parts * 128 * 4
+    # 128 requests x 8 KV heads: one wavefront per pair already, no slices
+    assert size(128, 8, 16, 128, 8192, 16) == 0
     assert size(0, 2, 16, 128, 4096, 16) == 0 and size(2, 2, 16, 128, 4096, 8) == 0
 
 
