@@ -22,7 +22,7 @@ import torch
 import block_drafting_sd_amd as sd
 from oracle import attention as oa, compare, step as ostep, summary as osum, verify as overify
 from synth import StepInputs, device as sdev
-from synth.configs import C1_32K, C2_128K
+from synth.configs import C1_32K, C2_128K, C4_RAGGED
 
 from gpu_common import DEV, bits, log, requires_gpu
 
@@ -218,6 +218,51 @@ def test_summary_init_sliced_ragged(head_dim, n_summary):
                                  hkv, inp.softmax_scale)
     z, c = _gpu_summary(inp, u, old, acc, state=(z, c))
     _check_summary(z, c, Z1, C1, f"fold across tiles D={head_dim} S={n_summary}")
+
+
+def test_summary_init_full_size_ragged():
+    """The ragged serving mix at full size (128 requests, 1K-128K-token
+    prefixes, 8 KV heads): with 1,024 (request, KV head) pairs every pair is
+    one wavefront walking its whole prefix; its first 16 requests alone
+    (128 pairs) are cut into slices and merged.  Sampled requests (the
+    longest, the shortest, one between) against the oracle."""
+    cfg = C4_RAGGED.with_(hidden=64, vocab=64)
+    inp = StepInputs(cfg)
+    t = sdev.attention_tensors(inp, DEV)
+    b = inp.budgets
+    hkv, D = cfg.num_heads_kv, cfg.head_dim
+    u = inp.summary_queries(16)
+    uu = sdev.bf16(u, DEV)
+    ref = {}
+
+    def oracle(r):
+        if r not in ref:
+            kl, vl = inp.logical_kv(r)
+            zr, cr = np.zeros((hkv, 16, D)), np.zeros((hkv, 16))
+            for g in range(hkv):
+                zr[g], cr[g] = osum.summary_of_rows(u[g], kl[:, g], vl[:, g], inp.softmax_scale)
+            ref[r] = (zr, cr)
+        return ref[r]
+
+    for nreq in (cfg.batch, 16):
+        max_pages = t["page_table"].shape[1]
+        ws = sd.summary_workspace_size(nreq, hkv, 16, D, max_pages)
+        z = torch.full((nreq, hkv, 16, D), float("nan"), device=DEV)
+        c = torch.full((nreq, hkv, 16), float("nan"), device=DEV)
+        sd.sd_summary_update(uu, t["k_cache"], t["v_cache"], t["page_table"][:nreq].contiguous(),
+                             t["ctx_len"][:nreq].contiguous(), None, z, c)
+        torch.cuda.synchronize()
+        n = b.ctx_len[:nreq]
+        reqs = sorted({int(np.argmax(n)), int(np.argmin(n)), nreq // 2})
+        zg, cg = z.cpu().numpy(), c.cpu().numpy()
+        for r in reqs:
+            zr, cr = oracle(r)
+            dz = np.abs(zg[r] - zr).max()
+            rel = np.linalg.norm(zg[r] - zr) / np.linalg.norm(zr)
+            dc = (np.abs(cg[r] - cr) / np.maximum(1, np.abs(cr))).max()
+            log(f"ragged summary init, {nreq} requests (workspace {ws} B), request {r} "
+                f"({int(n[r])} tokens): Z max-abs {dz:.3g}, rel-L2 {rel:.3g}, c max-rel {dc:.3g}")
+            assert dz <= Z_ATOL and rel <= 1e-4 and dc <= C_RTOL
 
 
 def test_summary_then_attention_chain():
