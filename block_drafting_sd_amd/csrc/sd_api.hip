@@ -309,10 +309,8 @@ sd_status sd_draft_attn_noalloc(const void* q, const void* k_blk, const void* v_
 }
 
 // Workspace of a whole-prefix initialisation: the slices' partial states.
-static size_t summary_ws_bytes(int64_t batch, int64_t hkv, int64_t n_summary, int64_t head_dim,
-                               const sd::SummaryPlan& p) {
-  if (p.nsplit <= 1) return 0;
-  const size_t parts = static_cast<size_t>(batch * hkv * p.nsplit * n_summary);
+static size_t summary_ws_bytes(int64_t batch, int64_t hkv, int64_t n_summary, int64_t head_dim) {
+  const size_t parts = static_cast<size_t>(sd::summary_init_slots(batch, hkv) * n_summary);
   return align_up(parts * 2 * sizeof(float)) + align_up(parts * head_dim * sizeof(float));
 }
 
@@ -321,8 +319,7 @@ size_t sd_summary_workspace_size(int32_t batch, int32_t num_heads_kv, int32_t n_
   if (batch < 1 || num_heads_kv < 1 || n_summary < 1 || head_dim < 1 || max_pages < 1 ||
       page_size != 16)
     return 0;
-  return summary_ws_bytes(batch, num_heads_kv, n_summary, head_dim,
-                          sd::summary_plan(batch, num_heads_kv, max_pages));
+  return summary_ws_bytes(batch, num_heads_kv, n_summary, head_dim);
 }
 
 sd_status sd_summary_update(const void* summary_queries, const void* k_cache, const void* v_cache,
@@ -341,19 +338,15 @@ sd_status sd_summary_update(const void* summary_queries, const void* k_cache, co
     return SD_ERR_SHAPE;
   if (static_cast<int64_t>(max_pages) * page_size > (int64_t(1) << 30)) return SD_ERR_SHAPE;
   if (static_cast<int64_t>(batch) * max_pages > (int64_t(1) << 31) - 1 ||
-      static_cast<int64_t>(batch) * num_heads_kv > (int64_t(1) << 31) - 1)
+      sd::summary_init_slots(batch, num_heads_kv) > (int64_t(1) << 31) - 1)
     return SD_ERR_SHAPE;
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(summary_queries))
     return SD_ERR_SHAPE;
-  sd::SummaryPlan plan{1, static_cast<int64_t>(max_pages) * page_size};
-  if (!accepted_len) plan = sd::summary_plan(batch, num_heads_kv, max_pages);
-  if (static_cast<int64_t>(batch) * num_heads_kv * plan.nsplit > (int64_t(1) << 31) - 1)
-    return SD_ERR_SHAPE;
   sd::SummaryArgs a{};
-  if (plan.nsplit > 1) {
-    const size_t need = summary_ws_bytes(batch, num_heads_kv, n_summary, head_dim, plan);
+  if (!accepted_len) {
+    const size_t need = summary_ws_bytes(batch, num_heads_kv, n_summary, head_dim);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SD_ERR_WORKSPACE;
-    const size_t parts = static_cast<size_t>(batch) * num_heads_kv * plan.nsplit * n_summary;
+    const size_t parts = static_cast<size_t>(sd::summary_init_slots(batch, num_heads_kv) * n_summary);
     char* w = static_cast<char*>(workspace);
     a.part_ml = reinterpret_cast<float2*>(w);
     a.part_o = reinterpret_cast<float*>(w + align_up(parts * 2 * sizeof(float)));
@@ -372,8 +365,6 @@ sd_status sd_summary_update(const void* summary_queries, const void* k_cache, co
   a.num_pages = num_pages;
   a.max_pages = max_pages;
   a.head_dim = head_dim;
-  a.nsplit = static_cast<int32_t>(plan.nsplit);
-  a.split_tokens = static_cast<int32_t>(plan.split_tokens);
   a.scale = softmax_scale;
   return from_hip(sd::launch_summary(a, static_cast<hipStream_t>(stream)));
 }

@@ -78,27 +78,24 @@ struct SummaryArgs {
   const int32_t* accepted;    // [batch], or null to initialise from the prefix
   float* z;                   // [batch][hkv][n_summary][D]
   float* c;                   // [batch][hkv][n_summary]
-  // slices of a whole-prefix initialisation (nsplit > 1): partial states
-  // [batch * hkv][nsplit][n_summary] (max in base 2, sum) and
-  // [batch * hkv][nsplit][n_summary][D] (unnormalised values), in the workspace
+  // slices of a whole-prefix initialisation: partial states per slice slot
+  // [slots][n_summary] (max in base 2, sum) and [slots][n_summary][D]
+  // (unnormalised values), in the workspace
   float2* part_ml;
   float* part_o;
   int32_t batch, hkv, n_summary, num_pages, max_pages, head_dim;
-  int32_t nsplit, split_tokens;   // nsplit = 1: one wave per (request, KV head)
   float scale;
 };
 
 constexpr int kSummaryMax = 64;            // summary entries per KV head
-constexpr int kSummaryInitWaves = 1024;    // wavefronts an initialisation aims for
+constexpr int kSummaryInitWaves = 1024;    // slices an initialisation aims for (one per SIMD)
 constexpr int kSummaryMinSplit = 512;      // fewest tokens per slice
 
-struct SummaryPlan {
-  int64_t nsplit, split_tokens;
-};
-// Slices of a whole-prefix initialisation; folds always use one.
-SummaryPlan summary_plan(int64_t batch, int64_t hkv, int64_t max_pages);
+// Slice slots of an initialisation (an upper bound on the slices; the extra
+// waves exit at once): kSummaryInitWaves + batch * hkv.
+int64_t summary_init_slots(int64_t batch, int64_t hkv);
 
-// Launches summary_rows (and summary_merge when the prefix is sliced).
+// Launches summary_rows (and, for an initialisation, summary_merge).
 hipError_t launch_summary(const SummaryArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------- scheduling

@@ -29,10 +29,12 @@
 //     lo = bf16(p - hi)), two MFMAs per product, so the weights keep
 //     ~2^-18 relative error; every sum is fp32.
 // A fold (one slice: the new rows) merges its result into the stored state
-// with eq. (11).  Initialising from a whole prefix splits the prefix into
-// slices whose partial states (max, sum, unnormalised O) go to the
-// workspace, and summary_merge combines them per (request, KV head) with the
-// same merge rule.
+// with eq. (11).  Initialising from whole prefixes cuts them into slices
+// sized from the lengths on the device (slice_tokens / locate_slice: about
+// kSummaryInitWaves slices of equal length over all rows and KV heads, so a
+// ragged batch's long prefixes are cut and its short ones are not); each
+// slice's partial state (max, sum, unnormalised O) goes to the workspace, and
+// summary_merge combines them per (request, KV head) with the same rule.
 #include "sd_common.h"
 #include "sd_internal.h"
 
@@ -58,30 +60,92 @@ struct Tile {
   u32x4 v[D / 16];      // value columns 16 nb + (lane % 16)
 };
 
+// Slice length of a whole-prefix initialisation, the same in every wave:
+// T = max(kSummaryMinSplit, ceil(sum_b N_b / kSummaryInitWaves) * hkv)
+// rounded up to a tile, capped at the page-table row (then every prefix is
+// one slice).  T >= sum_b N_b * hkv / kSummaryInitWaves bounds the slices.
+__device__ int slice_tokens(const SummaryArgs& a, int lane) {
+  const int n_max = a.max_pages * 16;
+  long long s = 0;
+  for (int b = lane; b < a.batch; b += 64) s += clampi(a.ctx_len[b], 0, n_max);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+  long long t = (s + kSummaryInitWaves - 1) / kSummaryInitWaves * a.hkv;   // >= s hkv / waves
+  t = (t + kTile - 1) / kTile * kTile;
+  t = t < kSummaryMinSplit ? kSummaryMinSplit : t;
+  const long long cap = (max(n_max, kSummaryMinSplit) + kTile - 1) / kTile * kTile;
+  return static_cast<int>(t < cap ? t : cap);
+}
+
+// Slots of the slices, request-major, then KV head, then slice: request b has
+// c_b = max(1, round(N_b / T)) slices per KV head (none for an empty prefix)
+// of ceil(N_b / c_b) tokens, starting at slot off_b; rounding to the nearest
+// count keeps a prefix just over a multiple of T from getting a tiny extra
+// slice (and an extra wavefront).  With slot >= 0 finds the request holding
+// that slot (false past the last slot); with slot < 0 stops at request
+// `want`.  At most kSummaryInitWaves + B * hkv slots exist (each prefix has
+// at most N_b / T + 1/2 slices per head).
+__device__ bool find_slices(const SummaryArgs& a, int T, int slot, int want, int lane, int& b,
+                            int& off, int& c) {
+  const int n_max = a.max_pages * 16;
+  int base = 0;
+  for (int b0 = 0; b0 < a.batch; b0 += 64) {
+    const int bb = b0 + lane;
+    const int nl = bb < a.batch ? clampi(a.ctx_len[bb], 0, n_max) : 0;
+    const int cl = nl > 0 ? max(1, (nl + T / 2) / T) : 0;
+    const int units = cl * a.hkv;
+    int incl = units;                                   // inclusive scan over the lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    const int chunk = __shfl(incl, 63, 64);
+    int l = -1;
+    if (slot >= 0) {
+      if (slot < base + chunk) l = __ffsll(static_cast<unsigned long long>(__ballot(slot < base + incl))) - 1;
+    } else if (want < b0 + 64) {
+      l = want - b0;
+    }
+    if (l >= 0) {
+      b = b0 + l;
+      off = base + __shfl(incl - units, l, 64);
+      c = __shfl(cl, l, 64);
+      return true;
+    }
+    base += chunk;
+  }
+  return false;
+}
+
 // D: head dim; QG: groups of 16 summary queries (S <= 16 QG); FOLD: a fold
 // (a.accepted given), whose stored state is loaded at the start (one group
 // of queries) so that its latency overlaps the page-id and row loads.
 template <int D, int QG, bool FOLD>
 __global__ __launch_bounds__(64) void summary_rows(SummaryArgs a) {
   constexpr int KS = D / 32, NB = D / 16;
-  const int pair = blockIdx.x / a.nsplit, split = blockIdx.x % a.nsplit;
-  const int b = pair / a.hkv, g = pair % a.hkv;
   const int lane = threadIdx.x, col = lane & 15, grp = lane >> 4;
   const int S = a.n_summary;
   const int n_max = a.max_pages * 16;
-  const int n = clampi(a.ctx_len[b], 0, n_max);
-  int lo, hi;   // rows [lo, hi) of this wave
+  int b, g, lo, hi;   // request, KV head, rows [lo, hi) of this wave
   if constexpr (FOLD) {
-    lo = n;
-    hi = min(n_max, n + clampi(a.accepted[b], 0, n_max) + 1);
+    b = blockIdx.x / a.hkv;
+    g = blockIdx.x % a.hkv;
+    lo = clampi(a.ctx_len[b], 0, n_max);
+    hi = min(n_max, lo + clampi(a.accepted[b], 0, n_max) + 1);
   } else {
-    lo = 0;
-    hi = n;
+    // slot blockIdx.x: slice j of KV head g of request b
+    const int T = slice_tokens(a, lane);
+    int off, c;
+    if (!find_slices(a, T, blockIdx.x, 0, lane, b, off, c)) return;   // past the last slot
+    const int k = static_cast<int>(blockIdx.x) - off;
+    const int n = clampi(a.ctx_len[b], 0, n_max);
+    const int tb = (n + c - 1) / c;                 // this request's slice length
+    g = k / c;
+    lo = (k % c) * tb;
+    hi = min(n, lo + tb);                           // (an empty last slice is possible)
   }
-  if (a.nsplit > 1) {
-    lo = max(lo, split * a.split_tokens);
-    hi = min(hi, (split + 1) * a.split_tokens);
-  }
+  const int pair = b * a.hkv + g;
 
   // a fold's stored state for the entries this lane merges (below)
   constexpr bool kEarly = FOLD && QG == 1;
@@ -241,7 +305,7 @@ __global__ __launch_bounds__(64) void summary_rows(SummaryArgs a) {
     l[qg] += xor_shuffle(l[qg], 32);
   }
 
-  if (a.nsplit > 1) {
+  if constexpr (!FOLD) {
     // partial state of the slice: max (base 2), sum, unnormalised O
     const size_t base = static_cast<size_t>(blockIdx.x) * S;
 #pragma unroll
@@ -262,7 +326,7 @@ __global__ __launch_bounds__(64) void summary_rows(SummaryArgs a) {
     return;
   }
 
-  // one slice: merge with the stored state (eq. (11)); initialisation replaces it
+  // a fold: merge with the stored state (eq. (11)); no new rows leave it as is
   float* zs = a.z + static_cast<size_t>(pair) * S * D;
   float* cs = a.c + static_cast<size_t>(pair) * S;
 #pragma unroll
@@ -272,24 +336,20 @@ __global__ __launch_bounds__(64) void summary_rows(SummaryArgs a) {
       const int q = 16 * qg + 4 * grp + i;
       const float mq = __shfl(m[qg], 4 * grp + i, 64);
       const float lq = __shfl(l[qg], 4 * grp + i, 64);
-      if (q >= S) continue;
-      const float c_new = lq > 0.f ? (mq + log2f(lq)) * kLn2 : -INFINITY;
-      float c_old = -INFINITY;
+      if (q >= S || !(lq > 0.f)) continue;
+      const float c_new = (mq + log2f(lq)) * kLn2;
+      float c_old;
       if constexpr (kEarly) c_old = c_pre[i];
-      else if constexpr (FOLD) c_old = cs[q];
+      else c_old = cs[q];
       float* zq = zs + static_cast<size_t>(q) * D;
-      if (c_new == -INFINITY) {
-        if (!FOLD) {   // empty prefix: the empty state
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) zq[16 * nb + col] = 0.f;
-        }
-      } else if (c_old == -INFINITY) {
+      float c = c_new;
+      if (c_old == -INFINITY) {
         const float inv = 1.f / lq;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) zq[16 * nb + col] = o[qg][nb][i] * inv;
       } else {
         const float mx = fmaxf(c_old, c_new);
-        const float c = mx + logf(expf(c_old - mx) + expf(c_new - mx));
+        c = mx + logf(expf(c_old - mx) + expf(c_new - mx));
         const float wo = expf(c_old - c), wn = expf(c_new - c) / lq;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -299,49 +359,44 @@ __global__ __launch_bounds__(64) void summary_rows(SummaryArgs a) {
           zq[16 * nb + col] = wo * z_old + wn * o[qg][nb][i];
         }
       }
-      if (col == 0) {
-        float c = c_old;
-        if (c_new != -INFINITY) {
-          if (c_old == -INFINITY) {
-            c = c_new;
-          } else {
-            const float mx = fmaxf(c_old, c_new);
-            c = mx + logf(expf(c_old - mx) + expf(c_new - mx));
-          }
-        }
-        cs[q] = FOLD ? c : c_new;
-      }
+      if (col == 0) cs[q] = c;
     }
   }
 }
 
 // Combines the slices of a whole-prefix initialisation: entry (q, d) of a
 // (request, KV head) is sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over
-// the non-empty slices s, M = max m_s (base 2); c = ln 2 (M + log2 of the
-// denominator).
+// its non-empty slices s, M = max m_s (base 2); c = ln 2 (M + log2 of the
+// denominator).  A prefix without rows gets the empty state (Z = 0,
+// c = -inf).
 __global__ __launch_bounds__(kMergeThreads) void summary_merge(SummaryArgs a) {
   const int pair = blockIdx.x, S = a.n_summary, D = a.head_dim;
+  const int b = pair / a.hkv, g = pair % a.hkv;
+  const int lane = threadIdx.x & 63;
+  const int T = slice_tokens(a, lane);
+  int bb, off, nc;
+  find_slices(a, T, -1, b, lane, bb, off, nc);
   const int e = blockIdx.y * kMergeThreads + threadIdx.x;
   if (e >= S * D) return;
   const int q = e / D, d = e % D;
-  const size_t base = static_cast<size_t>(pair) * a.nsplit;
+  const size_t base = static_cast<size_t>(off) + static_cast<size_t>(g) * nc;
   // one pass with a running maximum over groups of 16 slices whose loads go
   // out together (clamped index; an empty slice's values are never written
   // and are dropped by a select)
   constexpr int U = 16;
   float M = -INFINITY, L = 0.f, O = 0.f;
-  for (int s0 = 0; s0 < a.nsplit; s0 += U) {
+  for (int s0 = 0; s0 < nc; s0 += U) {
     float2 ml[U];
     float os[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const size_t i = (base + min(s0 + u, a.nsplit - 1)) * S + q;
+      const size_t i = (base + min(s0 + u, nc - 1)) * S + q;
       ml[u] = a.part_ml[i];
       os[u] = a.part_o[i * D + d];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool live = s0 + u < a.nsplit && ml[u].y > 0.f;
+      const bool live = s0 + u < nc && ml[u].y > 0.f;
       const float mn = live ? fmaxf(M, ml[u].x) : M;
       const float r = mn == M ? 1.f : exp2f(M - mn);    // M = -inf: 0
       const float w = live ? exp2f(ml[u].x - mn) : 0.f;
@@ -364,31 +419,17 @@ hipError_t launch_rows(const SummaryArgs& a, dim3 grid, hipStream_t s) {
 
 }  // namespace
 
-SummaryPlan summary_plan(int64_t batch, int64_t hkv, int64_t max_pages) {
-  // about 1,024 wavefronts (one per SIMD) in slices of at least 512 tokens:
-  // at 16 x 131,072-token prefixes 8,192 / 4,096 / 2,048 / 1,024 / 768 / 512
-  // wavefronts took 1.44 / 1.35 / 1.30 / 1.26 / 1.24 / 1.25 ms (fewer
-  // wavefronts: fewer partials to write and merge, less per-wave start-up)
-  const int64_t pairs = batch * hkv, n_max = max_pages * 16;
-  const int64_t want = (kSummaryInitWaves + pairs - 1) / pairs;
-  int64_t tok = (n_max + want - 1) / want;
-  tok = ((tok + kTile - 1) / kTile) * kTile;
-  if (tok < kSummaryMinSplit) tok = kSummaryMinSplit;
-  SummaryPlan p;
-  p.nsplit = (n_max + tok - 1) / tok;
-  p.split_tokens = p.nsplit > 1 ? tok : n_max;
-  return p;
-}
+int64_t summary_init_slots(int64_t batch, int64_t hkv) { return kSummaryInitWaves + batch * hkv; }
 
 hipError_t launch_summary(const SummaryArgs& a, hipStream_t s) {
   const int head_dim = a.head_dim;
-  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.batch) * a.hkv * a.nsplit));
-  hipError_t e;
-  if (a.accepted)
-    e = head_dim == 64 ? launch_rows<64, true>(a, grid, s) : launch_rows<128, true>(a, grid, s);
-  else
-    e = head_dim == 64 ? launch_rows<64, false>(a, grid, s) : launch_rows<128, false>(a, grid, s);
-  if (e != hipSuccess || a.nsplit == 1) return e;
+  if (a.accepted)   // a fold: one wave per (request, KV head)
+    return head_dim == 64 ? launch_rows<64, true>(a, dim3(a.batch * a.hkv), s)
+                          : launch_rows<128, true>(a, dim3(a.batch * a.hkv), s);
+  // an initialisation: one wave per slice slot, then the merge
+  const dim3 grid(static_cast<uint32_t>(summary_init_slots(a.batch, a.hkv)));
+  hipError_t e = head_dim == 64 ? launch_rows<64, false>(a, grid, s) : launch_rows<128, false>(a, grid, s);
+  if (e != hipSuccess) return e;
   const dim3 mgrid(a.batch * a.hkv, (a.n_summary * head_dim + kMergeThreads - 1) / kMergeThreads);
   return launch_kernel(summary_merge, mgrid, dim3(kMergeThreads), s, a);
 }

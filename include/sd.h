@@ -252,12 +252,12 @@ sd_status sd_draft_attn_noalloc(const void* q, const void* k_blk, const void* v_
  *   summary_values  fp32 [batch, Hkv, n_summary, D]  Z, updated in place
  *   summary_lse     fp32 [batch, Hkv, n_summary]     c, updated in place
  *   workspace       initialisation (accepted_len == NULL) only: at least
- *                   sd_summary_workspace_size(...) bytes (NULL allowed when
- *                   that size is 0); folds ignore it
- * Work: one wavefront per (request, KV head) for a fold; an initialisation
- * slices every prefix (about 1,024 wavefronts, slices of >= 512 tokens,
- * sized from max_pages; none when there are 1,024 or more (request, KV head)
- * pairs) and merges the slices' states in a second kernel.
+ *                   sd_summary_workspace_size(...) bytes; folds ignore it
+ * Work: one wavefront per (request, KV head) for a fold.  An initialisation
+ * cuts the prefixes into slices sized on the device from the lengths
+ * themselves (T = max(512, ceil(sum_b N_b / 1024) * Hkv) tokens; request b
+ * gets max(1, round(N_b / T)) equal slices per KV head, about 1,024 in all),
+ * one wavefront each, and merges the slices' states in a second kernel.
  * Errors: SD_ERR_NULL, SD_ERR_SHAPE (as listed above, unaligned pointers),
  * SD_ERR_WORKSPACE (initialisation with a missing or short workspace),
  * SD_ERR_LAUNCH.

@@ -152,29 +152,27 @@ def _sum(lib, **kw):
     (dict(u=None), 1), (dict(z=None), 1), (dict(c=None), 1), (dict(ctx_len=None), 1),
     (dict(batch=0), 2), (dict(d=96), 2), (dict(n_sum=0), 2), (dict(n_sum=65), 2),
     (dict(page_size=8), 2), (dict(scale=-1.0), 2), (dict(k_cache=ODD), 2), (dict(u=ODD), 2),
-    # an initialisation over 4,096-page rows is sliced and needs the workspace
-    (dict(acc=None, max_pages=4096, ws=None), 3), (dict(acc=None, max_pages=4096, ws_bytes=16), 3),
-    (dict(acc=None, max_pages=4096, ws=ODD), 3),
+    # an initialisation needs the workspace
+    (dict(acc=None, ws=None), 3), (dict(acc=None, ws_bytes=16), 3), (dict(acc=None, ws=ODD), 3),
 ])
 def test_summary_update_validation(lib, kw, status):
     assert _sum(lib, **kw) == status
 
 
 def test_summary_workspace_size(lib):
-    """A fold needs no workspace; an initialisation is cut into slices of at
-    least 512 tokens, aiming at 1,024 wavefronts, each slice keeping a
-    (max, sum, S x D values) partial state in fp32."""
+    """A fold needs no workspace; an initialisation keeps a (max, sum,
+    S x D values) fp32 partial state per slice slot: 1,024 + B * Hkv slots
+    (slices of length max(512, ceil(sum N_b / 1,024) * Hkv) tokens are at
+    most that many), each array rounded up to 256 bytes."""
     size = lib.sd_summary_workspace_size
-    assert size(2, 2, 16, 128, 5, 16) == 0          # 80 tokens: one slice
-    assert size(2, 2, 16, 128, 32, 16) == 0         # 512 tokens: one slice
-    # 16 requests x 8 KV heads over 131,072 tokens: 8 slices of 16,384 tokens
-    parts = 16 * 8 * 8 * 16
-    assert size(16, 8, 16, 128, 8192, 16) == 2 * parts * 4 + parts * 128 * 4
-    # 4 pairs over 65,536 tokens: slices of 512 tokens, 128 of them
-    parts = 4 * 128 * 16
-    assert size(2, 2, 16, 128, 4096, 16) == 2 * parts * 4 + parts * 128 * 4
-    # 128 requests x 8 KV heads: one wavefront per pair already, no slices
-    assert size(128, 8, 16, 128, 8192, 16) == 0
+
+    def expect(batch, hkv, s, d):
+        parts = (1024 + batch * hkv) * s
+        return -(-parts * 8 // 256) * 256 + -(-parts * d * 4 // 256) * 256
+
+    for args in ((2, 2, 16, 128, 5), (16, 8, 16, 128, 8192), (128, 8, 16, 128, 8192),
+                 (3, 1, 5, 64, 100)):
+        assert size(*args, 16) == expect(*args[:4])
     assert size(0, 2, 16, 128, 4096, 16) == 0 and size(2, 2, 16, 128, 4096, 8) == 0
 
 
