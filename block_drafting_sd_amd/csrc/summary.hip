@@ -30,7 +30,7 @@
 //     ~2^-18 relative error; every sum is fp32.
 // A fold (one slice: the new rows) merges its result into the stored state
 // with eq. (11).  Initialising from whole prefixes cuts them into slices
-// sized from the lengths on the device (slice_tokens / locate_slice: about
+// sized from the lengths on the device (slice_tokens / find_slices: about
 // kSummaryInitWaves slices of equal length over all rows and KV heads, so a
 // ragged batch's long prefixes are cut and its short ones are not); each
 // slice's partial state (max, sum, unnormalised O) goes to the workspace, and
