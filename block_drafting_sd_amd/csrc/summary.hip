@@ -78,13 +78,14 @@ __device__ int slice_tokens(const SummaryArgs& a, int lane) {
 }
 
 // Slots of the slices, request-major, then KV head, then slice: request b has
-// c_b = max(1, round(N_b / T)) slices per KV head (none for an empty prefix)
-// of ceil(N_b / c_b) tokens, starting at slot off_b; rounding to the nearest
-// count keeps a prefix just over a multiple of T from getting a tiny extra
-// slice (and an extra wavefront).  With slot >= 0 finds the request holding
-// that slot (false past the last slot); with slot < 0 stops at request
-// `want`.  At most kSummaryInitWaves + B * hkv slots exist (each prefix has
-// at most N_b / T + 1/2 slices per head).
+// c_b = ceil(N_b / (9 T / 8)) slices per KV head (none for an empty prefix)
+// of ceil(N_b / c_b) <= 9 T / 8 tokens, starting at slot off_b; the eighth of
+// slack keeps a prefix just past a multiple of T from getting an extra slice
+// (and an extra wavefront), while no slice grows much beyond T, the ragged
+// batch's tail.  With slot >= 0 finds the request holding that slot (false
+// past the last slot); with slot < 0 stops at request `want`.  At most
+// kSummaryInitWaves + B * hkv slots exist (each prefix has fewer than
+// N_b / T + 1 slices per head).
 __device__ bool find_slices(const SummaryArgs& a, int T, int slot, int want, int lane, int& b,
                             int& off, int& c) {
   const int n_max = a.max_pages * 16;
@@ -92,7 +93,7 @@ __device__ bool find_slices(const SummaryArgs& a, int T, int slot, int want, int
   for (int b0 = 0; b0 < a.batch; b0 += 64) {
     const int bb = b0 + lane;
     const int nl = bb < a.batch ? clampi(a.ctx_len[bb], 0, n_max) : 0;
-    const int cl = nl > 0 ? max(1, (nl + T / 2) / T) : 0;
+    const int cl = nl > 0 ? static_cast<int>((8LL * nl + 9LL * T - 1) / (9LL * T)) : 0;
     const int units = cl * a.hkv;
     int incl = units;                                   // inclusive scan over the lanes
 #pragma unroll
