@@ -88,11 +88,11 @@ struct SummaryArgs {
 };
 
 constexpr int kSummaryMax = 64;            // summary entries per KV head
-constexpr int kSummaryInitWaves = 1024;    // slices an initialisation aims for (one per SIMD)
-constexpr int kSummaryMinSplit = 512;      // fewest tokens per slice
+constexpr int kSummaryInitWaves = 1024;    // waves of an initialisation (one per SIMD)
+constexpr int kSummaryMinSplit = 512;      // fewest rows per wave
 
-// Slice slots of an initialisation (an upper bound on the slices; the extra
-// waves exit at once): kSummaryInitWaves + batch * hkv.
+// Partial slots of an initialisation: the piece of pair p that wave w covers
+// goes to slot p + w, so kSummaryInitWaves + batch * hkv of them.
 int64_t summary_init_slots(int64_t batch, int64_t hkv);
 
 // Launches summary_rows (and, for an initialisation, summary_merge).

@@ -29,12 +29,12 @@
 //     lo = bf16(p - hi)), two MFMAs per product, so the weights keep
 //     ~2^-18 relative error; every sum is fp32.
 // A fold (one slice: the new rows) merges its result into the stored state
-// with eq. (11).  Initialising from whole prefixes cuts them into slices
-// sized from the lengths on the device (slice_tokens / find_slices: about
-// kSummaryInitWaves slices of equal length over all rows and KV heads, so a
-// ragged batch's long prefixes are cut and its short ones are not); each
-// slice's partial state (max, sum, unnormalised O) goes to the workspace, and
-// summary_merge combines them per (request, KV head) with the same rule.
+// with eq. (11).  Initialising from whole prefixes splits the concatenation
+// of every (request, KV head)'s rows into kSummaryInitWaves equal runs, one
+// per wave, whatever the lengths (concat_size / find_request); each piece of
+// a (request, KV head) that a wave covers leaves its partial state (max, sum,
+// unnormalised O) in the workspace, and summary_merge combines a pair's
+// pieces with the same rule.
 #include "sd_common.h"
 #include "sd_internal.h"
 
@@ -60,58 +60,51 @@ struct Tile {
   u32x4 v[D / 16];      // value columns 16 nb + (lane % 16)
 };
 
-// Slice length of a whole-prefix initialisation, the same in every wave:
-// T = max(kSummaryMinSplit, ceil(sum_b N_b / kSummaryInitWaves) * hkv)
-// rounded up to a tile, capped at the page-table row (then every prefix is
-// one slice).  T >= sum_b N_b * hkv / kSummaryInitWaves bounds the slices.
-__device__ int slice_tokens(const SummaryArgs& a, int lane) {
+// A whole-prefix initialisation walks the concatenation of every (request,
+// KV head)'s rows: request b's KV head g owns rows P_b + g N_b .. P_b +
+// (g + 1) N_b, P_b = hkv * sum_{b' < b} N_b'.  Wave w takes rows w T ..
+// (w + 1) T, T = max(kSummaryMinSplit, ceil(total / kSummaryInitWaves)), so
+// every wave has the same work whatever the lengths; the piece of pair p that
+// wave w covers goes to slot p + w (both grow along the rows, so no two
+// pieces share a slot, and slots stay below B * hkv + kSummaryInitWaves).
+
+// total rows (hkv * sum_b N_b) and T, the same in every wave
+__device__ void concat_size(const SummaryArgs& a, int lane, long long& total, long long& T) {
   const int n_max = a.max_pages * 16;
   long long s = 0;
   for (int b = lane; b < a.batch; b += 64) s += clampi(a.ctx_len[b], 0, n_max);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
-  long long t = (s + kSummaryInitWaves - 1) / kSummaryInitWaves * a.hkv;   // >= s hkv / waves
-  t = (t + kTile - 1) / kTile * kTile;
-  t = t < kSummaryMinSplit ? kSummaryMinSplit : t;
-  const long long cap = (max(n_max, kSummaryMinSplit) + kTile - 1) / kTile * kTile;
-  return static_cast<int>(t < cap ? t : cap);
+  total = s * a.hkv;
+  T = (total + kSummaryInitWaves - 1) / kSummaryInitWaves;
+  T = T < kSummaryMinSplit ? kSummaryMinSplit : T;
 }
 
-// Slots of the slices, request-major, then KV head, then slice: request b has
-// c_b = ceil(N_b / (9 T / 8)) slices per KV head (none for an empty prefix)
-// of ceil(N_b / c_b) <= 9 T / 8 tokens, starting at slot off_b; the eighth of
-// slack keeps a prefix just past a multiple of T from getting an extra slice
-// (and an extra wavefront), while no slice grows much beyond T, the ragged
-// batch's tail.  With slot >= 0 finds the request holding that slot (false
-// past the last slot); with slot < 0 stops at request `want`.  At most
-// kSummaryInitWaves + B * hkv slots exist (each prefix has fewer than
-// N_b / T + 1 slices per head).
-__device__ bool find_slices(const SummaryArgs& a, int T, int slot, int want, int lane, int& b,
-                            int& off, int& c) {
+// Request b and its first row P_b: with row >= 0 the request whose rows hold
+// `row` (false past the last row); with row < 0 request `want`.
+__device__ bool find_request(const SummaryArgs& a, long long row, int want, int lane, int& b,
+                             long long& pb) {
   const int n_max = a.max_pages * 16;
-  int base = 0;
+  long long base = 0;
   for (int b0 = 0; b0 < a.batch; b0 += 64) {
     const int bb = b0 + lane;
-    const int nl = bb < a.batch ? clampi(a.ctx_len[bb], 0, n_max) : 0;
-    const int cl = nl > 0 ? static_cast<int>((8LL * nl + 9LL * T - 1) / (9LL * T)) : 0;
-    const int units = cl * a.hkv;
-    int incl = units;                                   // inclusive scan over the lanes
+    const long long rows = bb < a.batch ? static_cast<long long>(clampi(a.ctx_len[bb], 0, n_max)) * a.hkv : 0;
+    long long incl = rows;                              // inclusive scan over the lanes
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o, 64);
+      const long long v = __shfl_up(incl, o, 64);
       if (lane >= o) incl += v;
     }
-    const int chunk = __shfl(incl, 63, 64);
+    const long long chunk = __shfl(incl, 63, 64);
     int l = -1;
-    if (slot >= 0) {
-      if (slot < base + chunk) l = __ffsll(static_cast<unsigned long long>(__ballot(slot < base + incl))) - 1;
+    if (row >= 0) {
+      if (row < base + chunk) l = __ffsll(static_cast<unsigned long long>(__ballot(row < base + incl))) - 1;
     } else if (want < b0 + 64) {
       l = want - b0;
     }
     if (l >= 0) {
       b = b0 + l;
-      off = base + __shfl(incl - units, l, 64);
-      c = __shfl(cl, l, 64);
+      pb = base + __shfl(incl - rows, l, 64);
       return true;
     }
     base += chunk;
@@ -128,24 +121,9 @@ __global__ __launch_bounds__(64) void summary_rows(SummaryArgs a) {
   const int lane = threadIdx.x, col = lane & 15, grp = lane >> 4;
   const int S = a.n_summary;
   const int n_max = a.max_pages * 16;
-  int b, g, lo, hi;   // request, KV head, rows [lo, hi) of this wave
-  if constexpr (FOLD) {
-    b = blockIdx.x / a.hkv;
-    g = blockIdx.x % a.hkv;
-    lo = clampi(a.ctx_len[b], 0, n_max);
-    hi = min(n_max, lo + clampi(a.accepted[b], 0, n_max) + 1);
-  } else {
-    // slot blockIdx.x: slice j of KV head g of request b
-    const int T = slice_tokens(a, lane);
-    int off, c;
-    if (!find_slices(a, T, blockIdx.x, 0, lane, b, off, c)) return;   // past the last slot
-    const int k = static_cast<int>(blockIdx.x) - off;
-    const int n = clampi(a.ctx_len[b], 0, n_max);
-    const int tb = (n + c - 1) / c;                 // this request's slice length
-    g = k / c;
-    lo = (k % c) * tb;
-    hi = min(n, lo + tb);                           // (an empty last slice is possible)
-  }
+  // a fold: request b, KV head g, its new rows [lo, hi)
+  const int b = FOLD ? static_cast<int>(blockIdx.x) / a.hkv : 0;
+  const int g = FOLD ? static_cast<int>(blockIdx.x) % a.hkv : 0;
   const int pair = b * a.hkv + g;
 
   // a fold's stored state for the entries this lane merges (below)
@@ -163,8 +141,15 @@ __global__ __launch_bounds__(64) void summary_rows(SummaryArgs a) {
     }
   }
 
-  // summary queries: B operand of the score products (query 16 qg + col)
   bf16x8 uq[QG][KS];
+  f32x4 o[QG][NB];
+  float m[QG], l[QG];
+  const float sl2 = a.scale * kLog2e;
+
+  // (m, l, O) of KV head g's summary queries over rows [lo, hi) of request b;
+  // l summed over the four lanes of a column at the end
+  auto walk = [&](int b, int g, int lo, int hi) {
+  // summary queries: B operand of the score products (query 16 qg + col)
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg) {
     const int q = 16 * qg + col;
@@ -173,8 +158,6 @@ __global__ __launch_bounds__(64) void summary_rows(SummaryArgs a) {
       uq[qg][ks] = q < S ? load_bf16x8(a.u + (static_cast<size_t>(g) * S + q) * D + 32 * ks + 8 * grp)
                          : zero_bf16x8();
   }
-  f32x4 o[QG][NB];
-  float m[QG], l[QG];
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg) {
     m[qg] = -INFINITY;
@@ -182,7 +165,6 @@ __global__ __launch_bounds__(64) void summary_rows(SummaryArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) o[qg][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const float sl2 = a.scale * kLog2e;
   const int* pt = a.page_table + static_cast<size_t>(b) * a.max_pages;
   // the lane's key tokens (chain h) lie in tile page col / 8, its value
   // tokens 8 grp .. 8 grp + 7 in tile page grp / 2
@@ -305,15 +287,30 @@ __global__ __launch_bounds__(64) void summary_rows(SummaryArgs a) {
     l[qg] += xor_shuffle(l[qg], 16);
     l[qg] += xor_shuffle(l[qg], 32);
   }
+  };
 
   if constexpr (!FOLD) {
-    // partial state of the slice: max (base 2), sum, unnormalised O
-    const size_t base = static_cast<size_t>(blockIdx.x) * S;
+    // rows [w T, (w + 1) T) of the concatenation, piece by piece
+    long long total, T;
+    concat_size(a, lane, total, T);
+    const long long w = blockIdx.x;
+    const long long r0 = w * T, r1 = min(total, r0 + T);
+    int rb;
+    long long pb;
+    if (r0 >= total || !find_request(a, r0, 0, lane, rb, pb)) return;   // past the last row
+    long long cur = r0;
+    for (;;) {
+      const int n = clampi(a.ctx_len[rb], 0, n_max);   // > 0: the request holds row cur
+      const int rg = static_cast<int>((cur - pb) / n);
+      const long long ps = pb + static_cast<long long>(rg) * n;   // first row of (rb, rg)
+      const long long pe = min(r1, ps + n);
+      walk(rb, rg, static_cast<int>(cur - ps), static_cast<int>(pe - ps));
+      // partial state of the piece: max (base 2), sum, unnormalised O
+      const size_t base = (static_cast<size_t>(rb) * a.hkv + rg + static_cast<size_t>(w)) * S;
 #pragma unroll
-    for (int qg = 0; qg < QG; ++qg) {
-      const int q = 16 * qg + col;
-      if (grp == 0 && q < S) a.part_ml[base + q] = make_float2(m[qg], l[qg]);
-      if (hi > lo) {
+      for (int qg = 0; qg < QG; ++qg) {
+        const int q = 16 * qg + col;
+        if (grp == 0 && q < S) a.part_ml[base + q] = make_float2(m[qg], l[qg]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int qi = 16 * qg + 4 * grp + i;
@@ -323,8 +320,23 @@ __global__ __launch_bounds__(64) void summary_rows(SummaryArgs a) {
           }
         }
       }
+      cur = pe;
+      if (cur >= r1) break;
+      if (rg + 1 == a.hkv) {   // the next request with rows
+        pb += static_cast<long long>(n) * a.hkv;
+        do {
+          ++rb;
+        } while (rb < a.batch && clampi(a.ctx_len[rb], 0, n_max) == 0);
+        if (rb >= a.batch) break;
+      }
     }
     return;
+  }
+
+  // a fold: the committed token and the accepted drafts of request b
+  {
+    const int lo = clampi(a.ctx_len[b], 0, n_max);
+    walk(b, g, lo, min(n_max, lo + clampi(a.accepted[b], 0, n_max) + 1));
   }
 
   // a fold: merge with the stored state (eq. (11)); no new rows leave it as is
@@ -365,22 +377,28 @@ __global__ __launch_bounds__(64) void summary_rows(SummaryArgs a) {
   }
 }
 
-// Combines the slices of a whole-prefix initialisation: entry (q, d) of a
+// Combines the pieces of a whole-prefix initialisation: entry (q, d) of a
 // (request, KV head) is sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over
-// its non-empty slices s, M = max m_s (base 2); c = ln 2 (M + log2 of the
-// denominator).  A prefix without rows gets the empty state (Z = 0,
-// c = -inf).
+// its pieces s (slots p + w for the waves w covering its rows), M = max m_s
+// (base 2); c = ln 2 (M + log2 of the denominator).  A prefix without rows
+// gets the empty state (Z = 0, c = -inf).
 __global__ __launch_bounds__(kMergeThreads) void summary_merge(SummaryArgs a) {
   const int pair = blockIdx.x, S = a.n_summary, D = a.head_dim;
   const int b = pair / a.hkv, g = pair % a.hkv;
   const int lane = threadIdx.x & 63;
-  const int T = slice_tokens(a, lane);
-  int bb, off, nc;
-  find_slices(a, T, -1, b, lane, bb, off, nc);
+  long long total, T;
+  concat_size(a, lane, total, T);
+  int bb;
+  long long pb;
+  find_request(a, -1, b, lane, bb, pb);
+  const int n = clampi(a.ctx_len[b], 0, a.max_pages * 16);
+  const long long ps = pb + static_cast<long long>(g) * n;   // first row of the pair
+  const int w0 = static_cast<int>(ps / T);
+  const int nc = n > 0 ? static_cast<int>((ps + n - 1) / T) - w0 + 1 : 0;
   const int e = blockIdx.y * kMergeThreads + threadIdx.x;
   if (e >= S * D) return;
   const int q = e / D, d = e % D;
-  const size_t base = static_cast<size_t>(off) + static_cast<size_t>(g) * nc;
+  const size_t base = static_cast<size_t>(pair) + w0;
   // one pass with a running maximum over groups of 16 slices whose loads go
   // out together (clamped index; an empty slice's values are never written
   // and are dropped by a select)
@@ -427,8 +445,9 @@ hipError_t launch_summary(const SummaryArgs& a, hipStream_t s) {
   if (a.accepted)   // a fold: one wave per (request, KV head)
     return head_dim == 64 ? launch_rows<64, true>(a, dim3(a.batch * a.hkv), s)
                           : launch_rows<128, true>(a, dim3(a.batch * a.hkv), s);
-  // an initialisation: one wave per slice slot, then the merge
-  const dim3 grid(static_cast<uint32_t>(summary_init_slots(a.batch, a.hkv)));
+  // an initialisation: kSummaryInitWaves waves over the concatenated rows,
+  // then the merge
+  const dim3 grid(kSummaryInitWaves);
   hipError_t e = head_dim == 64 ? launch_rows<64, false>(a, grid, s) : launch_rows<128, false>(a, grid, s);
   if (e != hipSuccess) return e;
   const dim3 mgrid(a.batch * a.hkv, (a.n_summary * head_dim + kMergeThreads - 1) / kMergeThreads);

@@ -254,10 +254,10 @@ sd_status sd_draft_attn_noalloc(const void* q, const void* k_blk, const void* v_
  *   workspace       initialisation (accepted_len == NULL) only: at least
  *                   sd_summary_workspace_size(...) bytes; folds ignore it
  * Work: one wavefront per (request, KV head) for a fold.  An initialisation
- * cuts the prefixes into slices sized on the device from the lengths
- * themselves (T = max(512, ceil(sum_b N_b / 1024) * Hkv) tokens; request b
- * gets ceil(N_b / (9 T / 8)) equal slices per KV head, about 1,024 in all),
- * one wavefront each, and merges the slices' states in a second kernel.
+ * runs 1,024 wavefronts over the concatenation of every (request, KV head)'s
+ * rows, each taking an equal run of max(512, ceil(Hkv * sum_b N_b / 1024))
+ * rows whatever the lengths (read on the device), and merges the pieces of
+ * each (request, KV head) in a second kernel.
  * Errors: SD_ERR_NULL, SD_ERR_SHAPE (as listed above, unaligned pointers),
  * SD_ERR_WORKSPACE (initialisation with a missing or short workspace),
  * SD_ERR_LAUNCH.

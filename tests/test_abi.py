@@ -161,9 +161,10 @@ def test_summary_update_validation(lib, kw, status):
 
 def test_summary_workspace_size(lib):
     """A fold needs no workspace; an initialisation keeps a (max, sum,
-    S x D values) fp32 partial state per slice slot: 1,024 + B * Hkv slots
-    (slices of length max(512, ceil(sum N_b / 1,024) * Hkv) tokens are at
-    most that many), each array rounded up to 256 bytes."""
+    S x D values) fp32 partial state per slot: 1,024 waves walk the
+    concatenated (request, KV head) rows and the piece of pair p that wave w
+    covers goes to slot p + w, so 1,024 + B * Hkv slots, each array rounded
+    up to 256 bytes."""
     size = lib.sd_summary_workspace_size
 
     def expect(batch, hkv, s, d):
