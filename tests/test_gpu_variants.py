@@ -220,6 +220,21 @@ def test_summary_init_sliced_ragged(head_dim, n_summary):
     _check_summary(z, c, Z1, C1, f"fold across tiles D={head_dim} S={n_summary}")
 
 
+def test_summary_init_empty_requests_between():
+    """Empty prefixes between non-empty ones inside one wavefront's run of
+    the concatenated rows (the walk skips them), and more requests than one
+    64-lane scan chunk."""
+    ctx = (5, 0, 0, 7, 0, 600, 0, 1, 33) + (0,) * 60 + (40, 0, 513)
+    inp = StepInputs(_cfg(batch=len(ctx), ctx=("list", ctx), draft_k=("list", (1,) * len(ctx)),
+                          seed=7373))
+    b = inp.budgets
+    u = inp.summary_queries(16)
+    Zr, Cr = osum.summary_init(u, inp.k_cache, inp.v_cache, inp.page_table, b.ctx_len,
+                               inp.cfg.num_heads_kv, inp.softmax_scale)
+    z, c = _gpu_summary(inp, u, b.ctx_len)
+    _check_summary(z, c, Zr, Cr, f"init with empty requests between ({len(ctx)} requests)")
+
+
 def test_summary_init_full_size_ragged():
     """The ragged serving mix at full size (128 requests, 1K-128K-token
     prefixes, 8 KV heads): with 1,024 (request, KV head) pairs every pair is
