@@ -246,11 +246,10 @@ def sd_summary_update(summary_queries, k_cache, v_cache, page_table, ctx_len, ac
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     ws, ws_bytes = None, 0
-    if accepted_len is None:
-        need = summary_workspace_size(batch, hkv, n_summary, D, max_pages, page_size)
-        if need or workspace is not None:
-            ws = _workspace(workspace, need, dev)
-            ws_bytes = ws.numel() * ws.element_size()
+    if accepted_len is None:   # an initialisation keeps its pieces' partial states there
+        ws = _workspace(workspace, summary_workspace_size(batch, hkv, n_summary, D, max_pages,
+                                                          page_size), dev)
+        ws_bytes = ws.numel() * ws.element_size()
     st = lib.sd_summary_update(_ptr(summary_queries), _ptr(k_cache), _ptr(v_cache),
                                _ptr(page_table), _ptr(ctx_len), _ptr(accepted_len), batch,
                                num_pages, max_pages, page_size, hkv, D, n_summary,
